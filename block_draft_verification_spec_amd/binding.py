@@ -1,0 +1,311 @@
+"""Thin ctypes binding of ``libspecverify.so`` (see ``include/spec_verify.h``).
+
+Argument marshalling only: torch tensors supply device pointers, shapes and
+the current HIP stream; every step of the computation runs in the HIP
+kernels.  There is no fallback: if the library is missing, or a call is made
+with tensors that are not on the GPU, the call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, 'libspecverify.so')
+
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_ECAPACITY, SV_EWORKSPACE, SV_EHIP = range(6)
+SV_F32, SV_BF16 = 0, 1
+SV_GDN_VERIFY_COMMIT, SV_GDN_VERIFY_ONLY, SV_GDN_COMMIT_ONLY = 0, 1, 2
+SV_ACCEPT_GREEDY, SV_ACCEPT_REJECTION = 0, 1
+SV_SCHEDULE_TWO_PHASE, SV_SCHEDULE_DEFERRED = 0, 1
+SV_DERR = {1: 'PAGE', 2: 'CAPACITY', 4: 'SEQLEN', 8: 'COMMIT', 16: 'TOKEN',
+           32: 'SLOT'}
+
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class SvBatch(ctypes.Structure):
+    _fields_ = [('B', _c_i32), ('max_T', _c_i32), ('total_T', _c_i32),
+                ('cu_seqlens', _vp)]
+
+
+class SvGdnPending(ctypes.Structure):
+    _fields_ = [('batch', SvBatch), ('k', _vp), ('v', _vp), ('alpha', _vp),
+                ('beta', _vp), ('commit_len', _vp)]
+
+
+class SvAttnLayer(ctypes.Structure):
+    _fields_ = [('q', _vp), ('k_new', _vp), ('v_new', _vp), ('k_cache', _vp),
+                ('v_cache', _vp), ('out', _vp)]
+
+
+class SvGdnLayer(ctypes.Structure):
+    _fields_ = [('state', _vp), ('q', _vp), ('k', _vp), ('v', _vp),
+                ('alpha', _vp), ('beta', _vp), ('out', _vp)]
+
+
+class SvAttnConfig(ctypes.Structure):
+    _fields_ = [('Hq', _c_i32), ('Hkv', _c_i32), ('D', _c_i32),
+                ('page_size', _c_i32), ('num_pages', _c_i32),
+                ('max_pages_per_seq', _c_i32), ('block_table', _vp),
+                ('dtype', ctypes.c_int), ('scale', ctypes.c_float)]
+
+
+class SvGdnConfig(ctypes.Structure):
+    _fields_ = [('H', _c_i32), ('dk', _c_i32), ('dv', _c_i32),
+                ('num_slots', _c_i32), ('state_slot', _vp),
+                ('io_dtype', ctypes.c_int)]
+
+
+class SvAcceptArgs(ctypes.Structure):
+    _fields_ = [('mode', ctypes.c_int), ('logit_dtype', ctypes.c_int),
+                ('V', _c_i32), ('target_logits', _vp), ('draft_logits', _vp),
+                ('draft_tokens', _vp), ('u_accept', _vp), ('u_final', _vp)]
+
+
+class SvStepPending(ctypes.Structure):
+    _fields_ = [('batch', SvBatch), ('layers', ctypes.POINTER(SvGdnLayer)),
+                ('commit_len', _vp)]
+
+
+_SIGS = {
+    'sv_last_error': ([], ctypes.c_char_p),
+    'sv_version': ([], ctypes.c_char_p),
+    'spec_verify_attention_workspace_bytes': (
+        [_c_i32] * 7 + [ctypes.c_int], _sz),
+    'spec_verify_attention': (
+        [ctypes.POINTER(SvBatch), _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+         _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int,
+         ctypes.c_float, _c_i32, _vp, _sz, _vp, _vp], ctypes.c_int),
+    'gdn_verify_commit': (
+        [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, _c_i32, _vp, _vp,
+         _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+         ctypes.POINTER(SvGdnPending), _vp, _vp], ctypes.c_int),
+    'spec_accept_workspace_bytes': ([_c_i32, _c_i32, _c_i32, ctypes.c_int], _sz),
+    'spec_accept': (
+        [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, ctypes.c_int, _c_i32,
+         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
+    'spec_verify_step_workspace_bytes': (
+        [ctypes.POINTER(SvBatch), ctypes.POINTER(SvAttnConfig),
+         ctypes.POINTER(SvAcceptArgs)], _sz),
+    'spec_verify_step': (
+        [ctypes.POINTER(SvBatch), _c_i32, ctypes.POINTER(ctypes.c_uint8),
+         ctypes.POINTER(SvAttnConfig), ctypes.POINTER(SvAttnLayer),
+         ctypes.POINTER(SvGdnConfig), ctypes.POINTER(SvGdnLayer),
+         ctypes.POINTER(SvAcceptArgs), _vp, _vp, _vp, ctypes.c_int,
+         ctypes.POINTER(SvStepPending), _vp, _sz, _vp, _vp], ctypes.c_int),
+}
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__(f'status {status}: {text}')
+        self.status = status
+
+
+def lib():
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f'{LIB_PATH} is missing: build it with '
+                '`python -m block_draft_verification_spec_amd.build`')
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != SV_OK:
+        raise SpecVerifyError(status, lib().sv_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError('expected a torch tensor')
+    if not t.is_cuda:
+        raise ValueError('tensor must live on the GPU')
+    if not t.is_contiguous():
+        raise ValueError('tensor must be contiguous')
+    return t.data_ptr()
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise ValueError(f'unsupported dtype {t.dtype}')
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _i32(t, name):
+    if t is not None and t.dtype != torch.int32:
+        raise ValueError(f'{name} must be int32')
+    return _ptr(t)
+
+
+def make_batch(cu_seqlens, B, max_T, total_T):
+    """sv_batch from a device int32 ``cu_seqlens`` and host sizes."""
+    return SvBatch(int(B), int(max_T), int(total_T), _i32(cu_seqlens, 'cu_seqlens'))
+
+
+def version():
+    return lib().sv_version().decode()
+
+
+def spec_verify_attention_workspace_bytes(B, total_T, Hq, Hkv, D,
+                                          max_pages_per_seq, page_size, dtype):
+    return lib().spec_verify_attention_workspace_bytes(
+        B, total_T, Hq, Hkv, D, max_pages_per_seq, page_size, dtype)
+
+
+def spec_verify_attention(batch, q, k_new, v_new, k_cache, v_cache,
+                          block_table, ctx_lens, out, scale=0.0, write_kv=True,
+                          workspace=None, err=None, stream=None):
+    """Paged verification attention (``spec_verify_attention``).
+
+    Shapes: q/out [total_T, Hq, D]; k_new/v_new [total_T, Hkv, D];
+    caches [num_pages, Hkv, P, D]; block_table int32 [B, max_pages];
+    ctx_lens int32 [B].
+    """
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k_new.shape[1]
+    num_pages, P = k_cache.shape[0], k_cache.shape[2]
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().spec_verify_attention(
+        ctypes.byref(batch), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), _i32(block_table, 'block_table'), block_table.shape[1],
+        num_pages, P, _i32(ctx_lens, 'ctx_lens'), _ptr(out), Hq, Hkv, D,
+        _dtype(q), float(scale), int(bool(write_kv)), _ptr(workspace), ws_n,
+        _i32(err, 'err'), _stream(stream)))
+
+
+def gdn_verify_commit(batch, mode, state, q, k, v, alpha, beta, commit_len,
+                      out, state_slot=None, pending=None, err=None,
+                      stream=None):
+    """GDN verify / commit (``gdn_verify_commit``).
+
+    state fp32 [num_slots, H, dv, dk]; q/k [total_T, H, dk]; v/out
+    [total_T, H, dv]; alpha/beta fp32 [total_T, H]; commit_len int32 [B].
+    ``pending``: an ``SvGdnPending`` or None.
+    """
+    num_slots, H, dv, dk = state.shape
+    if state.dtype != torch.float32:
+        raise ValueError('state must be float32')
+    _check(lib().gdn_verify_commit(
+        ctypes.byref(batch), int(mode), _ptr(state), _i32(state_slot, 'state_slot'),
+        num_slots, _ptr(q), _ptr(k), _ptr(v), _dtype(k), _ptr(alpha), _ptr(beta),
+        _i32(commit_len, 'commit_len'), _ptr(out), H, dk, dv,
+        ctypes.byref(pending) if pending is not None else None,
+        _i32(err, 'err'), _stream(stream)))
+
+
+def make_gdn_pending(batch, k, v, alpha, beta, commit_len):
+    return SvGdnPending(batch, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                        _i32(commit_len, 'commit_len'))
+
+
+def spec_accept_workspace_bytes(B, total_T, V, mode):
+    return lib().spec_accept_workspace_bytes(B, total_T, V, mode)
+
+
+def spec_accept(batch, mode, target_logits, draft_tokens, result,
+                draft_logits=None, u_accept=None, u_final=None,
+                commit_len_out=None, ctx_lens_inout=None, workspace=None,
+                err=None, stream=None):
+    """Acceptance (``spec_accept``).  ``result`` int32 [B * (1 + max_T)]."""
+    V = target_logits.shape[1]
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().spec_accept(
+        ctypes.byref(batch), int(mode), _ptr(target_logits), _ptr(draft_logits),
+        _dtype(target_logits), V, _i32(draft_tokens, 'draft_tokens'),
+        _ptr(u_accept), _ptr(u_final), _i32(result, 'result'),
+        _i32(commit_len_out, 'commit_len_out'), _i32(ctx_lens_inout, 'ctx_lens'),
+        _ptr(workspace), ws_n, _i32(err, 'err'), _stream(stream)))
+
+
+class StepArgs:
+    """Host-side structures of one ``spec_verify_step`` call.
+
+    Keeps the ctypes arrays alive for as long as the object lives (the call
+    reads them only while it enqueues, so they can be reused step to step).
+    """
+
+    def __init__(self, layer_kind, attn_cfg, attn_layers, gdn_cfg, gdn_layers,
+                 accept_args):
+        self.layer_kind = (ctypes.c_uint8 * len(layer_kind))(*layer_kind)
+        self.n_layers = len(layer_kind)
+        self.attn_cfg = attn_cfg
+        self.attn = (SvAttnLayer * max(1, len(attn_layers)))(*attn_layers)
+        self.gdn_cfg = gdn_cfg
+        self.gdn = (SvGdnLayer * max(1, len(gdn_layers)))(*gdn_layers)
+        self.acc = accept_args
+
+
+def attn_config(Hq, Hkv, D, page_size, num_pages, block_table, dtype, scale=0.0):
+    return SvAttnConfig(Hq, Hkv, D, page_size, num_pages, block_table.shape[1],
+                        _i32(block_table, 'block_table'), dtype, float(scale))
+
+
+def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None):
+    return SvGdnConfig(H, dk, dv, num_slots, _i32(state_slot, 'state_slot'), io_dtype)
+
+
+def attn_layer(q, k_new, v_new, k_cache, v_cache, out):
+    return SvAttnLayer(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                       _ptr(v_cache), _ptr(out))
+
+
+def gdn_layer(state, q, k, v, alpha, beta, out):
+    return SvGdnLayer(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                      _ptr(beta), _ptr(out))
+
+
+def accept_args(mode, target_logits, draft_tokens, draft_logits=None,
+                u_accept=None, u_final=None):
+    return SvAcceptArgs(int(mode), _dtype(target_logits), target_logits.shape[1],
+                        _ptr(target_logits), _ptr(draft_logits),
+                        _i32(draft_tokens, 'draft_tokens'), _ptr(u_accept),
+                        _ptr(u_final))
+
+
+def spec_verify_step_workspace_bytes(batch, step_args):
+    a = step_args
+    has_attn = any(k == 1 for k in a.layer_kind)
+    return lib().spec_verify_step_workspace_bytes(
+        ctypes.byref(batch), ctypes.byref(a.attn_cfg) if has_attn else None,
+        ctypes.byref(a.acc))
+
+
+def spec_verify_step(batch, step_args, ctx_lens, result, commit_len,
+                     schedule=SV_SCHEDULE_TWO_PHASE, pending=None,
+                     workspace=None, err=None, stream=None):
+    """The whole step (``spec_verify_step``).  ``pending``: SvStepPending."""
+    a = step_args
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().spec_verify_step(
+        ctypes.byref(batch), a.n_layers, a.layer_kind,
+        ctypes.byref(a.attn_cfg) if a.attn_cfg is not None else None, a.attn,
+        ctypes.byref(a.gdn_cfg) if a.gdn_cfg is not None else None, a.gdn,
+        ctypes.byref(a.acc), _i32(ctx_lens, 'ctx_lens'), _i32(result, 'result'),
+        _i32(commit_len, 'commit_len'), int(schedule),
+        ctypes.byref(pending) if pending is not None else None,
+        _ptr(workspace), ws_n, _i32(err, 'err'), _stream(stream)))

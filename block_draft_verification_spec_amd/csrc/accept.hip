@@ -1,0 +1,480 @@
+// Acceptance of the verified drafts: greedy and rejection sampling.
+//
+// Greedy (onnxruntime-genai pull request 2457, greedy MTP step and the device
+// argmax of all verify rows read back once): g_i = argmax of target row i,
+// lowest index on ties; a = leading run of drafts equal to g_i; y = g_a.
+// Rejection sampling (Leviathan, Kalman & Matias 2023, Algorithm 1; Chen et
+// al. 2023), temperature 1: draft x_i passes iff u_i q_i(x_i) < p_i(x_i); at
+// the first failure y is drawn from max(0, p_i - q_i) (from p_i if that is all
+// zero), and after k passes from p_k, by inverse CDF in vocabulary order with
+// the supplied uniform: y = first index whose running sum exceeds u * total.
+// Output rows follow the lmdeploy reject sampler (pull request 3945, review of
+// reject_sampler.py): accepted drafts, then y, padded with -1.
+//
+// Kernels (all reductions that decide an integer run in fp64, so that the
+// decisions agree with an fp64 reference except on a set of uniforms of
+// measure ~1e-16 per decision):
+//   greedy:    row_argmax_partial  (chunk x row)  -> decide_greedy (sequence)
+//   rejection: row_stats_partial   (chunk x row)  -> decide_reject (sequence)
+//              -> residual_partial (chunk x seq)  -> final_draw    (sequence)
+// A chunk is 4096 vocabulary entries read by 256 threads with coalesced,
+// stride-256 element loads, so any V and any row alignment is supported.
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int kChunk = 4096;
+constexpr int kThreads = 256;
+constexpr int kPerThread = kChunk / kThreads;
+
+__host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Workspace layout (byte offsets are 256-aligned).
+struct AcceptWs {
+  size_t keys, stats, dec, fin, csum, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline AcceptWs accept_ws_layout(int B, int total_T, int V, int mode) {
+  AcceptWs w{};
+  const int nc = n_chunks(V);
+  size_t off = 0;
+  w.keys = off;   // greedy: uint64 [total_T][nc]
+  if (mode == SV_ACCEPT_GREEDY) off += align256(sizeof(unsigned long long) * size_t(total_T) * nc);
+  w.stats = off;  // rejection: double2 {chunk max, chunk sum} [rows][nc]
+  const int rows = 2 * total_T - B;
+  if (mode == SV_ACCEPT_REJECTION) off += align256(sizeof(double2) * size_t(rows) * nc);
+  w.dec = off;    // int4 per sequence {a, kind, target row, draft row}
+  off += align256(sizeof(int4) * size_t(B));
+  w.fin = off;    // double4 per sequence {Mt, Zt, Md, Zd}
+  off += align256(sizeof(double4) * size_t(B));
+  w.csum = off;   // double [B][nc]
+  off += align256(sizeof(double) * size_t(B) * nc);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld(const void* base, size_t i) {
+  return io<T>::load(base, i);
+}
+
+__device__ __forceinline__ unsigned long long argmax_key(float f, int idx) {
+  uint32_t u = __float_as_uint(f);
+  if (f == 0.f) u = 0;  // -0 == +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(ord) << 32) |
+         static_cast<unsigned long long>(0xffffffffu - static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ int key_index(unsigned long long key) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key & 0xffffffffu));
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sequence validation shared by the per-sequence kernels.
+__device__ __forceinline__ bool seq_ok(const AcceptArgs& a, int b, int* x0, int* T) {
+  *x0 = a.cu[b];
+  *T = a.cu[b + 1] - *x0;
+  // the k_b = T_b - 1 drafts sit at rows x0 - b .. x0 - b + T_b - 2
+  return *T >= 1 && *T <= a.max_T && *x0 >= b && *x0 + *T <= a.total_T &&
+         *x0 - b + *T - 1 <= a.total_T - a.B;
+}
+
+__device__ void write_outputs(const AcceptArgs& a, int b, int x0, int acc, int y) {
+  const int d0 = x0 - b;
+  int32_t* row = a.result + a.B + static_cast<size_t>(b) * a.max_T;
+  for (int j = 0; j < a.max_T; ++j)
+    row[j] = j < acc ? a.draft_tokens[d0 + j] : (j == acc ? y : -1);
+  a.result[b] = acc;
+  if (a.commit_len_out) a.commit_len_out[b] = acc + 1;
+  if (a.ctx_lens) a.ctx_lens[b] += acc + 1;
+}
+
+// ------------------------------------------------------------------ greedy
+template <typename T>
+__global__ __launch_bounds__(kThreads) void row_argmax_partial(AcceptArgs a) {
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nc = gridDim.x;
+  const size_t base = static_cast<size_t>(row) * a.V;
+  unsigned long long best = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int idx = chunk * kChunk + e * kThreads + tid;
+    if (idx < a.V) {
+      const unsigned long long key = argmax_key(ld<T>(a.target, base + idx), idx);
+      best = key > best ? key : best;
+    }
+  }
+  best = wave_max_u64(best);
+  __shared__ unsigned long long red[kThreads / 64];
+  if ((tid & 63) == 0) red[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / 64; ++w) best = red[w] > best ? red[w] : best;
+    const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+    reinterpret_cast<unsigned long long*>(static_cast<char*>(a.ws) + L.keys)
+        [static_cast<size_t>(row) * nc + chunk] = best;
+  }
+}
+
+__global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int x0, T;
+  if (!seq_ok(a, b, &x0, &T)) {
+    if (lane == 0) flag_error(a.err, SV_DERR_SEQLEN);
+    return;
+  }
+  const int nc = n_chunks(a.V);
+  const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  const unsigned long long* keys =
+      reinterpret_cast<const unsigned long long*>(static_cast<const char*>(a.ws) + L.keys);
+  const int d0 = x0 - b;
+  int acc = 0, y = -1;
+  for (int i = 0; i < T; ++i) {
+    unsigned long long best = 0;
+    for (int c = lane; c < nc; c += 64) {
+      const unsigned long long k = keys[static_cast<size_t>(x0 + i) * nc + c];
+      best = k > best ? k : best;
+    }
+    best = wave_max_u64(best);
+    const int g = key_index(best);
+    if (i == T - 1 || a.draft_tokens[d0 + i] != g) {
+      acc = i;
+      y = g;
+      break;
+    }
+  }
+  if (lane == 0) write_outputs(a, b, x0, acc, y);
+}
+
+// ------------------------------------------------------------------ rejection
+// Row r < total_T: target row r; otherwise draft row r - total_T.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
+  const int chunk = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nc = gridDim.x;
+  const void* src = r < a.total_T ? a.target : a.draft;
+  const size_t base = static_cast<size_t>(r < a.total_T ? r : r - a.total_T) * a.V;
+  float vals[kPerThread];
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int idx = chunk * kChunk + e * kThreads + tid;
+    vals[e] = idx < a.V ? ld<T>(src, base + idx) : -INFINITY;
+    m = fmaxf(m, vals[e]);
+  }
+  __shared__ float redm[kThreads / 64];
+  __shared__ double reds[kThreads / 64];
+  m = wave_max_f32(m);
+  if ((tid & 63) == 0) redm[tid >> 6] = m;
+  __syncthreads();
+  m = redm[0];
+  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, redm[w]);
+  double s = 0.0;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if (vals[e] > -INFINITY) s += exp(static_cast<double>(vals[e]) - static_cast<double>(m));
+  }
+  s = wave_sum_f64(s);
+  if ((tid & 63) == 0) reds[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    s = reds[0];
+    for (int w = 1; w < kThreads / 64; ++w) s += reds[w];
+    const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+    reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats)
+        [static_cast<size_t>(r) * nc + chunk] = make_double2(static_cast<double>(m), s);
+  }
+}
+
+// Combine the chunk statistics of one row: M = max, Z = sum_c z_c e^(m_c - M).
+__device__ double2 row_norm(const double2* stats, int row, int nc, int lane) {
+  double M = -INFINITY;
+  for (int c = lane; c < nc; c += 64) M = fmax(M, stats[static_cast<size_t>(row) * nc + c].x);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+  double Z = 0.0;
+  for (int c = lane; c < nc; c += 64) {
+    const double2 st = stats[static_cast<size_t>(row) * nc + c];
+    if (st.y > 0.0) Z += st.y * exp(st.x - M);
+  }
+  Z = wave_sum_f64(Z);
+  return make_double2(M, Z);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void decide_reject(AcceptArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  int4* dec = reinterpret_cast<int4*>(static_cast<char*>(a.ws) + L.dec);
+  int x0, tn;
+  if (!seq_ok(a, b, &x0, &tn)) {
+    if (lane == 0) {
+      flag_error(a.err, SV_DERR_SEQLEN);
+      dec[b] = make_int4(-1, -1, -1, -1);
+    }
+    return;
+  }
+  const int d0 = x0 - b;
+  for (int i = 0; i + 1 < tn; ++i) {
+    const int x = a.draft_tokens[d0 + i];
+    if (x < 0 || x >= a.V) {
+      if (lane == 0) {
+        flag_error(a.err, SV_DERR_TOKEN);
+        dec[b] = make_int4(-1, -1, -1, -1);
+      }
+      return;
+    }
+  }
+  const int nc = n_chunks(a.V);
+  const double2* stats = reinterpret_cast<const double2*>(static_cast<const char*>(a.ws) + L.stats);
+  double4* fin = reinterpret_cast<double4*>(static_cast<char*>(a.ws) + L.fin);
+  for (int i = 0; i + 1 < tn; ++i) {
+    const int x = a.draft_tokens[d0 + i];
+    const double2 nt = row_norm(stats, x0 + i, nc, lane);
+    const double2 nd = row_norm(stats, a.total_T + d0 + i, nc, lane);
+    const double p = exp(static_cast<double>(ld<T>(a.target, static_cast<size_t>(x0 + i) * a.V + x)) - nt.x) / nt.y;
+    const double q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(d0 + i) * a.V + x)) - nd.x) / nd.y;
+    const double u = static_cast<double>(a.u_accept[d0 + i]);
+    if (!(u * q < p)) {
+      if (lane == 0) {
+        dec[b] = make_int4(i, 1, x0 + i, d0 + i);   // kind 1: residual
+        fin[b] = make_double4(nt.x, nt.y, nd.x, nd.y);
+      }
+      return;
+    }
+  }
+  const double2 nt = row_norm(stats, x0 + tn - 1, nc, lane);
+  if (lane == 0) {
+    dec[b] = make_int4(tn - 1, 0, x0 + tn - 1, -1);   // kind 0: target row
+    fin[b] = make_double4(nt.x, nt.y, 0.0, 0.0);
+  }
+}
+
+// Weight of vocabulary entry y for the final draw of a sequence.
+template <typename T>
+__device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int rt, int rd,
+                                              const double4& f, int y) {
+  const double p = exp(static_cast<double>(ld<T>(a.target, static_cast<size_t>(rt) * a.V + y)) - f.x) / f.y;
+  if (kind == 0) return p;
+  const double q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(rd) * a.V + y)) - f.z) / f.w;
+  return fmax(p - q, 0.0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
+  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  const int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
+  if (d.x < 0) return;
+  const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
+  double s = 0.0;
+#pragma unroll 4
+  for (int e = 0; e < kPerThread; ++e) {
+    const int y = chunk * kChunk + e * kThreads + tid;
+    if (y < a.V) s += draw_weight<T>(a, d.y, d.z, d.w, f, y);
+  }
+  s = wave_sum_f64(s);
+  __shared__ double red[kThreads / 64];
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    s = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) s += red[w];
+    reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum)
+        [static_cast<size_t>(b) * gridDim.x + chunk] = s;
+  }
+}
+
+// Inverse-CDF search inside one chunk: returns the first y of the chunk whose
+// running sum (starting at `base`) exceeds t, or -1.  Block-wide, 256 threads;
+// each thread owns kPerThread consecutive entries.
+template <typename T>
+__device__ int chunk_search(const AcceptArgs& a, int kind, int rt, int rd, const double4& f,
+                            int chunk, double base, double t, int* last_pos) {
+  const int tid = threadIdx.x;
+  __shared__ double pre[kThreads];
+  __shared__ int found;
+  __shared__ int lastp;
+  double w[kPerThread];
+  double s = 0.0;
+  const int y0 = chunk * kChunk + tid * kPerThread;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int y = y0 + e;
+    w[e] = y < a.V ? draw_weight<T>(a, kind, rt, rd, f, y) : 0.0;
+    s += w[e];
+  }
+  pre[tid] = s;
+  if (tid == 0) {
+    found = 0x7fffffff;
+    lastp = -1;
+  }
+  __syncthreads();
+  if (tid == 0) {   // exclusive prefix over the 256 thread sums, in order
+    double run = base;
+    for (int i = 0; i < kThreads; ++i) {
+      const double v = pre[i];
+      pre[i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  double run = pre[tid];
+  int hit = -1, lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    run += w[e];
+    if (w[e] > 0.0) lastpos = y0 + e;
+    if (hit < 0 && run > t && w[e] > 0.0) hit = y0 + e;
+  }
+  if (hit >= 0) atomicMin(&found, hit);
+  if (lastpos >= 0) atomicMax(&lastp, lastpos);
+  __syncthreads();
+  *last_pos = lastp;
+  return found == 0x7fffffff ? -1 : found;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
+  if (d.x < 0) return;
+  const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
+  const int nc = n_chunks(a.V);
+  double* csum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum) + static_cast<size_t>(b) * nc;
+  __shared__ double total_s;
+  if (tid == 0) {
+    double tot = 0.0;
+    for (int c = 0; c < nc; ++c) tot += csum[c];
+    total_s = tot;
+  }
+  __syncthreads();
+  double total = total_s;
+  if (d.y == 1 && !(total > 0.0)) {
+    // p == q up to rounding: the residual is empty, draw from p instead.
+    d.y = 0;
+    __syncthreads();
+    for (int c = 0; c < nc; ++c) {
+      double s = 0.0;
+      for (int e = 0; e < kPerThread; ++e) {
+        const int y = c * kChunk + e * kThreads + tid;
+        if (y < a.V) s += draw_weight<T>(a, 0, d.z, d.w, f, y);
+      }
+      s = wave_sum_f64(s);
+      __shared__ double red[kThreads / 64];
+      if ((tid & 63) == 0) red[tid >> 6] = s;
+      __syncthreads();
+      if (tid == 0) {
+        double v = red[0];
+        for (int w = 1; w < kThreads / 64; ++w) v += red[w];
+        csum[c] = v;
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      double tot = 0.0;
+      for (int c = 0; c < nc; ++c) tot += csum[c];
+      total_s = tot;
+    }
+    __syncthreads();
+    total = total_s;
+  }
+  const double t = static_cast<double>(a.u_final[b]) * total;
+  // chunk whose inclusive running sum first exceeds t
+  __shared__ int chunk_s;
+  __shared__ double base_s;
+  if (tid == 0) {
+    double run = 0.0;
+    int cidx = -1;
+    double base = 0.0;
+    for (int c = 0; c < nc; ++c) {
+      if (run + csum[c] > t && csum[c] > 0.0) {
+        cidx = c;
+        base = run;
+        break;
+      }
+      run += csum[c];
+    }
+    chunk_s = cidx;
+    base_s = base;
+  }
+  __syncthreads();
+  int y = -1;
+  int chunk = chunk_s;
+  if (chunk < 0) {
+    // rounding left no crossing: last index with positive weight
+    for (int c = nc - 1; c >= 0 && y < 0; --c) {
+      if (!(csum[c] > 0.0)) continue;
+      int lastp;
+      chunk_search<T>(a, d.y, d.z, d.w, f, c, 0.0, INFINITY, &lastp);
+      y = lastp;
+    }
+  } else {
+    int lastp;
+    y = chunk_search<T>(a, d.y, d.z, d.w, f, chunk, base_s, t, &lastp);
+    if (y < 0) y = lastp;
+  }
+  if (tid == 0) {
+    int x0, tn;
+    seq_ok(a, b, &x0, &tn);
+    write_outputs(a, b, x0, d.x, y);
+  }
+}
+
+template <typename T>
+hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
+  const int nc = n_chunks(a.V);
+  if (a.mode == SV_ACCEPT_GREEDY) {
+    hipLaunchKernelGGL((row_argmax_partial<T>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
+  } else {
+    const int rows = 2 * a.total_T - a.B;
+    hipLaunchKernelGGL((row_stats_partial<T>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((final_draw<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t accept_workspace_bytes(int B, int total_T, int V, int mode) {
+  return accept_ws_layout(B, total_T, V, mode).total;
+}
+
+hipError_t launch_accept(const AcceptArgs& a, sv_dtype dtype, hipStream_t stream) {
+  return dtype == SV_BF16 ? launch_typed<bf16_t>(a, stream) : launch_typed<float>(a, stream);
+}
+
+}  // namespace sv

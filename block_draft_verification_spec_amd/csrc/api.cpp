@@ -1,0 +1,400 @@
+// C ABI of the verification library: host-side validation and launch order.
+// Every entry point checks its arguments, returns a status (never aborts)
+// and only enqueues kernels on the caller's stream.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+#include "spec_verify.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sv_status fail(sv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sv_status ok() {
+  g_last_error.clear();
+  return SV_OK;
+}
+
+sv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+sv_status check_batch(const sv_batch* b, const char* who) {
+  if (!b) return fail(SV_EINVAL, "%s: batch is null", who);
+  if (b->B < 1) return fail(SV_EINVAL, "%s: B must be >= 1 (got %d)", who, b->B);
+  if (b->max_T < 1 || b->max_T > sv::kMaxT)
+    return fail(SV_ECAPACITY, "%s: max_T must be in 1..%d (got %d)", who, sv::kMaxT, b->max_T);
+  if (b->total_T < b->B || static_cast<long long>(b->total_T) > static_cast<long long>(b->B) * b->max_T)
+    return fail(SV_EINVAL, "%s: total_T=%d inconsistent with B=%d, max_T=%d", who, b->total_T,
+                b->B, b->max_T);
+  if (!b->cu_seqlens) return fail(SV_EINVAL, "%s: cu_seqlens is null", who);
+  return SV_OK;
+}
+
+sv_status check_attn(const sv_batch* batch, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, const int32_t* block_table,
+                     int32_t max_pages, int32_t num_pages, int32_t P, const int32_t* ctx_lens,
+                     void* out, int32_t Hq, int32_t Hkv, int32_t D, sv_dtype dtype) {
+  const char* who = "spec_verify_attention";
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !ctx_lens || !out)
+    return fail(SV_EINVAL, "%s: a required pointer is null", who);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(SV_EINVAL, "%s: Hq=%d must be a positive multiple of Hkv=%d", who, Hq, Hkv);
+  if (P < 1 || max_pages < 1 || num_pages < 1)
+    return fail(SV_EINVAL, "%s: page_size, max_pages_per_seq, num_pages must be >= 1", who);
+  if (dtype == SV_BF16) {
+    if (D != 64 && D != 128) return fail(SV_EDTYPE, "%s: bf16 path needs D in {64,128} (got %d)", who, D);
+    if (!(P % 64 == 0 || 64 % P == 0))
+      return fail(SV_EINVAL, "%s: page_size %d must divide or be a multiple of 64", who, P);
+    if ((Hq / Hkv) * batch->max_T > 64)
+      return fail(SV_ECAPACITY, "%s: (Hq/Hkv)*max_T = %d exceeds 64 query rows", who,
+                  (Hq / Hkv) * batch->max_T);
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
+         reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) & 15)
+      return fail(SV_EINVAL, "%s: bf16 tensors must be 16-byte aligned", who);
+  } else if (dtype == SV_F32) {
+    if (D < 1 || D > 128) return fail(SV_EDTYPE, "%s: fp32 path needs 1 <= D <= 128 (got %d)", who, D);
+  } else {
+    return fail(SV_EDTYPE, "%s: unsupported dtype %d", who, static_cast<int>(dtype));
+  }
+  return SV_OK;
+}
+
+sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_new,
+                            const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* block_table, int32_t max_pages, int32_t num_pages,
+                            int32_t P, const int32_t* ctx_lens, void* out, int32_t Hq,
+                            int32_t Hkv, int32_t D, sv_dtype dtype, float scale, int32_t write_kv,
+                            void* ws, int32_t* err) {
+  sv::AttnArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.P = P;
+  a.ctx_lens = ctx_lens;
+  a.out = out;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.scale = scale == 0.f ? 1.f / std::sqrt(static_cast<float>(D)) : scale;
+  a.write_kv = write_kv ? 1 : 0;
+  a.err = err;
+  if (dtype == SV_BF16) {
+    sv::attn_split_plan(a.B, Hkv, max_pages, P, &a.nsplit, &a.tiles_per_split);
+    const size_t rows = static_cast<size_t>(a.total_T) * Hq * a.nsplit;
+    const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~size_t(255);
+    a.part_o = static_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+  }
+  return a;
+}
+
+sv_status check_gdn_common(const sv_batch* batch, float* state, int32_t num_slots,
+                           sv_dtype io_dtype, int32_t H, int32_t dk, int32_t dv, const char* who) {
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  if (!state) return fail(SV_EINVAL, "%s: state is null", who);
+  if (num_slots < 1) return fail(SV_EINVAL, "%s: num_slots must be >= 1", who);
+  if (io_dtype != SV_F32 && io_dtype != SV_BF16)
+    return fail(SV_EDTYPE, "%s: unsupported io dtype %d", who, static_cast<int>(io_dtype));
+  if (dk != 64 && dk != 128) return fail(SV_EDTYPE, "%s: dk must be 64 or 128 (got %d)", who, dk);
+  if (dv < 64 || dv > 256 || dv % 64 != 0)
+    return fail(SV_EDTYPE, "%s: dv must be a multiple of 64 up to 256 (got %d)", who, dv);
+  if (H < 1) return fail(SV_EINVAL, "%s: H must be >= 1", who);
+  if (reinterpret_cast<uintptr_t>(state) & 15)
+    return fail(SV_EINVAL, "%s: state must be 16-byte aligned", who);
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_last_error(void) { return g_last_error.c_str(); }
+
+const char* sv_version(void) { return "specverify 0.1 gfx950"; }
+
+size_t spec_verify_attention_workspace_bytes(int32_t B, int32_t total_T, int32_t Hq, int32_t Hkv,
+                                             int32_t D, int32_t max_pages_per_seq,
+                                             int32_t page_size, sv_dtype dtype) {
+  if (B < 1 || total_T < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_pages_per_seq < 1 || page_size < 1)
+    return 0;
+  return sv::attn_workspace_bytes(B, total_T, Hq, Hkv, D, max_pages_per_seq, page_size, dtype);
+}
+
+sv_status spec_verify_attention(const sv_batch* batch, const void* q, const void* k_new,
+                                const void* v_new, void* k_cache, void* v_cache,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                int32_t num_pages, int32_t page_size, const int32_t* ctx_lens,
+                                void* out, int32_t Hq, int32_t Hkv, int32_t D, sv_dtype dtype,
+                                float scale, int32_t write_kv, void* workspace,
+                                size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  sv_status st = check_attn(batch, q, k_new, v_new, k_cache, v_cache, block_table,
+                            max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv, D,
+                            dtype);
+  if (st != SV_OK) return st;
+  const size_t need = sv::attn_workspace_bytes(batch->B, batch->total_T, Hq, Hkv, D,
+                                               max_pages_per_seq, page_size, dtype);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SV_EWORKSPACE, "spec_verify_attention: workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : size_t(0));
+  sv::AttnArgs a = make_attn_args(batch, q, k_new, v_new, k_cache, v_cache, block_table,
+                                  max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv,
+                                  D, dtype, scale, write_kv, workspace, err);
+  return hip_status(sv::launch_attention(a, dtype, stream), "spec_verify_attention");
+}
+
+sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, float* state,
+                            const int32_t* state_slot, int32_t num_slots, const void* q,
+                            const void* k, const void* v, sv_dtype io_dtype, const float* alpha,
+                            const float* beta, const int32_t* commit_len, void* out, int32_t H,
+                            int32_t dk, int32_t dv, const sv_gdn_pending* pending, int32_t* err,
+                            hipStream_t stream) {
+  const char* who = "gdn_verify_commit";
+  sv_status st = check_gdn_common(batch, state, num_slots, io_dtype, H, dk, dv, who);
+  if (st != SV_OK) return st;
+  if (mode != SV_GDN_VERIFY_COMMIT && mode != SV_GDN_VERIFY_ONLY && mode != SV_GDN_COMMIT_ONLY)
+    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
+  if (!k || !v || !alpha || !beta) return fail(SV_EINVAL, "%s: k, v, alpha, beta are required", who);
+  if (mode != SV_GDN_COMMIT_ONLY && (!q || !out))
+    return fail(SV_EINVAL, "%s: q and out are required unless COMMIT_ONLY", who);
+  if (mode != SV_GDN_VERIFY_ONLY && !commit_len)
+    return fail(SV_EINVAL, "%s: commit_len is required unless VERIFY_ONLY", who);
+  if (!state_slot && num_slots < batch->B)
+    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  sv::GdnScalars s{};
+  s.B = batch->B;
+  s.total_T = batch->total_T;
+  s.max_T = batch->max_T;
+  s.cu = batch->cu_seqlens;
+  s.mode = mode;
+  s.state_slot = state_slot;
+  s.num_slots = num_slots;
+  s.commit_len = commit_len;
+  s.H = H;
+  s.dk = dk;
+  s.dv = dv;
+  s.err = err;
+  sv::GdnFullPtrs p{};
+  p.state = state;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.out = out;
+  if (pending) {
+    st = check_batch(&pending->batch, "gdn_verify_commit (pending)");
+    if (st != SV_OK) return st;
+    if (pending->batch.B != batch->B)
+      return fail(SV_EINVAL, "%s: pending batch has B=%d, this batch B=%d", who,
+                  pending->batch.B, batch->B);
+    if (!pending->k || !pending->v || !pending->alpha || !pending->beta || !pending->commit_len)
+      return fail(SV_EINVAL, "%s: pending k, v, alpha, beta, commit_len are required", who);
+    s.has_pending = 1;
+    s.p_total_T = pending->batch.total_T;
+    s.p_max_T = pending->batch.max_T;
+    s.p_cu = pending->batch.cu_seqlens;
+    s.p_commit = pending->commit_len;
+    p.pk = pending->k;
+    p.pv = pending->v;
+    p.palpha = pending->alpha;
+    p.pbeta = pending->beta;
+  }
+  return hip_status(sv::launch_gdn(s, p, io_dtype, stream), who);
+}
+
+size_t spec_accept_workspace_bytes(int32_t B, int32_t total_T, int32_t V, sv_accept_mode mode) {
+  if (B < 1 || total_T < 1 || V < 1) return 0;
+  return sv::accept_workspace_bytes(B, total_T, V, mode);
+}
+
+sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode, const void* target_logits,
+                      const void* draft_logits, sv_dtype logit_dtype, int32_t V,
+                      const int32_t* draft_tokens, const float* u_accept, const float* u_final,
+                      int32_t* result, int32_t* commit_len_out, int32_t* ctx_lens_inout,
+                      void* workspace, size_t workspace_bytes, int32_t* err,
+                      hipStream_t stream) {
+  const char* who = "spec_accept";
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  if (mode != SV_ACCEPT_GREEDY && mode != SV_ACCEPT_REJECTION)
+    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
+  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+    return fail(SV_EDTYPE, "%s: unsupported logit dtype %d", who, static_cast<int>(logit_dtype));
+  if (V < 1) return fail(SV_EINVAL, "%s: V must be >= 1", who);
+  if (!target_logits || !result) return fail(SV_EINVAL, "%s: target_logits and result are required", who);
+  if (batch->total_T > batch->B && !draft_tokens)
+    return fail(SV_EINVAL, "%s: draft_tokens is required when there are drafts", who);
+  if (mode == SV_ACCEPT_REJECTION && (!u_final || (batch->total_T > batch->B && (!draft_logits || !u_accept))))
+    return fail(SV_EINVAL, "%s: rejection needs draft_logits, u_accept and u_final", who);
+  const size_t need = sv::accept_workspace_bytes(batch->B, batch->total_T, V, mode);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
+                workspace ? workspace_bytes : size_t(0));
+  sv::AcceptArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.mode = mode;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.V = V;
+  a.draft_tokens = draft_tokens;
+  a.u_accept = u_accept;
+  a.u_final = u_final;
+  a.result = result;
+  a.commit_len_out = commit_len_out;
+  a.ctx_lens = ctx_lens_inout;
+  a.err = err;
+  a.ws = workspace;
+  return hip_status(sv::launch_accept(a, logit_dtype, stream), who);
+}
+
+size_t spec_verify_step_workspace_bytes(const sv_batch* batch, const sv_attn_config* acfg,
+                                        const sv_accept_args* acc) {
+  if (!batch || batch->B < 1 || batch->total_T < 1) return 0;
+  size_t need = 0;
+  if (acfg)
+    need = std::max(need, sv::attn_workspace_bytes(batch->B, batch->total_T, acfg->Hq, acfg->Hkv,
+                                                   acfg->D, acfg->max_pages_per_seq,
+                                                   acfg->page_size, acfg->dtype));
+  if (acc && acc->V >= 1)
+    need = std::max(need, sv::accept_workspace_bytes(batch->B, batch->total_T, acc->V, acc->mode));
+  return need;
+}
+
+sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_t* layer_kind,
+                           const sv_attn_config* acfg, const sv_attn_layer* attn,
+                           const sv_gdn_config* gcfg, const sv_gdn_layer* gdn,
+                           const sv_accept_args* acc, int32_t* ctx_lens, int32_t* result,
+                           int32_t* commit_len, sv_schedule schedule,
+                           const sv_step_pending* pending, void* workspace,
+                           size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  const char* who = "spec_verify_step";
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  if (n_layers < 0 || (n_layers > 0 && !layer_kind))
+    return fail(SV_EINVAL, "%s: layer_kind is required", who);
+  if (!acc || !ctx_lens || !result || !commit_len)
+    return fail(SV_EINVAL, "%s: accept args, ctx_lens, result and commit_len are required", who);
+  if (schedule != SV_SCHEDULE_TWO_PHASE && schedule != SV_SCHEDULE_DEFERRED)
+    return fail(SV_EINVAL, "%s: unknown schedule %d", who, static_cast<int>(schedule));
+  int n_attn = 0, n_gdn = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (layer_kind[l] == 1) ++n_attn;
+    else if (layer_kind[l] == 0) ++n_gdn;
+    else return fail(SV_EINVAL, "%s: layer_kind[%d] = %d is neither 0 nor 1", who, l, layer_kind[l]);
+  }
+  if (n_attn && (!acfg || !attn)) return fail(SV_EINVAL, "%s: attention config/layers missing", who);
+  if (n_gdn && (!gcfg || !gdn)) return fail(SV_EINVAL, "%s: GDN config/layers missing", who);
+  if (pending && schedule != SV_SCHEDULE_DEFERRED)
+    return fail(SV_EINVAL, "%s: pending tokens are only used by the deferred schedule", who);
+  if (pending && (!pending->layers || !pending->commit_len))
+    return fail(SV_EINVAL, "%s: pending layers and commit_len are required", who);
+  const size_t need = spec_verify_step_workspace_bytes(batch, n_attn ? acfg : nullptr, acc);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
+                workspace ? workspace_bytes : size_t(0));
+
+  // 1. verify every layer in model order
+  int ia = 0, ig = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (layer_kind[l] == 1) {
+      const sv_attn_layer& L = attn[ia++];
+      st = spec_verify_attention(batch, L.q, L.k_new, L.v_new, L.k_cache, L.v_cache,
+                                 acfg->block_table, acfg->max_pages_per_seq, acfg->num_pages,
+                                 acfg->page_size, ctx_lens, L.out, acfg->Hq, acfg->Hkv, acfg->D,
+                                 acfg->dtype, acfg->scale, 1, workspace, workspace_bytes, err,
+                                 stream);
+    } else {
+      const sv_gdn_layer& G = gdn[ig];
+      sv_gdn_pending pg{};
+      const sv_gdn_pending* pp = nullptr;
+      if (pending) {
+        const sv_gdn_layer& P = pending->layers[ig];
+        pg.batch = pending->batch;
+        pg.k = P.k;
+        pg.v = P.v;
+        pg.alpha = P.alpha;
+        pg.beta = P.beta;
+        pg.commit_len = pending->commit_len;
+        pp = &pg;
+      }
+      ++ig;
+      st = gdn_verify_commit(batch, SV_GDN_VERIFY_ONLY, G.state, gcfg->state_slot,
+                             gcfg->num_slots, G.q, G.k, G.v, gcfg->io_dtype, G.alpha, G.beta,
+                             nullptr, G.out, gcfg->H, gcfg->dk, gcfg->dv, pp, err, stream);
+    }
+    if (st != SV_OK) return st;
+  }
+  // 2. acceptance (ctx_lens is advanced by a+1 here, after every attention layer)
+  st = spec_accept(batch, acc->mode, acc->target_logits, acc->draft_logits, acc->logit_dtype,
+                   acc->V, acc->draft_tokens, acc->u_accept, acc->u_final, result, commit_len,
+                   ctx_lens, workspace, workspace_bytes, err, stream);
+  if (st != SV_OK) return st;
+  // 3. two-phase: commit the first a+1 tokens of every GDN layer
+  if (schedule == SV_SCHEDULE_TWO_PHASE && n_gdn > 0) {
+    sv_status cs = check_gdn_common(batch, gdn[0].state, gcfg->num_slots, gcfg->io_dtype, gcfg->H,
+                                    gcfg->dk, gcfg->dv, who);
+    if (cs != SV_OK) return cs;
+    sv::GdnScalars s{};
+    s.B = batch->B;
+    s.total_T = batch->total_T;
+    s.max_T = batch->max_T;
+    s.cu = batch->cu_seqlens;
+    s.mode = SV_GDN_COMMIT_ONLY;
+    s.state_slot = gcfg->state_slot;
+    s.num_slots = gcfg->num_slots;
+    s.commit_len = commit_len;
+    s.H = gcfg->H;
+    s.dk = gcfg->dk;
+    s.dv = gcfg->dv;
+    s.err = err;
+    for (int l0 = 0; l0 < n_gdn; l0 += sv::kGdnLayersPerLaunch) {
+      const int nl = std::min(sv::kGdnLayersPerLaunch, n_gdn - l0);
+      sv::GdnCommitTable t{};
+      for (int i = 0; i < nl; ++i) {
+        const sv_gdn_layer& G = gdn[l0 + i];
+        if (!G.state || !G.k || !G.v || !G.alpha || !G.beta)
+          return fail(SV_EINVAL, "%s: GDN layer %d lacks state/k/v/alpha/beta", who, l0 + i);
+        t.l[i] = sv::GdnCommitPtrs{G.state, G.k, G.v, G.alpha, G.beta};
+      }
+      st = hip_status(sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, stream), who);
+      if (st != SV_OK) return st;
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

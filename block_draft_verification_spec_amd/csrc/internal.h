@@ -1,0 +1,104 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+constexpr int kMaxT = 8;                 // verify tokens per sequence
+constexpr int kGdnLayersPerLaunch = 48;  // layers in one batched commit launch
+
+// ---------------------------------------------------------------- GDN
+struct GdnScalars {
+  int B, total_T, max_T;
+  const int32_t* cu;            // [B+1]
+  int mode;                     // sv_gdn_mode
+  const int32_t* state_slot;    // [B] or null
+  int num_slots;
+  const int32_t* commit_len;    // [B] or null (VERIFY_ONLY)
+  int H, dk, dv;
+  int has_pending;
+  int p_total_T, p_max_T;
+  const int32_t* p_cu;          // [B+1]
+  const int32_t* p_commit;      // [B]
+  int32_t* err;
+};
+
+struct GdnFullPtrs {
+  float* state;
+  const void* q; const void* k; const void* v;
+  const float* alpha; const float* beta;
+  void* out;
+  const void* pk; const void* pv; const float* palpha; const float* pbeta;
+};
+
+struct GdnCommitPtrs {
+  float* state;
+  const void* k; const void* v;
+  const float* alpha; const float* beta;
+};
+
+struct GdnCommitTable {
+  GdnCommitPtrs l[kGdnLayersPerLaunch];
+};
+
+hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io,
+                      hipStream_t stream);
+// COMMIT_ONLY over n_layers (<= kGdnLayersPerLaunch) layers in one launch.
+hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
+                                   int n_layers, sv_dtype io, hipStream_t stream);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  int B, total_T, max_T;
+  const int32_t* cu;
+  const void* q; const void* k_new; const void* v_new;
+  void* k_cache; void* v_cache;
+  const int32_t* block_table;
+  int max_pages, num_pages, P;
+  const int32_t* ctx_lens;
+  void* out;
+  int Hq, Hkv, D;
+  float scale;                  // already resolved (never 0)
+  int write_kv;
+  int32_t* err;
+  // split-KV partials
+  float* part_o;                // [total_T, Hq, nsplit, D]
+  float* part_ml;               // [total_T, Hq, nsplit, 2]
+  int nsplit;                   // splits per sequence (grid.x)
+  int tiles_per_split;          // 64-key tiles per split
+};
+
+// Number of splits and tiles per split for a launch (host decision).
+void attn_split_plan(int B, int Hkv, int max_pages, int P, int* nsplit,
+                     int* tiles_per_split);
+size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D,
+                            int max_pages, int P, sv_dtype dtype);
+hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype,
+                            hipStream_t stream);
+
+// ---------------------------------------------------------------- accept
+struct AcceptArgs {
+  int B, total_T, max_T;
+  const int32_t* cu;
+  int mode;                     // sv_accept_mode
+  const void* target; const void* draft;
+  int V;
+  const int32_t* draft_tokens;
+  const float* u_accept; const float* u_final;
+  int32_t* result;
+  int32_t* commit_len_out;
+  int32_t* ctx_lens;
+  int32_t* err;
+  void* ws;
+};
+
+size_t accept_workspace_bytes(int B, int total_T, int V, int mode);
+hipError_t launch_accept(const AcceptArgs& a, sv_dtype dtype,
+                         hipStream_t stream);
+
+}  // namespace sv

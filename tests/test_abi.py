@@ -1,0 +1,152 @@
+"""The C-ABI library loads and exports every symbol include/*.h declares, and
+its host-side validation rejects bad arguments with a status (no GPU work)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from block_draft_verification_spec_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, 'include', '*.h')):
+        text = open(h).read()
+        text = re.sub(r'/\*.*?\*/', '', text, flags=re.S)
+        for m in re.finditer(r'SV_API\s+[\w\s\*]+?\b(\w+)\s*\(', text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {'spec_verify_attention', 'gdn_verify_commit', 'spec_accept',
+            'spec_verify_step', 'sv_last_error'} <= names
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_empty_error():
+    assert 'gfx950' in bd.version()
+
+
+def _batch(B=2, max_T=4, total_T=8, cu=1):
+    return bd.SvBatch(B, max_T, total_T, cu)
+
+
+@pytest.mark.parametrize("B,max_T,total_T,msg", [
+    (0, 4, 8, 'B must be'),
+    (2, 9, 8, 'max_T'),
+    (2, 0, 8, 'max_T'),
+    (2, 4, 1, 'inconsistent'),
+    (2, 4, 9, 'inconsistent'),
+])
+def test_batch_validation(B, max_T, total_T, msg):
+    L = bd.lib()
+    b = _batch(B, max_T, total_T)
+    st = L.spec_accept(ctypes.byref(b), 0, 8, None, 1, 10, 8, None, None, 8,
+                       None, None, 8, 1 << 20, None, None)
+    assert st != bd.SV_OK
+    assert msg in L.sv_last_error().decode()
+
+
+def test_attention_validation():
+    L = bd.lib()
+    b = _batch()
+    args = dict(q=16, k=16, v=16, kc=16, vc=16, bt=16, maxp=4, npages=8, P=64,
+                ctx=16, out=16, Hq=32, Hkv=8, D=128, dt=bd.SV_BF16)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.spec_verify_attention(
+            ctypes.byref(b), a['q'], a['k'], a['v'], a['kc'], a['vc'], a['bt'],
+            a['maxp'], a['npages'], a['P'], a['ctx'], a['out'], a['Hq'],
+            a['Hkv'], a['D'], a['dt'], 0.0, 1, 16, 0, None, None)
+    assert call(Hq=30) == bd.SV_EINVAL                       # Hq % Hkv
+    assert call(D=96) == bd.SV_EDTYPE                        # bf16 head size
+    assert call(P=48) == bd.SV_EINVAL                        # page size
+    assert call(q=None) == bd.SV_EINVAL
+    assert call(dt=7) == bd.SV_EDTYPE
+    assert call(Hq=64, Hkv=2) == bd.SV_ECAPACITY             # 32 heads x 4 > 64 rows
+    assert call(q=24) == bd.SV_EINVAL                        # misaligned
+    assert call() == bd.SV_EWORKSPACE                        # workspace too small
+    assert 'workspace' in L.sv_last_error().decode()
+
+
+def test_gdn_validation():
+    L = bd.lib()
+    b = _batch()
+
+    def call(mode=0, state=16, dk=128, dv=128, q=16, out=16, commit=16, slots=2,
+             io=bd.SV_BF16):
+        return L.gdn_verify_commit(ctypes.byref(b), mode, state, None, slots, q,
+                                   16, 16, io, 16, 16, commit, out, 4, dk, dv,
+                                   None, None, None)
+    assert call(dk=96) == bd.SV_EDTYPE
+    assert call(dv=96) == bd.SV_EDTYPE
+    assert call(state=None) == bd.SV_EINVAL
+    assert call(mode=0, commit=None) == bd.SV_EINVAL         # commit_len required
+    assert call(mode=1, q=None) == bd.SV_EINVAL              # q required
+    assert call(mode=5) == bd.SV_EINVAL
+    assert call(slots=1) == bd.SV_EINVAL                     # identity map needs B slots
+    assert call(io=3) == bd.SV_EDTYPE
+    assert call(state=20) == bd.SV_EINVAL                    # misaligned state
+
+
+def test_accept_validation():
+    L = bd.lib()
+    b = _batch()
+
+    def call(mode=1, target=16, draft=16, ua=16, uf=16, dt=None, res=16, ws=16,
+             wsn=1 << 30, V=100, dtype=bd.SV_BF16):
+        return L.spec_accept(ctypes.byref(b), mode, target, draft, dtype, V,
+                             16 if dt is None else dt, ua, uf, res, None, None, ws,
+                             wsn, None, None)
+    assert call(draft=None) == bd.SV_EINVAL
+    assert call(uf=None) == bd.SV_EINVAL
+    assert call(mode=0, draft=None, ua=None, uf=None, wsn=4) == bd.SV_EWORKSPACE
+    assert call(res=None) == bd.SV_EINVAL
+    assert call(V=0) == bd.SV_EINVAL
+    assert call(dtype=9) == bd.SV_EDTYPE
+    assert call(mode=4) == bd.SV_EINVAL
+
+
+def test_step_validation():
+    L = bd.lib()
+    b = _batch()
+    kinds = (ctypes.c_uint8 * 2)(0, 2)
+    acc = bd.SvAcceptArgs(0, bd.SV_BF16, 100, 16, None, 16, None, None)
+    st = L.spec_verify_step(ctypes.byref(b), 2, kinds, None, None, None, None,
+                            ctypes.byref(acc), 16, 16, 16, 0, None, 16, 1 << 30,
+                            None, None)
+    assert st == bd.SV_EINVAL and 'layer_kind' in L.sv_last_error().decode()
+    kinds = (ctypes.c_uint8 * 1)(1)
+    st = L.spec_verify_step(ctypes.byref(b), 1, kinds, None, None, None, None,
+                            ctypes.byref(acc), 16, 16, 16, 0, None, 16, 1 << 30,
+                            None, None)
+    assert st == bd.SV_EINVAL and 'attention' in L.sv_last_error().decode()
+
+
+def test_workspace_sizes_are_consistent():
+    L = bd.lib()
+    a = L.spec_verify_attention_workspace_bytes(64, 256, 32, 8, 128, 130, 64, bd.SV_BF16)
+    assert a > 256 * 32 * 128 * 4
+    assert L.spec_verify_attention_workspace_bytes(64, 256, 32, 8, 128, 130, 64, bd.SV_F32) == 0
+    g = L.spec_accept_workspace_bytes(64, 256, 151936, bd.SV_ACCEPT_GREEDY)
+    r = L.spec_accept_workspace_bytes(64, 256, 151936, bd.SV_ACCEPT_REJECTION)
+    assert 0 < g < r
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    b = _batch()
+    with pytest.raises((ValueError, RuntimeError)):
+        bd.spec_accept(b, 0, torch.zeros(8, 100, dtype=torch.bfloat16),
+                       torch.zeros(6, dtype=torch.int32),
+                       torch.zeros(10, dtype=torch.int32))

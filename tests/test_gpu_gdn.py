@@ -1,0 +1,178 @@
+"""GPU parity of gdn_verify_commit against the oracle (through the C ABI).
+
+Tolerances: committed state max|dS| / max|S_ref| <= 1e-4 per (b, h) tile;
+outputs max-abs <= 2e-3 (fp32 I/O) or <= 1e-2 + half a bf16 ulp of |o_ref|
+(bf16 I/O).  Self-consistency checks on the GPU are bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from block_draft_verification_spec_amd import binding as bd
+from gpu_helpers import (DEV, check_gdn_out, check_gdn_state, err_word, np64, npi,
+                         say, sv_batch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(batch, g, mode, commit, slots=None, pending=None, state=None):
+    out = torch.full_like(g['v'], float('nan'))
+    st = (g['state'] if state is None else state).clone()
+    err = err_word()
+    bd.gdn_verify_commit(sv_batch(batch), mode, st, g['q'], g['k'], g['v'],
+                         g['alpha'], g['beta'], commit, out, state_slot=slots,
+                         pending=pending, err=err)
+    torch.cuda.synchronize()
+    return out, st, int(err.item())
+
+
+def _oracle(batch, g, mode, commit, slots=None):
+    return oracle.gdn_step(np64(g['state']), None if slots is None else npi(slots),
+                           np64(g['q']), np64(g['k']), np64(g['v']), np64(g['alpha']),
+                           np64(g['beta']), npi(batch.cu_seqlens),
+                           None if commit is None else npi(commit), mode)
+
+
+MODES = [bd.SV_GDN_VERIFY_COMMIT, bd.SV_GDN_VERIFY_ONLY, bd.SV_GDN_COMMIT_ONLY]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_fp32_all_modes(mode):
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 0, DEV)
+    g = wl.make_gdn_layer(w, batch, 1, DEV)
+    commit = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
+    say('tiny fp32 GDN mode', mode)
+    out, st, err = _run(batch, g, mode, commit)
+    assert err == 0
+    o_ref, S_ref = _oracle(batch, g, mode, None if mode == bd.SV_GDN_VERIFY_ONLY else commit)
+    check_gdn_state(np64(st), S_ref)
+    if mode != bd.SV_GDN_COMMIT_ONLY:
+        check_gdn_out(np64(out), o_ref, torch.float32)
+    if mode == bd.SV_GDN_VERIFY_ONLY:
+        assert torch.equal(st, g['state'])
+
+
+@pytest.mark.parametrize("seed", [2, 102])
+def test_full_size_verify_commit_bf16(seed):
+    w = wl.WORKLOADS[2]
+    batch = wl.make_batch(w, seed, DEV)
+    g = wl.make_gdn_layer(w, batch, seed + 1, DEV)
+    commit = wl.make_commit_len(batch, seed + 2, device=DEV)
+    say('GDN full-size VERIFY_COMMIT seed', seed)
+    out, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert err == 0
+    o_ref, S_ref = _oracle(batch, g, oracle.GDN_VERIFY_COMMIT, commit)
+    e_s = check_gdn_state(np64(st), S_ref)
+    e_o = check_gdn_out(np64(out), o_ref, torch.bfloat16)
+    say(f'  state err {e_s:.2e}  out err {e_o:.2e}')
+    # COMMIT_ONLY gives the same state bit for bit; VERIFY_ONLY leaves it alone
+    _, st2, _ = _run(batch, g, bd.SV_GDN_COMMIT_ONLY, commit)
+    assert torch.equal(st2, st)
+    out3, st3, _ = _run(batch, g, bd.SV_GDN_VERIFY_ONLY, None)
+    assert torch.equal(st3, g['state'])
+    assert torch.equal(out3, out)
+
+
+def test_ragged_slots_and_head_sizes():
+    for dk, dv, dt in [(64, 128, torch.float32), (128, 64, torch.bfloat16),
+                       (64, 64, torch.bfloat16), (128, 256, torch.float32)]:
+        w = wl.Workload('gdn_ragged', B=9, k=7, ragged_k=True, ctx=(0, 0), H=3,
+                        dk=dk, dv=dv, gdn_dtype=dt)
+        batch = wl.make_batch(w, 5, DEV)
+        g = wl.make_gdn_layer(w, batch, 6, DEV, num_slots=13)
+        slots = wl.make_state_slots(batch, 13, 7, DEV)
+        T = torch.tensor(batch.T)
+        commit = (torch.arange(batch.B) % (T + 1)).to(torch.int32).to(DEV)
+        say('GDN ragged dk', dk, 'dv', dv, dt)
+        out, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit, slots=slots)
+        assert err == 0
+        o_ref, S_ref = _oracle(batch, g, oracle.GDN_VERIFY_COMMIT, commit, slots)
+        check_gdn_state(np64(st), S_ref)
+        check_gdn_out(np64(out), o_ref, dt)
+        used = set(npi(slots).tolist())
+        for s in range(13):
+            if s not in used:
+                assert torch.equal(st[s], g['state'][s])
+
+
+def test_identity_gates_leave_state_bit_exact():
+    w = wl.WORKLOADS[2]
+    batch = wl.make_batch(w, 3, DEV)
+    g = wl.make_gdn_layer(w, batch, 4, DEV)
+    g['alpha'].fill_(1.0)
+    g['beta'].fill_(0.0)
+    commit = torch.tensor(batch.T, dtype=torch.int32, device=DEV)
+    _, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert err == 0 and torch.equal(st, g['state'])
+
+
+def test_commit_equals_run_on_prefix_bit_exact():
+    w = wl.WORKLOADS[2]
+    w = wl.Workload(**{**w.__dict__, 'B': 16, 'H': 8})
+    batch = wl.make_batch(w, 8, DEV)
+    g = wl.make_gdn_layer(w, batch, 9, DEV)
+    commit = (torch.arange(batch.B) % 5).to(torch.int32).to(DEV)
+    _, st, _ = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit)
+    # one batch holding only the first c_b tokens of every sequence (c_b >= 1)
+    keep = [b for b in range(batch.B) if int(commit[b]) > 0]
+    rows = [batch.cu_seqlens[b].item() + t for b in keep for t in range(int(commit[b]))]
+    cu = torch.zeros(len(keep) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(commit[keep].cpu(), 0)
+    sub = wl.Batch(B=len(keep), max_T=batch.max_T, T=[int(commit[b]) for b in keep],
+                   ctx=[0] * len(keep), cu_seqlens=cu.to(DEV),
+                   ctx_lens=torch.zeros(len(keep), dtype=torch.int32, device=DEV),
+                   block_table=None, num_pages=0, P=64)
+    ridx = torch.tensor(rows, device=DEV)
+    g2 = {k: (v[ridx].contiguous() if k != 'state' else v[keep].contiguous())
+          for k, v in g.items()}
+    _, st2, _ = _run(sub, g2, bd.SV_GDN_COMMIT_ONLY,
+                     torch.tensor(sub.T, dtype=torch.int32, device=DEV))
+    assert torch.equal(st2, st[keep])
+    for b in range(batch.B):
+        if int(commit[b]) == 0:
+            assert torch.equal(st[b], g['state'][b])
+
+
+def test_deferred_pending_then_verify():
+    w = wl.WORKLOADS[2]
+    w = wl.Workload(**{**w.__dict__, 'B': 12, 'H': 4})
+    prev = wl.make_batch(w, 10, DEV)
+    gp = wl.make_gdn_layer(w, prev, 11, DEV)
+    pcommit = wl.make_commit_len(prev, 12, device=DEV)
+    cur = wl.make_batch(wl.Workload(**{**w.__dict__, 'k': 5, 'ragged_k': True}), 13, DEV)
+    gc = wl.make_gdn_layer(w, cur, 14, DEV)
+    gc['state'] = gp['state']
+    pend = bd.make_gdn_pending(sv_batch(prev), gp['k'], gp['v'], gp['alpha'],
+                               gp['beta'], pcommit)
+    say('GDN deferred: pending replay + verify')
+    out, st, err = _run(cur, gc, bd.SV_GDN_VERIFY_ONLY, None, pending=pend)
+    assert err == 0
+    _, S_mid = oracle.gdn_step(np64(gp['state']), None, None, np64(gp['k']), np64(gp['v']),
+                               np64(gp['alpha']), np64(gp['beta']), npi(prev.cu_seqlens),
+                               npi(pcommit), oracle.GDN_COMMIT_ONLY)
+    check_gdn_state(np64(st), S_mid)
+    o_ref, _ = oracle.gdn_step(S_mid, None, np64(gc['q']), np64(gc['k']), np64(gc['v']),
+                               np64(gc['alpha']), np64(gc['beta']), npi(cur.cu_seqlens),
+                               None, oracle.GDN_VERIFY_ONLY)
+    check_gdn_out(np64(out), o_ref, torch.bfloat16)
+    # the pending replay is the same arithmetic as a plain COMMIT_ONLY call
+    _, st_two, _ = _run(prev, gp, bd.SV_GDN_COMMIT_ONLY, pcommit)
+    assert torch.equal(st_two, st)
+
+
+def test_bad_commit_length_is_flagged_and_skipped():
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 0, DEV)
+    g = wl.make_gdn_layer(w, batch, 1, DEV)
+    commit = torch.tensor([2, 9], dtype=torch.int32, device=DEV)
+    out, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert err & 8
+    assert torch.equal(st[1], g['state'][1])       # skipped
+    _, S_ref = oracle.gdn_step(np64(g['state'][:1]), None, np64(g['q'][:4]), np64(g['k'][:4]),
+                               np64(g['v'][:4]), np64(g['alpha'][:4]), np64(g['beta'][:4]),
+                               np.array([0, 4]), np.array([2]), oracle.GDN_VERIFY_COMMIT)
+    check_gdn_state(np64(st[:1]), S_ref)

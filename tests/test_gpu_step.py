@@ -1,0 +1,211 @@
+"""GPU parity of spec_verify_step (the whole step) against the oracle.
+
+Same tolerances as the per-op tests; acceptance, commit lengths, ctx_lens and
+the KV pools are bit-exact.  The deferred schedule must leave exactly the
+states of the two-phase schedule (bit for bit) once flushed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from block_draft_verification_spec_amd import binding as bd
+from gpu_helpers import (DEV, bits, check_attn_out, check_gdn_out, check_gdn_state,
+                         err_word, np64, npi, say, sv_batch)
+
+pytestmark = pytest.mark.gpu
+
+
+def make_step(w, batch, seed, mode):
+    layers = []
+    for i, kind in enumerate(w.layers):
+        if kind == 'attn':
+            lay = wl.make_attn_layer(w, batch, seed + 10 * i, DEV)
+            lay['out'] = torch.full_like(lay['q'], float('nan'))
+        else:
+            lay = wl.make_gdn_layer(w, batch, seed + 10 * i, DEV)
+            lay['out'] = torch.full_like(lay['v'], float('nan'))
+        lay['kind'] = kind
+        layers.append(lay)
+    acc = wl.make_accept(w, batch, seed + 999, mode, DEV)
+    return layers, acc
+
+
+def run_step(w, batch, layers, acc, mode, schedule=bd.SV_SCHEDULE_TWO_PHASE, pending=None,
+             ctx=None):
+    dt_a = bd.SV_BF16 if w.attn_dtype == torch.bfloat16 else bd.SV_F32
+    dt_g = bd.SV_BF16 if w.gdn_dtype == torch.bfloat16 else bd.SV_F32
+    a_layers = [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
+                              l['out']) for l in layers if l['kind'] == 'attn']
+    g_layers = [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'],
+                             l['out']) for l in layers if l['kind'] == 'gdn']
+    args = bd.StepArgs([1 if l['kind'] == 'attn' else 0 for l in layers],
+                       bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages,
+                                      batch.block_table, dt_a),
+                       a_layers, bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt_g), g_layers,
+                       bd.accept_args(mode, acc['target_logits'], acc['draft_tokens'],
+                                      acc.get('draft_logits'), acc.get('u_accept'),
+                                      acc.get('u_final')))
+    sb = sv_batch(batch)
+    ws = torch.empty(max(1, bd.spec_verify_step_workspace_bytes(sb, args)), dtype=torch.uint8,
+                     device=DEV)
+    result = torch.full((batch.B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
+    commit = torch.full((batch.B,), -7, dtype=torch.int32, device=DEV)
+    ctx = (batch.ctx_lens if ctx is None else ctx).clone()
+    err = err_word()
+    bd.spec_verify_step(sb, args, ctx, result, commit, schedule=schedule, pending=pending,
+                        workspace=ws, err=err)
+    torch.cuda.synchronize()
+    r = npi(result)
+    return dict(acc=r[:batch.B], out=r[batch.B:].reshape(batch.B, batch.max_T),
+                commit=commit, ctx=ctx, err=int(err.item()), args=args)
+
+
+def oracle_step(w, batch, layers, acc, mode, ctx=None):
+    lays = []
+    for l in layers:
+        if l['kind'] == 'attn':
+            lays.append({'kind': 'attn', 'q': np64(l['q']), 'k_new': np64(l['k_new']),
+                         'v_new': np64(l['v_new']), 'k_cache': np64(l['k_cache']),
+                         'v_cache': np64(l['v_cache'])})
+        else:
+            lays.append({'kind': 'gdn', 'state': np64(l['state']), 'q': np64(l['q']),
+                         'k': np64(l['k']), 'v': np64(l['v']), 'alpha': np64(l['alpha']),
+                         'beta': np64(l['beta'])})
+    ai = {'target_logits': np64(acc['target_logits']), 'draft_tokens': npi(acc['draft_tokens'])}
+    if mode == bd.SV_ACCEPT_REJECTION:
+        ai.update(draft_logits=np64(acc['draft_logits']), u_accept=np64(acc['u_accept']),
+                  u_final=np64(acc['u_final']))
+    return oracle.verify_step(lays, npi(batch.cu_seqlens),
+                              npi(batch.ctx_lens) if ctx is None else ctx,
+                              npi(batch.block_table), batch.P, batch.max_T,
+                              'greedy' if mode == bd.SV_ACCEPT_GREEDY else 'rejection', ai)
+
+
+def compare(w, layers, res, ref, before):
+    assert res['err'] == 0
+    np.testing.assert_array_equal(res['acc'], ref['accept_len'])
+    np.testing.assert_array_equal(res['out'], ref['out_tokens'])
+    np.testing.assert_array_equal(npi(res['commit']), ref['commit_len'])
+    np.testing.assert_array_equal(npi(res['ctx']), ref['ctx_lens'])
+    for i, l in enumerate(layers):
+        if l['kind'] == 'attn':
+            check_attn_out(np64(l['out']), ref['outputs'][i], w.attn_dtype)
+            # pools: compare the bit patterns the oracle's append produced
+            assert np.array_equal(bits(l['k_cache']), bits_of(ref['k_cache'][i], before[i][0]))
+            assert np.array_equal(bits(l['v_cache']), bits_of(ref['v_cache'][i], before[i][1]))
+        else:
+            check_gdn_out(np64(l['out']), ref['outputs'][i], w.gdn_dtype)
+            check_gdn_state(np64(l['state']), ref['state'][i])
+
+
+def bits_of(values64, like):
+    t = torch.from_numpy(values64).to(like.dtype)
+    return bits(t)
+
+
+@pytest.mark.parametrize("mode", [bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION])
+def test_tiny_fp32_step(mode):
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 0, DEV)
+    layers, acc = make_step(w, batch, 1, 'greedy' if mode == 0 else 'rejection')
+    ref = oracle_step(w, batch, layers, acc, mode)
+    before = [(l.get('k_cache'), l.get('v_cache')) for l in layers]
+    for l in layers:
+        if l['kind'] == 'attn':
+            l['k_cache'] = l['k_cache'].clone()
+            l['v_cache'] = l['v_cache'].clone()
+        else:
+            l['state'] = l['state'].clone()
+    say('tiny step mode', mode)
+    res = run_step(w, batch, layers, acc, mode)
+    compare(w, layers, res, ref, before)
+
+
+@pytest.mark.parametrize("mode", [bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION])
+def test_hybrid_group_step(mode):
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1)})
+    batch = wl.make_batch(w, 5, DEV)
+    layers, acc = make_step(w, batch, 6, 'greedy' if mode == 0 else 'rejection')
+    ref = oracle_step(w, batch, layers, acc, mode)
+    before = [(l.get('k_cache'), l.get('v_cache')) for l in layers]
+    for l in layers:
+        if l['kind'] == 'attn':
+            l['k_cache'] = l['k_cache'].clone()
+            l['v_cache'] = l['v_cache'].clone()
+        else:
+            l['state'] = l['state'].clone()
+    say('hybrid group step mode', mode)
+    res = run_step(w, batch, layers, acc, mode)
+    compare(w, layers, res, ref, before)
+
+
+def test_deferred_schedule_equals_two_phase():
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1)})
+    batch = wl.make_batch(w, 7, DEV, reserve=8)
+    l1, a1 = make_step(w, batch, 8, 'rejection')
+    l2, a2 = make_step(w, batch, 9, 'rejection')
+    init = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in l.items()}
+            for l in l1]
+
+    def fresh(src, states_from, pools_from):
+        out = []
+        for s, st, pl in zip(src, states_from, pools_from):
+            d = dict(s)
+            d['out'] = torch.full_like(s['out'], float('nan'))
+            if s['kind'] == 'gdn':
+                d['state'] = st['state']
+            else:
+                d['k_cache'], d['v_cache'] = pl['k_cache'], pl['v_cache']
+            out.append(d)
+        return out
+
+    results = {}
+    for sched in (bd.SV_SCHEDULE_TWO_PHASE, bd.SV_SCHEDULE_DEFERRED):
+        st = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in l.items()}
+              for l in init]
+        s1 = fresh(l1, st, st)
+        r1 = run_step(w, batch, s1, a1, bd.SV_ACCEPT_REJECTION, schedule=sched)
+        s2 = fresh(l2, s1, s1)
+        pend = None
+        if sched == bd.SV_SCHEDULE_DEFERRED:
+            pl = [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'],
+                               l['out']) for l in s1 if l['kind'] == 'gdn']
+            arr = (bd.SvGdnLayer * len(pl))(*pl)
+            pend = bd.SvStepPending(sv_batch(batch), arr, r1['commit'].data_ptr())
+        r2 = run_step(w, batch, s2, a2, bd.SV_ACCEPT_REJECTION, schedule=sched, pending=pend,
+                      ctx=r1['ctx'])
+        assert r1['err'] == 0 and r2['err'] == 0
+        if sched == bd.SV_SCHEDULE_DEFERRED:
+            for l in s2:     # flush the second step's accepted tokens
+                if l['kind'] == 'gdn':
+                    bd.gdn_verify_commit(sv_batch(batch), bd.SV_GDN_COMMIT_ONLY, l['state'],
+                                         l['q'], l['k'], l['v'], l['alpha'], l['beta'],
+                                         r2['commit'], l['out'])
+            torch.cuda.synchronize()
+        results[sched] = (r1, r2, s2)
+    (t1, t2, ts), (d1, d2, ds) = results[0], results[1]
+    np.testing.assert_array_equal(t1['out'], d1['out'])
+    np.testing.assert_array_equal(t2['out'], d2['out'])
+    for a, b in zip(ts, ds):
+        assert torch.equal(a['out'], b['out'])
+        if a['kind'] == 'gdn':
+            assert torch.equal(a['state'], b['state'])
+        else:
+            assert torch.equal(a['k_cache'], b['k_cache'])
+    # and against the oracle: two steps in a row
+    ref1 = oracle_step(w, batch, [dict(l, **({'state': i['state']} if l['kind'] == 'gdn' else
+                                            {'k_cache': i['k_cache'], 'v_cache': i['v_cache']}))
+                                  for l, i in zip(l1, init)], a1, bd.SV_ACCEPT_REJECTION)
+    np.testing.assert_array_equal(t1['out'], ref1['out_tokens'])
+    for i, l in enumerate(ts):
+        if l['kind'] == 'gdn':
+            s_mid = ref1['state'][i]
+            _, S2 = oracle.gdn_step(s_mid, None, None, np64(l['k']), np64(l['v']),
+                                    np64(l['alpha']), np64(l['beta']), npi(batch.cu_seqlens),
+                                    npi(t2['commit']), oracle.GDN_COMMIT_ONLY)
+            check_gdn_state(np64(l['state']), S2)

@@ -124,8 +124,11 @@ class Batch:
 
 
 def make_batch(w: Workload, seed: int, device='cpu', ctx_override=None,
-               k_override=None) -> Batch:
-    """Draft counts, context lengths and a shuffled paged block table."""
+               k_override=None, reserve=0) -> Batch:
+    """Draft counts, context lengths and a shuffled paged block table.
+
+    The table of sequence b covers ``ctx_b + T_b + reserve`` positions
+    (``reserve`` leaves room for later steps)."""
     g = generator(seed)                         # host draws: small
     B = w.B
     if k_override is not None:
@@ -142,7 +145,7 @@ def make_batch(w: Workload, seed: int, device='cpu', ctx_override=None,
     else:
         ctx = torch.randint(w.ctx[0], w.ctx[1] + 1, (B,), generator=g).tolist()
     P = w.P
-    need = [-(-(L + t) // P) for L, t in zip(ctx, T)]
+    need = [-(-(L + t + reserve) // P) for L, t in zip(ctx, T)]
     max_pages = max(w.max_pages_per_seq, max(need))
     total_need = sum(need)
     num_pages = max(int(round(total_need * w.pool_factor)), w.min_pool_pages,
