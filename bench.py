@@ -1,0 +1,352 @@
+"""Benchmark of the block speculative-verification step on one MI355X.
+
+Workload: the full hybrid verify step (64 layers, GDN,GDN,GDN,ATT x 16;
+B = 64 sequences, k = 3 drafts, contexts ~U[2048, 8192], 32q/8kv heads,
+D = 128, bf16 paged KV in 64-token pages; 48 GDN layers with 32 heads,
+dk = dv = 128, fp32 state; acceptance over V = 151936 bf16 logits),
+synthetic seeded inputs resident in HBM before timing starts.
+
+A step = one call of spec_verify_step: every layer's verify pass, the
+acceptance, the GDN commit (deferred schedule: folded into the next step's
+verify pass; the timed region ends with a flush so every accepted token of
+every timed step is committed) and the ctx_lens update.
+
+Prints one JSON line.  value = verified draft tokens per second (sum_b k_b
+per step).  Also reported: algorithmic HBM bytes per step and GB/s (% of the
+8 TB/s peak), the roofline of the dominant kernel (the paged attention call,
+timed per launch with HIP events on the stream it runs on), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument('--gpus', type=int, default=1)
+    p.add_argument('--steps', type=int, default=20)
+    p.add_argument('--warmup', type=int, default=5)
+    p.add_argument('--workload', type=int, default=3, help='index into workloads.WORKLOADS')
+    p.add_argument('--accept', choices=['rejection', 'greedy'], default='rejection')
+    p.add_argument('--schedule', choices=['deferred', 'two_phase'], default='deferred')
+    p.add_argument('--no-cpu-baseline', action='store_true')
+    p.add_argument('--attn-reps', type=int, default=3,
+                   help='passes over the attention layers for the per-launch timing')
+    p.add_argument('--seed', type=int, default=3)
+    p.add_argument('--calibrate-copy', action='store_true',
+                   help='only run a plain 1 GiB device copy (counter calibration)')
+    p.add_argument('--cpu-budget', type=float, default=15.0,
+                   help='seconds of oracle work for the CPU baseline sample')
+    return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of exactly 1 GiB, three times: the
+    reference for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.uint8, device='cuda')
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({'calibrate_copy_bytes': n, 'copies': 3}), flush=True)
+
+
+def attn_bytes(w, batch):
+    """Algorithmic HBM bytes of one attention layer (one launch)."""
+    s = 2  # bf16
+    ctx = sum(batch.ctx)
+    T = batch.total_T
+    kv_ctx = ctx * w.Hkv * w.D * 2 * s
+    per_tok = w.Hq * w.D * s + 2 * w.Hkv * w.D * s + 2 * w.Hkv * w.D * s + w.Hq * w.D * s
+    return kv_ctx + T * per_tok + batch.B * batch.block_table.shape[1] * 4
+
+
+def gdn_bytes(w, batch):
+    s = 2
+    T = batch.total_T
+    return (2 * batch.B * w.H * w.dv * w.dk * 4 + T * w.H * (2 * w.dk + w.dv) * s
+            + T * w.H * 8 + T * w.H * w.dv * s)
+
+
+def accept_bytes(w, batch, mode):
+    s = 2
+    T = batch.total_T
+    b = T * w.V * s
+    if mode == 'rejection':
+        b += (T - batch.B) * w.V * s
+    return b
+
+
+def cpu_baseline(w, batch, layers, acc, mode, draft_tokens_per_step, budget):
+    """The oracle as it stands, on a bounded sample, scaled to one step.
+
+    Within a time budget: GDN layers on the full batch, one at a time (at
+    least one); attention of one layer, one sequence at a time (its pages
+    only; at least one), scaled to the whole batch by context length;
+    acceptance on all rows.  The per-layer costs are then multiplied by the
+    layer counts of the step.
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get('num_threads', 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    f64 = lambda t: t.detach().double().cpu().numpy()
+    i64 = lambda t: t.detach().cpu().numpy().astype(np.int64)
+    cu = i64(batch.cu_seqlens)
+    ctx = i64(batch.ctx_lens)
+    table = i64(batch.block_table)
+    # acceptance on the full batch
+    ai = [f64(acc['target_logits']), i64(acc['draft_tokens'])]
+    t0 = time.perf_counter()
+    if mode == 'greedy':
+        oracle.greedy_accept(ai[0], ai[1], cu, batch.max_T)
+    else:
+        oracle.rejection_accept(ai[0], f64(acc['draft_logits']), ai[1], f64(acc['u_accept']),
+                                f64(acc['u_final']), cu, batch.max_T)
+    t_acc = time.perf_counter() - t0
+    # GDN layers on the full batch
+    gdn = [l for l in layers if l['kind'] == 'gdn']
+    t_gdn_sum, n_gdn_done = 0.0, 0
+    for g in gdn:
+        args = (f64(g['state']), None, f64(g['q']), f64(g['k']), f64(g['v']),
+                f64(g['alpha']), f64(g['beta']), cu, None, oracle.GDN_VERIFY_ONLY)
+        t0 = time.perf_counter()
+        oracle.gdn_step(*args)
+        t_gdn_sum += time.perf_counter() - t0
+        n_gdn_done += 1
+        if t_gdn_sum > 0.4 * budget:
+            break
+    t_gdn = t_gdn_sum / n_gdn_done
+    # attention, sequence by sequence
+    a = next(l for l in layers if l['kind'] == 'attn')
+    t_att_sample, seqs = 0.0, []
+    for b in range(batch.B):
+        pages = table[b][table[b] >= 0]
+        idx = torch.from_numpy(pages).to(a['k_cache'].device)
+        kc, vc = f64(a['k_cache'][idx]), f64(a['v_cache'][idx])
+        sub_t = np.arange(len(pages))[None, :]
+        rows = slice(cu[b], cu[b + 1])
+        q, kn, vn = f64(a['q'][rows]), f64(a['k_new'][rows]), f64(a['v_new'][rows])
+        t0 = time.perf_counter()
+        oracle.verify_attention(q, kn, vn, kc, vc, sub_t, ctx[b:b + 1],
+                                np.array([0, cu[b + 1] - cu[b]]), batch.P)
+        t_att_sample += time.perf_counter() - t0
+        seqs.append(b)
+        if t_att_sample > 0.5 * budget:
+            break
+    t_att = t_att_sample * float(ctx.sum()) / float(ctx[seqs].sum())
+    n_att = sum(1 for l in layers if l['kind'] == 'attn')
+    n_gdn = len(layers) - n_att
+    t_step = n_att * t_att + n_gdn * t_gdn + t_acc
+    return {
+        'value': draft_tokens_per_step / t_step, 'unit': 'verified draft tokens/s',
+        'cores': int(threads), 'kind': 'oracle',
+        'sample': (f'{n_gdn_done} GDN layer(s) on all {batch.B} sequences, attention of one '
+                   f'layer for {len(seqs)} of {batch.B} sequences (scaled by context length), '
+                   f'{mode} acceptance on all rows; per-layer times scaled to {n_gdn} GDN + '
+                   f'{n_att} attention layers per step'),
+        'seconds_measured': round(t_gdn_sum + t_att_sample + t_acc, 2),
+        'seconds_per_step_extrapolated': round(t_step, 2),
+        'affinity_cpus': len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f'bench.py runs on one GPU only (asked for --gpus {args.gpus}): this '
+              'library has no multi-GPU path; see DESIGN.md for how the step would shard.',
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+
+    dev = 'cuda'
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    mode = args.accept
+    steps, warmup = args.steps, args.warmup
+    # room in every block table for the tokens all steps commit
+    batch = wl.make_batch(w, args.seed, dev, reserve=w.max_T * (steps + warmup + 2))
+    layers = []
+    for i, kind in enumerate(w.layers):
+        if kind == 'attn':
+            lay = wl.make_attn_layer(w, batch, 1000 + i, dev)
+            lay['out'] = torch.empty_like(lay['q'])
+        else:
+            lay = wl.make_gdn_layer(w, batch, 1000 + i, dev)
+            lay['out'] = torch.empty_like(lay['v'])
+        lay['kind'] = kind
+        layers.append(lay)
+    acc = wl.make_accept(w, batch, 2000, mode, dev)
+    torch.cuda.synchronize()
+    print(f'[bench] inputs ready: {w.name}, {len(layers)} layers, '
+          f'{torch.cuda.memory_allocated() / 2**30:.1f} GiB', file=sys.stderr, flush=True)
+
+    dt_a = bd.SV_BF16 if w.attn_dtype == torch.bfloat16 else bd.SV_F32
+    dt_g = bd.SV_BF16 if w.gdn_dtype == torch.bfloat16 else bd.SV_F32
+    amode = bd.SV_ACCEPT_GREEDY if mode == 'greedy' else bd.SV_ACCEPT_REJECTION
+    gdn_layers = [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'],
+                               l['out']) for l in layers if l['kind'] == 'gdn']
+    step_args = bd.StepArgs(
+        [1 if l['kind'] == 'attn' else 0 for l in layers],
+        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table, dt_a),
+        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'])
+         for l in layers if l['kind'] == 'attn'],
+        bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt_g), gdn_layers,
+        bd.accept_args(amode, acc['target_logits'], acc['draft_tokens'],
+                       acc.get('draft_logits'), acc.get('u_accept'), acc.get('u_final')))
+    sb = bd.make_batch(batch.cu_seqlens, batch.B, batch.max_T, batch.total_T)
+    ws = torch.zeros(bd.spec_verify_step_workspace_bytes(sb, step_args), dtype=torch.uint8,
+                     device=dev)
+    result = torch.empty(batch.B * (1 + batch.max_T), dtype=torch.int32, device=dev)
+    commits = [torch.zeros(batch.B, dtype=torch.int32, device=dev) for _ in range(2)]
+    ctx = batch.ctx_lens.clone()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    deferred = args.schedule == 'deferred'
+    sched = bd.SV_SCHEDULE_DEFERRED if deferred else bd.SV_SCHEDULE_TWO_PHASE
+    # pending tokens of the previous step: the same input buffers (their
+    # values do not change the work), with the previous step's commit lengths
+    pend_arr = (bd.SvGdnLayer * len(gdn_layers))(*gdn_layers)
+    state = {'n': 0}
+
+    def one_step():
+        i = state['n']
+        pend = None
+        if deferred and i > 0:
+            pend = bd.SvStepPending(sb, pend_arr, commits[(i - 1) % 2].data_ptr())
+        bd.spec_verify_step(sb, step_args, ctx, result, commits[i % 2], schedule=sched,
+                            pending=pend, workspace=ws, err=err)
+        state['n'] = i + 1
+
+    def flush():
+        if deferred and state['n'] > 0:
+            last = commits[(state['n'] - 1) % 2]
+            for l in layers:
+                if l['kind'] == 'gdn':
+                    bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, l['state'], l['q'], l['k'],
+                                         l['v'], l['alpha'], l['beta'], last, l['out'])
+            state['n'] = 0
+
+    for _ in range(warmup):
+        one_step()
+    flush()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, f'device error flag {int(err.item())}'
+    print('[bench] warmup done', file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+    flush()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / steps
+    assert int(err.item()) == 0, f'device error flag {int(err.item())}'
+    accepted = result[:batch.B].double().mean().item()
+    print(f'[bench] timed {steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / steps:.3f})',
+          file=sys.stderr, flush=True)
+
+    # ---- per-part timing and the dominant kernel's per-launch duration
+    att_layers = [l for l in layers if l['kind'] == 'attn']
+    nbytes_a = bd.spec_verify_attention_workspace_bytes(
+        batch.B, batch.total_T, w.Hq, w.Hkv, w.D, batch.block_table.shape[1], batch.P, dt_a)
+    ctx_fixed = ctx.clone()
+    durs = []
+    for _ in range(args.attn_reps):
+        for l in att_layers:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            bd.spec_verify_attention(sb, l['q'], l['k_new'], l['v_new'], l['k_cache'],
+                                     l['v_cache'], batch.block_table, ctx_fixed, l['out'],
+                                     workspace=ws, err=err)
+            s1.record(stream)
+            durs.append((s0, s1))
+    torch.cuda.synchronize()
+    att_ms = [a.elapsed_time(b) for a, b in durs]
+    att_ms_mean = sum(att_ms) / len(att_ms)
+    # attention bytes at the contexts the timed calls used
+    cur_ctx = ctx_fixed.tolist()
+    b_att = attn_bytes(w, wl.Batch(**{**batch.__dict__, 'ctx': cur_ctx}))
+    gdn_l = [l for l in layers if l['kind'] == 'gdn']
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for l in gdn_l:
+        bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_COMMIT, l['state'], l['q'], l['k'], l['v'],
+                             l['alpha'], l['beta'], commits[0], l['out'])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gdn_ms = g0.elapsed_time(g1) / max(1, len(gdn_l))
+
+    T = batch.total_T
+    n_att, n_gdn = len(att_layers), len(gdn_l)
+    draft_per_step = T - batch.B
+    ctx_mid = [c for c in cur_ctx]
+    b_step = (n_att * attn_bytes(w, wl.Batch(**{**batch.__dict__, 'ctx': ctx_mid}))
+              + n_gdn * gdn_bytes(w, batch) + accept_bytes(w, batch, mode))
+    gbs = b_step / (ms_step * 1e-3) / 1e9
+    achieved = b_att / (att_ms_mean * 1e-3) / 1e9
+
+    line = {
+        'metric': 'verified draft tokens/sec at 1 GPU + achieved HBM GB/s (% of MI355X peak)',
+        'value': round(draft_per_step / (ms_step * 1e-3), 1),
+        'unit': 'verified draft tokens/s',
+        'n_gpus': 1, 'steps': steps, 'warmup': warmup,
+        'ms_per_step': round(ms_step, 4),
+        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None,
+        'dtype': 'bf16',
+        'data': 'synthetic (seeded; no model weights)',
+        'config': {'workload': w.name, 'layers': f'{n_gdn} GDN + {n_att} attention',
+                   'batch': batch.B, 'drafts_per_seq': w.k, 'ctx': list(w.ctx),
+                   'Hq_Hkv_D': [w.Hq, w.Hkv, w.D], 'page': batch.P,
+                   'gdn_H_dk_dv': [w.H, w.dk, w.dv], 'vocab': w.V, 'accept': mode,
+                   'schedule': args.schedule},
+        'step_hbm': {'algorithmic_bytes': b_step, 'GBps': round(gbs, 1),
+                     'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4)},
+        'roofline': {'kernel': 'spec_verify_attention (split-KV verify attention, one layer)',
+                     'bound': 'hbm', 'achieved': round(achieved, 1), 'peak': HBM_PEAK_GBS,
+                     'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
+                     'traffic': None, 'bytes_per_launch': b_att,
+                     'launch_ms': round(att_ms_mean, 4), 'launches': len(att_ms)},
+        'parts_ms': {'attention_layer': round(att_ms_mean, 4),
+                     'gdn_layer_verify_commit': round(gdn_ms, 4)},
+        'mean_accept_len': round(accepted, 3),
+        'dtype_detail': 'bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance',
+    }
+    if not args.no_cpu_baseline:
+        print('[bench] timing the CPU oracle on a bounded sample', file=sys.stderr, flush=True)
+        line['cpu_baseline'] = cpu_baseline(w, batch, layers, acc, mode, draft_per_step,
+                                           args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == '__main__':
+    main()

@@ -63,8 +63,8 @@ sv_status check_attn(const sv_batch* batch, const void* q, const void* k_new, co
     return fail(SV_EINVAL, "%s: page_size, max_pages_per_seq, num_pages must be >= 1", who);
   if (dtype == SV_BF16) {
     if (D != 64 && D != 128) return fail(SV_EDTYPE, "%s: bf16 path needs D in {64,128} (got %d)", who, D);
-    if (!(P % 64 == 0 || 64 % P == 0))
-      return fail(SV_EINVAL, "%s: page_size %d must divide or be a multiple of 64", who, P);
+    if (P < 16 || !(P % 64 == 0 || 64 % P == 0))
+      return fail(SV_EINVAL, "%s: page_size %d must be 16, 32 or a multiple of 64", who, P);
     if ((Hq / Hkv) * batch->max_T > 64)
       return fail(SV_ECAPACITY, "%s: (Hq/Hkv)*max_T = %d exceeds 64 query rows", who,
                   (Hq / Hkv) * batch->max_T);
@@ -110,10 +110,7 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
   a.err = err;
   if (dtype == SV_BF16) {
     sv::attn_split_plan(a.B, Hkv, max_pages, P, &a.nsplit, &a.tiles_per_split);
-    const size_t rows = static_cast<size_t>(a.total_T) * Hq * a.nsplit;
-    const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~size_t(255);
-    a.part_o = static_cast<float*>(ws);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+    sv::attn_workspace_carve(ws, a.total_T, Hq, D, a.nsplit, &a.part_o, &a.part_ml);
   }
   return a;
 }

@@ -15,6 +15,8 @@
 //   * the G = Hq / Hkv query heads of a KV head and the T_b verify tokens form
 //     M = G * T_b query rows (row m = token m / G, head m % G), padded to
 //     16-row tiles; one KV read serves all of them;
+//   * the page ids a split touches are read once into LDS, so a tile's K/V
+//     loads never wait on a block-table load;
 //   * a 64-key tile of K and V is loaded with coalesced 16-byte loads into
 //     registers (prefetched one tile ahead), K is stored row-major in LDS and
 //     V transposed (4 keys x 8 dims per thread, transposed in registers);
@@ -81,6 +83,8 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 // --------------------------------------------------------------------------
 // bf16 MFMA split kernel
 // --------------------------------------------------------------------------
+constexpr int kMaxSplitPages = 72;  // pages a split may touch (tiles_per_split <= 16, P >= 16)
+
 template <int D, int NQT>
 __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   constexpr int CPK = D / 8;        // 16-byte chunks per key row
@@ -93,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKT * KS + D * VS];
   __shared__ float wm[4][ROWS];
   __shared__ float wl[4][ROWS];
+  __shared__ int s_pages[kMaxSplitPages];
   uint16_t* Ks = lds;
   uint16_t* Vt = lds + kKT * KS;
 
@@ -108,6 +113,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
   const int G = a.Hq / a.Hkv;
   const int M = G * T;
+  const int P = a.P;
+
+  // ---- the split's page ids, read once: positions t_begin*64 .. pos_end-1
+  const int pos_end = min(t_end * kKT, L + T);
+  const int first_page = (t_begin * kKT) / P;
+  const int n_pages = (pos_end - 1) / P - first_page + 1;
+  bool bad_page = false;
+  if (tid < n_pages) {
+    int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + first_page + tid];
+    if (pid < 0 || pid >= a.num_pages) {
+      bad_page = true;
+      pid = -1;
+    }
+    s_pages[tid] = pid;
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T): row 16 nt + lr, dims
   // 32 s + 8 lg .. + 7.
@@ -128,35 +148,32 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
       qf[nt][s] = t.v;
     }
   }
+  __syncthreads();
 
   // ---- per-thread slice of a tile: keys KPT*kb .. +KPT-1, dims 8*dc .. +7
   const int dc = tid % CPK, kb = tid / CPK;
   uint4 kreg[KPT], vreg[KPT];
-  bool bad_page = false;
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int p = tile * kKT + KPT * kb + i;
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (p < L) {
-        const long long off = page_offset(a, b, g, p, 8 * dc);
-        if (off >= 0) {
-          kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + off);
-          vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + off);
-        } else {
-          bad_page = true;
-        }
-      } else if (p < L + T) {
-        const size_t off = (static_cast<size_t>(x0 + p - L) * a.Hkv + g) * D + 8 * dc;
-        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + off);
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + off);
-        if (a.write_kv) {
-          const long long po = page_offset(a, b, g, p, 8 * dc);
+      if (p < L + T) {
+        const int pid = s_pages[p / P - first_page];
+        const long long po =
+            pid < 0 ? -1 : ((static_cast<long long>(pid) * a.Hkv + g) * P + (p % P)) * D + 8 * dc;
+        if (p < L) {
           if (po >= 0) {
+            kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + po);
+            vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + po);
+          }
+        } else {
+          const size_t off = (static_cast<size_t>(x0 + p - L) * a.Hkv + g) * D + 8 * dc;
+          kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + off);
+          vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + off);
+          if (a.write_kv && po >= 0) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + po) = kv;
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + po) = vv;
-          } else {
-            bad_page = true;
           }
         }
       }
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
     __syncthreads();
   }
 
-  // ---- write the split result: row m -> (token j, head g*G + hh)
+  // ---- this split's result: row m -> (token j, head g*G + hh)
   for (int i = tid; i < M * (D / 4); i += kThreads) {
     const int m = i / (D / 4), d4 = (i - m * (D / 4)) * 4;
     const float mm = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
@@ -307,8 +324,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
     for (int ww = 0; ww < 4; ++ww)
       if (wm[ww][m] != -INFINITY) ls += wl[ww][m] * exp2f(wm[ww][m] - mm);
     const int j = m / G, hh = m - j * G;
-    const int h = g * G + hh;
-    const size_t row = static_cast<size_t>(x0 + j) * a.Hq + h;
+    const size_t row = static_cast<size_t>(x0 + j) * a.Hq + g * G + hh;
     const float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
     if (nsplit_b == 1) {
       const float inv = 1.f / ls;
@@ -328,7 +344,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// log-sum-exp combine of the splits (bf16 path)
+// log-sum-exp combine of the splits (bf16 path).  A separate launch: the
+// kernel boundary makes every split's partial visible, where a device-scope
+// fence inside the split kernel would write back and invalidate the whole L2
+// of an XCD once per workgroup.
 // --------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
@@ -475,6 +494,14 @@ size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D, int max_
   const size_t rows = static_cast<size_t>(total_T) * Hq * ns;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~size_t(255);
   return o_bytes + rows * 2 * sizeof(float);
+}
+
+void attn_workspace_carve(void* ws, int total_T, int Hq, int D, int nsplit, float** part_o,
+                          float** part_ml) {
+  const size_t rows = static_cast<size_t>(total_T) * Hq * nsplit;
+  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~size_t(255);
+  *part_o = static_cast<float*>(ws);
+  *part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
 }
 
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype, hipStream_t stream) {

@@ -64,4 +64,21 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Data-parallel-primitive lane moves within rows of 16 lanes (VALU operand
+// modifiers, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over each row of 16 lanes, result in every lane of the row:
+// rotate by 8, rotate by 4, then swap lane pairs 2 apart and 1 apart.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0x128>(v);  // row_ror:8
+  v += dpp_mov<0x124>(v);  // row_ror:4
+  v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
+  return v;
+}
+
 }  // namespace sv

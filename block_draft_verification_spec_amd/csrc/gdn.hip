@@ -43,7 +43,6 @@ struct GdnSmem {
   float v_s[kMaxTok][kRowsPerBlock];
   float a_s[kMaxTok];
   float b_s[kMaxTok];
-  float kq_s[kMaxT];
   float o_s[kMaxT][kRowsPerBlock];
 };
 
@@ -64,7 +63,6 @@ __device__ __forceinline__ void gdn_tile(
   auto& v_s = sm.v_s;
   auto& a_s = sm.a_s;
   auto& b_s = sm.b_s;
-  auto& kq_s = sm.kq_s;
   auto& o_s = sm.o_s;
 
   const int tid = threadIdx.x;
@@ -151,15 +149,6 @@ __device__ __forceinline__ void gdn_tile(
     b_s[t] = t < pc ? pbeta[gi] : beta[gi];
   }
   __syncthreads();
-  if (verify && tid < 64) {
-    for (int t = 0; t < T; ++t) {
-      float acc = 0.f;
-      for (int e = tid; e < DK; e += 64) acc += k_s[pc + t][e] * q_s[t][e];
-      acc = group_sum<64>(acc);
-      if (tid == 0) kq_s[t] = acc;
-    }
-  }
-  __syncthreads();
 
   // ---- the recurrence, one token at a time
   for (int i = 0; i < n_tot; ++i) {
@@ -169,6 +158,7 @@ __device__ __forceinline__ void gdn_tile(
     for (int vv = 0; vv < NV4; ++vv)
       kk[vv] = *reinterpret_cast<const float4*>(&k_s[i][vv * 64 + 4 * cl]);
     float uk[kRowsPerThread], uq[kRowsPerThread];
+    float kq = 0.f;
 #pragma unroll
     for (int r = 0; r < kRowsPerThread; ++r) {
       float acc = 0.f;
@@ -182,6 +172,8 @@ __device__ __forceinline__ void gdn_tile(
       for (int vv = 0; vv < NV4; ++vv)
         qq[vv] = *reinterpret_cast<const float4*>(&q_s[i - pc][vv * 64 + 4 * cl]);
 #pragma unroll
+      for (int vv = 0; vv < NV4; ++vv) kq += dot4(kk[vv], qq[vv]);
+#pragma unroll
       for (int r = 0; r < kRowsPerThread; ++r) {
         float acc = 0.f;
 #pragma unroll
@@ -189,11 +181,13 @@ __device__ __forceinline__ void gdn_tile(
         uq[r] = acc;
       }
     }
+    // full-row dot products: sum over the 16 lanes that share the rows
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) uk[r] = group_sum<16>(uk[r]);
+    for (int r = 0; r < kRowsPerThread; ++r) uk[r] = row16_sum(uk[r]);
     if (emit) {
+      kq = row16_sum(kq);
 #pragma unroll
-      for (int r = 0; r < kRowsPerThread; ++r) uq[r] = group_sum<16>(uq[r]);
+      for (int r = 0; r < kRowsPerThread; ++r) uq[r] = row16_sum(uq[r]);
     }
     const float al = a_s[i];
     const float be = b_s[i];
@@ -208,7 +202,7 @@ __device__ __forceinline__ void gdn_tile(
         sr[r][vv].z = al * sr[r][vv].z + w * kk[vv].z;
         sr[r][vv].w = al * sr[r][vv].w + w * kk[vv].w;
       }
-      if (emit && cl == 0) o_s[i - pc][rl] = al * uq[r] + w * kq_s[i - pc];
+      if (emit && cl == 0) o_s[i - pc][rl] = al * uq[r] + w * kq;
     }
     if (i == store_at) {
 #pragma unroll

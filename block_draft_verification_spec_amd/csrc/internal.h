@@ -76,8 +76,11 @@ struct AttnArgs {
 // Number of splits and tiles per split for a launch (host decision).
 void attn_split_plan(int B, int Hkv, int max_pages, int P, int* nsplit,
                      int* tiles_per_split);
+// Workspace of one attention call: [partial O | partial (m, l)].
 size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D,
                             int max_pages, int P, sv_dtype dtype);
+void attn_workspace_carve(void* ws, int total_T, int Hq, int D, int nsplit,
+                          float** part_o, float** part_ml);
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype,
                             hipStream_t stream);
 

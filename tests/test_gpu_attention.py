@@ -26,7 +26,7 @@ def _run(w, batch, lay, table=None, kc=None, vc=None, write_kv=True):
     dt = bd.SV_BF16 if lay['q'].dtype == torch.bfloat16 else bd.SV_F32
     nbytes = bd.spec_verify_attention_workspace_bytes(
         batch.B, batch.total_T, w.Hq, w.Hkv, w.D, table.shape[1], batch.P, dt)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=DEV)
     err = err_word()
     bd.spec_verify_attention(sv_batch(batch), lay['q'], lay['k_new'], lay['v_new'], kc, vc,
                              table, batch.ctx_lens, out, write_kv=write_kv,
@@ -159,3 +159,24 @@ def test_bad_page_and_capacity_are_flagged():
     assert err & 2
     rows = slice(int(batch.cu_seqlens[2]), int(batch.cu_seqlens[3]))
     assert torch.isnan(out[rows].float()).all()     # skipped sequence untouched
+
+
+
+def test_repeated_calls_on_one_workspace_are_identical():
+    w = wl.Workload('reuse', B=6, k=3, ragged_k=False, ctx=(3000, 9000))
+    batch = wl.make_batch(w, 81, DEV)
+    lay = wl.make_attn_layer(w, batch, 82, DEV)
+    nbytes = bd.spec_verify_attention_workspace_bytes(
+        batch.B, batch.total_T, w.Hq, w.Hkv, w.D, batch.block_table.shape[1], batch.P,
+        bd.SV_BF16)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device=DEV)   # garbage scratch
+    outs = []
+    for _ in range(3):
+        out = torch.full_like(lay['q'], float('nan'))
+        bd.spec_verify_attention(sv_batch(batch), lay['q'], lay['k_new'], lay['v_new'],
+                                 lay['k_cache'].clone(), lay['v_cache'].clone(),
+                                 batch.block_table, batch.ctx_lens, out, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    _check(w, batch, lay)

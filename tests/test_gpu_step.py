@@ -49,7 +49,7 @@ def run_step(w, batch, layers, acc, mode, schedule=bd.SV_SCHEDULE_TWO_PHASE, pen
                                       acc.get('draft_logits'), acc.get('u_accept'),
                                       acc.get('u_final')))
     sb = sv_batch(batch)
-    ws = torch.empty(max(1, bd.spec_verify_step_workspace_bytes(sb, args)), dtype=torch.uint8,
+    ws = torch.zeros(max(1, bd.spec_verify_step_workspace_bytes(sb, args)), dtype=torch.uint8,
                      device=DEV)
     result = torch.full((batch.B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
     commit = torch.full((batch.B,), -7, dtype=torch.int32, device=DEV)
