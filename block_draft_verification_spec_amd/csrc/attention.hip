@@ -17,9 +17,10 @@
 //     16-row tiles; one KV read serves all of them;
 //   * the page ids a split touches are read once into LDS, so a tile's K/V
 //     loads never wait on a block-table load;
-//   * a 64-key tile of K and V is loaded with coalesced 16-byte loads into
-//     registers (prefetched one tile ahead), K is stored row-major in LDS and
-//     V transposed (4 keys x 8 dims per thread, transposed in registers);
+//   * a 64-key tile of K and V is loaded with coalesced 16-byte loads into a
+//     ring of register buffers (up to 3 tiles ahead), K is stored row-major
+//     in LDS and V transposed (4 keys x 8 dims per thread, transposed in
+//     registers);
 //   * wave w owns keys 16 w .. 16 w + 15 of every tile:
 //       S^T (16 keys x 16 rows) = K Q^T   with mfma_f32_16x16x32_bf16
 //       O^T (16 dims x 16 rows) += V^T P^T with mfma_f32_16x16x16bf16_1k
@@ -52,6 +53,13 @@ union U16x8 {
   uint16_t h[8];
 };
 
+// 16-bit element e (0..7, a compile-time constant after unrolling) of a
+// 16-byte vector, as the low half of a 32-bit value.
+__device__ __forceinline__ uint32_t half16(const uint4& u, int e) {
+  const uint32_t w = e < 2 ? u.x : (e < 4 ? u.y : (e < 6 ? u.z : u.w));
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
 __device__ __forceinline__ int seq_tiles(int L, int T) { return (L + T + kKT - 1) / kKT; }
 
 // Validate a sequence for attention.  Returns false (and maybe flags) if the
@@ -83,9 +91,13 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 // --------------------------------------------------------------------------
 // bf16 MFMA split kernel
 // --------------------------------------------------------------------------
+constexpr int kMaxTilesPerSplit = 16;
 constexpr int kMaxSplitPages = 72;  // pages a split may touch (tiles_per_split <= 16, P >= 16)
 
-template <int D, int NQT>
+// PF: tiles in flight per workgroup (a ring of register buffers).  Registers
+// are the largest staging store of a CU, so the loads of PF tiles are kept
+// outstanding while the current tile is computed from LDS.
+template <int D, int NQT, int PF>
 __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   constexpr int CPK = D / 8;        // 16-byte chunks per key row
   constexpr int KPT = CPK / 4;      // keys per thread per tile (4 or 2)
@@ -152,35 +164,53 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
 
   // ---- per-thread slice of a tile: keys KPT*kb .. +KPT-1, dims 8*dc .. +7
   const int dc = tid % CPK, kb = tid / CPK;
-  uint4 kreg[KPT], vreg[KPT];
-  auto load_tile = [&](int tile) {
+  // Branch-free tile load: every thread issues the same 2 * KPT loads for
+  // every tile, so the compiler's wait counts stay exact across the ring.
+  // Keys at or past the split's end (pos_end) read a valid dummy row (an
+  // in-flight row of the sequence) and are zeroed; they are also masked.
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+  auto load_tile = [&](int tile, uint4 (&kreg)[KPT], uint4 (&vreg)[KPT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int p = tile * kKT + KPT * kb + i;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (p < L + T) {
-        const int pid = s_pages[p / P - first_page];
-        const long long po =
-            pid < 0 ? -1 : ((static_cast<long long>(pid) * a.Hkv + g) * P + (p % P)) * D + 8 * dc;
-        if (p < L) {
-          if (po >= 0) {
-            kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + po);
-            vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + po);
-          }
-        } else {
-          const size_t off = (static_cast<size_t>(x0 + p - L) * a.Hkv + g) * D + 8 * dc;
-          kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + off);
-          vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + off);
-          if (a.write_kv && po >= 0) {
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + po) = kv;
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + po) = vv;
-          }
-        }
-      }
-      kreg[i] = kv;
-      vreg[i] = vv;
+      const int pc = min(p, pos_end - 1);
+      const int pid = s_pages[pc / P - first_page];
+      const bool in_ctx = p < L && p < pos_end && pid >= 0;
+      const bool in_new = p >= L && p < pos_end;
+      const size_t off_c =
+          ((static_cast<size_t>(max(pid, 0)) * a.Hkv + g) * P + (pc % P)) * D + 8 * dc;
+      const size_t off_n =
+          (static_cast<size_t>(x0 + min(max(p - L, 0), T - 1)) * a.Hkv + g) * D + 8 * dc;
+      uint4 kv = *reinterpret_cast<const uint4*>(in_ctx ? kc + off_c : kn + off_n);
+      uint4 vv = *reinterpret_cast<const uint4*>(in_ctx ? vc + off_c : vn + off_n);
+      // zero by mask, not by select: a select lets the compiler move the
+      // load under a branch, which breaks the exact wait counts
+      const uint32_t keep = (in_ctx || in_new) ? 0xffffffffu : 0u;
+      kreg[i] = make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
+      vreg[i] = make_uint4(vv.x & keep, vv.y & keep, vv.z & keep, vv.w & keep);
     }
   };
+
+  // Write-through of the in-flight K/V rows into their slots, by the split
+  // that owns those positions (reads of them come from k_new / v_new).
+  if (a.write_kv) {
+    for (int idx = tid; idx < T * CPK; idx += kThreads) {
+      const int j = idx / CPK, c = idx - j * CPK;
+      const int p = L + j;
+      if (p < t_begin * kKT || p >= pos_end) continue;
+      const int pid = s_pages[p / P - first_page];
+      if (pid < 0) continue;
+      const size_t off_c = ((static_cast<size_t>(pid) * a.Hkv + g) * P + (p % P)) * D + 8 * c;
+      const size_t off_n = (static_cast<size_t>(x0 + j) * a.Hkv + g) * D + 8 * c;
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + off_c) =
+          *reinterpret_cast<const uint4*>(kn + off_n);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + off_c) =
+          *reinterpret_cast<const uint4*>(vn + off_n);
+    }
+  }
 
   float4_t oacc[NQT][NDT];
   float m_run[NQT], l_run[NQT];
@@ -193,85 +223,104 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   }
   const float sl2 = a.scale * kLog2e;
 
-  load_tile(t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    __syncthreads();  // previous tile's LDS reads are done
-    // K rows: 16-byte stores; V transposed: KPT keys of one dim per store.
+  auto write_lds = [&](const uint4 (&kreg)[KPT], const uint4 (&vreg)[KPT]) __attribute__((always_inline)) {
+      // K rows: 16-byte stores; V transposed: KPT keys of one dim per store.
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      *reinterpret_cast<uint4*>(Ks + (KPT * kb + i) * KS + 8 * dc) = kreg[i];
+      for (int i = 0; i < KPT; ++i)
+        *reinterpret_cast<uint4*>(Ks + (KPT * kb + i) * KS + 8 * dc) = kreg[i];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t hv[KPT];
+      for (int e = 0; e < 8; ++e) {
+        uint32_t hv[KPT];
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        U16x8 t;
-        t.u = vreg[i];
-        hv[i] = t.h[e];
+        for (int i = 0; i < KPT; ++i) hv[i] = half16(vreg[i], e);
+        uint16_t* dst = Vt + (8 * dc + e) * VS + KPT * kb;
+        if constexpr (KPT == 4) {
+          uint2 pk;
+          pk.x = hv[0] | (hv[1] << 16);
+          pk.y = hv[2] | (hv[3] << 16);
+          *reinterpret_cast<uint2*>(dst) = pk;
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
+        }
       }
-      uint16_t* dst = Vt + (8 * dc + e) * VS + KPT * kb;
-      if constexpr (KPT == 4) {
-        uint2 pk;
-        pk.x = static_cast<uint32_t>(hv[0]) | (static_cast<uint32_t>(hv[1]) << 16);
-        pk.y = static_cast<uint32_t>(hv[2]) | (static_cast<uint32_t>(hv[3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) =
-            static_cast<uint32_t>(hv[0]) | (static_cast<uint32_t>(hv[1]) << 16);
-      }
-    }
-    __syncthreads();
-    if (tile + 1 < t_end) load_tile(tile + 1);
-
-    const int kbase = tile * kKT + 16 * w;  // first key of this wave
+  };
+  auto compute_tile = [&](int tile) __attribute__((always_inline)) {
+      const int kbase = tile * kKT + 16 * w;  // first key of this wave
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NQT; ++nt) {
+        float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        U16x8 af;
-        af.u = *reinterpret_cast<const uint4*>(Ks + (16 * w + lr) * KS + 32 * ks + 8 * lg);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, qf[nt][ks], s, 0, 0, 0);
-      }
-      // lane holds S^T[key 4 lg + r][row lr]
-      const int m = 16 * nt + lr;
-      const int j = m / G;
-      const int lim = (m < M) ? L + j : -1;  // last visible position
-      float sv[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = kbase + 4 * lg + r;
-        sv[r] = (p <= lim) ? s[r] * sl2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[r]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[nt], tmax);
-      short4_t pf;
-      float psum = 0.f;
-      if (m_new == -INFINITY) {
-        pf = short4_t{0, 0, 0, 0};
-      } else {
-        const float alpha = exp2f(m_run[nt] - m_new);
+        for (int ks = 0; ks < NKS; ++ks) {
+          U16x8 af;
+          af.u = *reinterpret_cast<const uint4*>(Ks + (16 * w + lr) * KS + 32 * ks + 8 * lg);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, qf[nt][ks], s, 0, 0, 0);
+        }
+        // lane holds S^T[key 4 lg + r][row lr]
+        const int m = 16 * nt + lr;
+        const int j = m / G;
+        const int lim = (m < M) ? L + j : -1;  // last visible position
+        float sv[4];
+        float tmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint16_t hb = f32_to_bf16(exp2f(sv[r] - m_new));
-          pf[r] = static_cast<short>(hb);
-          psum += bf16_to_f32(hb);
+          const int p = kbase + 4 * lg + r;
+          sv[r] = (p <= lim && p < pos_end) ? s[r] * sl2 : -INFINITY;
+          tmax = fmaxf(tmax, sv[r]);
         }
-        l_run[nt] = l_run[nt] * alpha + psum;
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run[nt], tmax);
+        short4_t pf;
+        float psum = 0.f;
+        if (m_new == -INFINITY) {
+          pf = short4_t{0, 0, 0, 0};
+        } else {
+          const float alpha = exp2f(m_run[nt] - m_new);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] *= alpha;
-        m_run[nt] = m_new;
-      }
+          for (int r = 0; r < 4; ++r) {
+            const uint16_t hb = f32_to_bf16(exp2f(sv[r] - m_new));
+            pf[r] = static_cast<short>(hb);
+            psum += bf16_to_f32(hb);
+          }
+          l_run[nt] = l_run[nt] * alpha + psum;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const short4_t vf =
-            *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS + 16 * w + 4 * lg);
-        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, oacc[nt][dt], 0, 0, 0);
+          for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] *= alpha;
+          m_run[nt] = m_new;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const short4_t vf =
+              *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS + 16 * w + 4 * lg);
+          oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, oacc[nt][dt], 0, 0, 0);
+        }
       }
-    }
+  };
+  // one tile: LDS store of its buffer, refill the buffer PF tiles ahead,
+  // compute from LDS
+  auto consume = [&](int tile, uint4 (&kreg)[KPT], uint4 (&vreg)[KPT]) __attribute__((always_inline)) {
+    __syncthreads();  // previous tile's LDS reads are done
+    write_lds(kreg, vreg);
+    __syncthreads();
+    load_tile(tile + PF, kreg, vreg);
+    compute_tile(tile);
+  };
+  // The ring runs a whole number of PF-tile rounds; tiles past t_end are
+  // fully masked and read only the dummy row.
+  uint4 kr0[KPT], vr0[KPT], kr1[KPT], vr1[KPT], kr2[KPT], vr2[KPT], kr3[KPT], vr3[KPT];
+  load_tile(t_begin, kr0, vr0);
+  if constexpr (PF > 1) load_tile(t_begin + 1, kr1, vr1);
+  if constexpr (PF > 2) load_tile(t_begin + 2, kr2, vr2);
+  if constexpr (PF > 3) load_tile(t_begin + 3, kr3, vr3);
+  // Fully unrolled (no loop back edge: the compiler would drain every
+  // outstanding load there); uniform early exit once the split is done.
+#pragma unroll
+  for (int round = 0; round < kMaxTilesPerSplit / PF; ++round) {
+    const int tile = t_begin + round * PF;
+    if (tile >= t_end) break;
+    consume(tile, kr0, vr0);
+    if constexpr (PF > 1) consume(tile + 1, kr1, vr1);
+    if constexpr (PF > 2) consume(tile + 2, kr2, vr2);
+    if constexpr (PF > 3) consume(tile + 3, kr3, vr3);
   }
   if (bad_page) flag_error(a.err, SV_DERR_PAGE);
 
@@ -469,7 +518,9 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
 
 template <int D, int NQT>
 void launch_bf16(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_split_bf16<D, NQT>), dim3(a.nsplit, a.Hkv, a.B), dim3(kThreads), 0,
+  // deeper prefetch where the accumulators leave room for it
+  constexpr int PF = NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
+  hipLaunchKernelGGL((attn_split_bf16<D, NQT, PF>), dim3(a.nsplit, a.Hkv, a.B), dim3(kThreads), 0,
                      stream, a);
 }
 
@@ -481,7 +532,7 @@ void attn_split_plan(int B, int Hkv, int max_pages, int P, int* nsplit, int* til
   const long long pairs = static_cast<long long>(B) * Hkv;
   const int want = static_cast<int>(std::max<long long>(1, (2048 + pairs - 1) / pairs));
   int tps = (max_tiles + want - 1) / want;
-  tps = std::min(16, std::max(4, tps));
+  tps = std::min(kMaxTilesPerSplit, std::max(4, tps));
   *tiles_per_split = tps;
   *nsplit = std::max(1, (max_tiles + tps - 1) / tps);
 }
