@@ -65,6 +65,9 @@ sv_status check_attn(const sv_batch* batch, const void* q, const void* k_new, co
     if (D != 64 && D != 128) return fail(SV_EDTYPE, "%s: bf16 path needs D in {64,128} (got %d)", who, D);
     if (P < 16 || !(P % 64 == 0 || 64 % P == 0))
       return fail(SV_EINVAL, "%s: page_size %d must be 16, 32 or a multiple of 64", who, P);
+    if (batch->B > 2048)
+      return fail(SV_ECAPACITY, "%s: the bf16 path takes at most 2048 sequences (got %d)", who,
+                  batch->B);
     if ((Hq / Hkv) * batch->max_T > 64)
       return fail(SV_ECAPACITY, "%s: (Hq/Hkv)*max_T = %d exceeds 64 query rows", who,
                   (Hq / Hkv) * batch->max_T);
@@ -109,8 +112,8 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
   a.write_kv = write_kv ? 1 : 0;
   a.err = err;
   if (dtype == SV_BF16) {
-    sv::attn_split_plan(a.B, Hkv, max_pages, P, &a.nsplit, &a.tiles_per_split);
-    sv::attn_workspace_carve(ws, a.total_T, Hq, D, a.nsplit, &a.part_o, &a.part_ml);
+    a.n_wg = sv::attn_stream_grid(D, Hq / Hkv, a.max_T);
+    sv::attn_workspace_carve(ws, a.B, Hkv, D, a.n_wg, &a.seg_meta, &a.part_o, &a.part_ml);
   }
   return a;
 }

@@ -11,12 +11,13 @@
 // KV append is an idempotent in-place write; the length update happens after
 // acceptance).
 //
-// bf16 path (one workgroup = 4 waves per (split, kv head, sequence)):
+// bf16 path (workgroups of 4 waves streaming balanced tile ranges, see the
+// stream kernel below):
 //   * the G = Hq / Hkv query heads of a KV head and the T_b verify tokens form
 //     M = G * T_b query rows (row m = token m / G, head m % G), padded to
 //     16-row tiles; one KV read serves all of them;
-//   * the page ids a split touches are read once into LDS, so a tile's K/V
-//     loads never wait on a block-table load;
+//   * the page ids of up to 256 tiles are staged in LDS at a time, so a
+//     tile's K/V loads never wait on a block-table load;
 //   * a 64-key tile of K and V is loaded with coalesced 16-byte loads into a
 //     ring of register buffers (up to 3 tiles ahead), K is stored row-major
 //     in LDS and V transposed (4 keys x 8 dims per thread, transposed in
@@ -26,12 +27,13 @@
 //       O^T (16 dims x 16 rows) += V^T P^T with mfma_f32_16x16x16bf16_1k
 //     so the online-softmax state of a query row and its output columns sit
 //     in the same lane and the rescale needs no shuffle;
-//   * the 4 waves merge their (max, sum, O) in LDS in a fixed order, and the
-//     split writes a partial (fp32) or, if it is the only split of its
-//     sequence, the final output;
-//   * a combine kernel merges the splits with the log-sum-exp rule
-//       m = max_s m_s, l = sum_s e^(m_s - m) l_s, o = sum_s e^(m_s - m) O_s / l.
+//   * the 4 waves merge their (max, sum, O) in LDS in a fixed order.
 // fp32 path: one wave per (query token, head), plain VALU online softmax.
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "device_common.h"
 #include "internal.h"
@@ -46,6 +48,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(4))) float float4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 union U16x8 {
   uint4 u;
@@ -57,6 +60,10 @@ union U16x8 {
 // 16-byte vector, as the low half of a 32-bit value.
 __device__ __forceinline__ uint32_t half16(const uint4& u, int e) {
   const uint32_t w = e < 2 ? u.x : (e < 4 ? u.y : (e < 6 ? u.z : u.w));
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+__device__ __forceinline__ uint32_t half16(u32x4_t u, int e) {
+  const uint32_t w = u[e >> 1];
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
@@ -89,16 +96,40 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 }
 
 // --------------------------------------------------------------------------
-// bf16 MFMA split kernel
+// bf16 MFMA stream kernel
 // --------------------------------------------------------------------------
-constexpr int kMaxTilesPerSplit = 16;
-constexpr int kMaxSplitPages = 72;  // pages a split may touch (tiles_per_split <= 16, P >= 16)
+// Work split: the (sequence, KV head) segments are laid end to end as one
+// sequence of N 64-key tiles (segment s = b * Hkv + g holds the tiles of
+// sequence b, head g, in position order), and workgroup w of W streams the
+// contiguous range [w N / W, (w + 1) N / W).  Every workgroup gets the same
+// number of tiles whatever the context lengths, and pays its start-up once.
+// A segment cut by range boundaries is computed in pieces; piece (s, w) of a
+// segment writes its partial (max, sum, O) to slot s + w (distinct for every
+// piece, since segments advance with w) and the workgroup that owns the
+// segment's first tile records which workgroups cover the segment; a combine
+// kernel merges the pieces.  A segment covered by one workgroup is written
+// directly.
+constexpr int kMaxB = 2048;        // sequences per call on the bf16 path
+constexpr int kChunkTiles = 256;   // tiles whose page ids are staged at once
+constexpr int kRound = 12;         // tiles per unrolled round (a multiple of PF)
+constexpr int kMaxRows = 64;       // query rows per (sequence, KV head)
 
-// PF: tiles in flight per workgroup (a ring of register buffers).  Registers
-// are the largest staging store of a CU, so the loads of PF tiles are kept
-// outstanding while the current tile is computed from LDS.
+// One tile's slice of K and V held by a thread.
+template <int KPT>
+struct TileRegs {
+  u32x4_t k[KPT];
+  u32x4_t v[KPT];
+};
+
+__host__ __device__ inline int piece_wg(int t, int W, int N) {
+  // the workgroup whose range [w N / W, (w + 1) N / W) holds tile t
+  return static_cast<int>(((static_cast<long long>(t) + 1) * W - 1) / N);
+}
+
+// PF: tiles in flight per workgroup (a ring of register buffers; registers
+// are the largest staging store of a CU).
 template <int D, int NQT, int PF>
-__global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void attn_stream_bf16(AttnArgs a) {
   constexpr int CPK = D / 8;        // 16-byte chunks per key row
   constexpr int KPT = CPK / 4;      // keys per thread per tile (4 or 2)
   constexpr int KS = D + 8;         // K row stride in LDS (bf16 elements)
@@ -106,297 +137,365 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16(AttnArgs a) {
   constexpr int NDT = D / 16;       // 16-dim output tiles
   constexpr int NKS = D / 32;       // k-steps of the QK^T product
   constexpr int ROWS = 16 * NQT;
+  static_assert(kRound % PF == 0, "round must hold whole ring turns");
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKT * KS + D * VS];
   __shared__ float wm[4][ROWS];
   __shared__ float wl[4][ROWS];
-  __shared__ int s_pages[kMaxSplitPages];
+  __shared__ int s_pre[kMaxB + 1];           // tiles before sequence b (all its heads)
+  __shared__ int s_ids[kChunkTiles * 4];     // page ids of the current chunk
+  __shared__ int s_scan[kThreads];
   uint16_t* Ks = lds;
   uint16_t* Vt = lds + kKT * KS;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  int x0, T, L;
-  if (!attn_seq_ok(a, b, &x0, &T, &L, split == 0 && g == 0 && tid == 0)) return;
-  const int ntiles = seq_tiles(L, T);
-  const int t_begin = split * a.tiles_per_split;
-  if (t_begin >= ntiles) return;
-  const int t_end = min(ntiles, t_begin + a.tiles_per_split);
-  const int nsplit_b = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  const int G = a.Hq / a.Hkv;
-  const int M = G * T;
-  const int P = a.P;
+  const int B = a.B, Hkv = a.Hkv, G = a.Hq / a.Hkv, P = a.P;
 
-  // ---- the split's page ids, read once: positions t_begin*64 .. pos_end-1
-  const int pos_end = min(t_end * kKT, L + T);
-  const int first_page = (t_begin * kKT) / P;
-  const int n_pages = (pos_end - 1) / P - first_page + 1;
-  bool bad_page = false;
-  if (tid < n_pages) {
-    int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + first_page + tid];
-    if (pid < 0 || pid >= a.num_pages) {
-      bad_page = true;
-      pid = -1;
-    }
-    s_pages[tid] = pid;
-  }
-
-  // ---- Q fragments (B operand of S^T = K Q^T): row 16 nt + lr, dims
-  // 32 s + 8 lg .. + 7.
-  bf16x8_t qf[NQT][NKS];
+  // ---- tiles of every sequence and their prefix over segments
+  constexpr int kPer = (kMaxB + kThreads - 1) / kThreads;
+  int part[kPer];
+  int run = 0;
 #pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    const int m = 16 * nt + lr;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      U16x8 t;
-      if (m < M) {
-        const int j = m / G, hh = m - j * G;
-        const size_t off = (static_cast<size_t>(x0 + j) * a.Hq + g * G + hh) * D + 32 * s + 8 * lg;
-        t.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-      } else {
-        t.u = make_uint4(0, 0, 0, 0);
-      }
-      qf[nt][s] = t.v;
+  for (int i = 0; i < kPer; ++i) {
+    const int b = tid * kPer + i;
+    int v = 0;
+    if (b < B) {
+      int x0, T, L;
+      if (attn_seq_ok(a, b, &x0, &T, &L, blockIdx.x == 0)) v = seq_tiles(L, T) * Hkv;
     }
+    run += v;
+    part[i] = run;
   }
+  s_scan[tid] = run;
   __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = s_scan[tid] - run;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = tid * kPer + i;
+    if (b < B) s_pre[b + 1] = excl + part[i];
+  }
+  if (tid == 0) s_pre[0] = 0;
+  __syncthreads();
+  const int N = s_pre[B];
+  const int W = gridDim.x, wg = blockIdx.x;
+  const int t_lo = static_cast<int>(static_cast<long long>(wg) * N / W);
+  const int t_hi = static_cast<int>(static_cast<long long>(wg + 1) * N / W);
 
-  // ---- per-thread slice of a tile: keys KPT*kb .. +KPT-1, dims 8*dc .. +7
-  const int dc = tid % CPK, kb = tid / CPK;
-  // Branch-free tile load: every thread issues the same 2 * KPT loads for
-  // every tile, so the compiler's wait counts stay exact across the ring.
-  // Keys at or past the split's end (pos_end) read a valid dummy row (an
-  // in-flight row of the sequence) and are zeroed; they are also masked.
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
   const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
   const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
-  auto load_tile = [&](int tile, uint4 (&kreg)[KPT], uint4 (&vreg)[KPT]) __attribute__((always_inline)) {
+  const int dc = tid % CPK, kb = tid / CPK;  // thread's slice: keys KPT*kb.., dims 8*dc..
+  const float sl2 = a.scale * kLog2e;
+  bool bad_page = false;
+
+  // State of the current piece and chunk (function scope, read by the
+  // always-inlined helpers below).
+  int b = 0, g = 0, x0 = 0, T = 1, L = 0, M = 1, pos_end = 1, first_page = 0;
+  bf16x8_t qf[NQT][NKS];
+  float4_t oacc[NQT][NDT];
+  float m_run[NQT], l_run[NQT];
+
+  // Branch-free tile load: every thread issues the same 2 * KPT loads for
+  // every tile, so the compiler's wait counts stay exact.  A key at or past
+  // pos_end (or in a bad page) reads a valid in-flight row of the sequence
+  // instead: its score is masked, so it gets probability exactly 0, and the
+  // finite values it brings add exactly 0.  Nothing is done to the loaded
+  // values before they are stored to LDS, so no instruction waits on a load
+  // earlier than the tile's own turn in the ring.
+  auto load_tile = [&](int tile) __attribute__((always_inline)) {
+    TileRegs<KPT> r;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int p = tile * kKT + KPT * kb + i;
       const int pc = min(p, pos_end - 1);
-      const int pid = s_pages[pc / P - first_page];
+      const int pid = s_ids[pc / P - first_page];
       const bool in_ctx = p < L && p < pos_end && pid >= 0;
-      const bool in_new = p >= L && p < pos_end;
       const size_t off_c =
-          ((static_cast<size_t>(max(pid, 0)) * a.Hkv + g) * P + (pc % P)) * D + 8 * dc;
+          ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pc % P)) * D + 8 * dc;
       const size_t off_n =
-          (static_cast<size_t>(x0 + min(max(p - L, 0), T - 1)) * a.Hkv + g) * D + 8 * dc;
-      uint4 kv = *reinterpret_cast<const uint4*>(in_ctx ? kc + off_c : kn + off_n);
-      uint4 vv = *reinterpret_cast<const uint4*>(in_ctx ? vc + off_c : vn + off_n);
-      // zero by mask, not by select: a select lets the compiler move the
-      // load under a branch, which breaks the exact wait counts
-      const uint32_t keep = (in_ctx || in_new) ? 0xffffffffu : 0u;
-      kreg[i] = make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
-      vreg[i] = make_uint4(vv.x & keep, vv.y & keep, vv.z & keep, vv.w & keep);
+          (static_cast<size_t>(x0 + min(max(p - L, 0), T - 1)) * Hkv + g) * D + 8 * dc;
+      r.k[i] = *reinterpret_cast<const u32x4_t*>(in_ctx ? kc + off_c : kn + off_n);
+      r.v[i] = *reinterpret_cast<const u32x4_t*>(in_ctx ? vc + off_c : vn + off_n);
     }
+    return r;
   };
-
-  // Write-through of the in-flight K/V rows into their slots, by the split
-  // that owns those positions (reads of them come from k_new / v_new).
-  if (a.write_kv) {
-    for (int idx = tid; idx < T * CPK; idx += kThreads) {
-      const int j = idx / CPK, c = idx - j * CPK;
-      const int p = L + j;
-      if (p < t_begin * kKT || p >= pos_end) continue;
-      const int pid = s_pages[p / P - first_page];
-      if (pid < 0) continue;
-      const size_t off_c = ((static_cast<size_t>(pid) * a.Hkv + g) * P + (p % P)) * D + 8 * c;
-      const size_t off_n = (static_cast<size_t>(x0 + j) * a.Hkv + g) * D + 8 * c;
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + off_c) =
-          *reinterpret_cast<const uint4*>(kn + off_n);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + off_c) =
-          *reinterpret_cast<const uint4*>(vn + off_n);
-    }
-  }
-
-  float4_t oacc[NQT][NDT];
-  float m_run[NQT], l_run[NQT];
+  // K rows: 16-byte stores; V transposed: KPT keys of one dim per store.
+  auto write_lds = [&](const TileRegs<KPT>& r) __attribute__((always_inline)) {
 #pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
+    for (int i = 0; i < KPT; ++i)
+      *reinterpret_cast<u32x4_t*>(Ks + (KPT * kb + i) * KS + 8 * dc) = r.k[i];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  const float sl2 = a.scale * kLog2e;
-
-  auto write_lds = [&](const uint4 (&kreg)[KPT], const uint4 (&vreg)[KPT]) __attribute__((always_inline)) {
-      // K rows: 16-byte stores; V transposed: KPT keys of one dim per store.
+    for (int e = 0; e < 8; ++e) {
+      uint32_t hv[KPT];
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        *reinterpret_cast<uint4*>(Ks + (KPT * kb + i) * KS + 8 * dc) = kreg[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t hv[KPT];
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) hv[i] = half16(vreg[i], e);
-        uint16_t* dst = Vt + (8 * dc + e) * VS + KPT * kb;
-        if constexpr (KPT == 4) {
-          uint2 pk;
-          pk.x = hv[0] | (hv[1] << 16);
-          pk.y = hv[2] | (hv[3] << 16);
-          *reinterpret_cast<uint2*>(dst) = pk;
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
-        }
+      for (int i = 0; i < KPT; ++i) hv[i] = half16(r.v[i], e);
+      uint16_t* dst = Vt + (8 * dc + e) * VS + KPT * kb;
+      if constexpr (KPT == 4) {
+        uint2 pk;
+        pk.x = hv[0] | (hv[1] << 16);
+        pk.y = hv[2] | (hv[3] << 16);
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
       }
+    }
   };
+  // wave w owns keys 16 w .. 16 w + 15 of the tile
   auto compute_tile = [&](int tile) __attribute__((always_inline)) {
-      const int kbase = tile * kKT + 16 * w;  // first key of this wave
+    const int kbase = tile * kKT + 16 * w;
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) {
-        float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NQT; ++nt) {
+      float4_t sacc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          U16x8 af;
-          af.u = *reinterpret_cast<const uint4*>(Ks + (16 * w + lr) * KS + 32 * ks + 8 * lg);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, qf[nt][ks], s, 0, 0, 0);
-        }
-        // lane holds S^T[key 4 lg + r][row lr]
-        const int m = 16 * nt + lr;
-        const int j = m / G;
-        const int lim = (m < M) ? L + j : -1;  // last visible position
-        float sv[4];
-        float tmax = -INFINITY;
+      for (int ks = 0; ks < NKS; ++ks) {
+        U16x8 af;
+        af.u = *reinterpret_cast<const uint4*>(Ks + (16 * w + lr) * KS + 32 * ks + 8 * lg);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, qf[nt][ks], sacc, 0, 0, 0);
+      }
+      // lane holds S^T[key 4 lg + r][row lr]
+      const int m = 16 * nt + lr;
+      const int lim = (m < M) ? L + m / G : -1;  // last visible position
+      float sv[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = kbase + 4 * lg + r;
+        sv[r] = (p <= lim && p < pos_end) ? sacc[r] * sl2 : -INFINITY;
+        tmax = fmaxf(tmax, sv[r]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run[nt], tmax);
+      short4_t pf;
+      if (m_new == -INFINITY) {
+        pf = short4_t{0, 0, 0, 0};
+      } else {
+        const float alpha = exp2f(m_run[nt] - m_new);
+        float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int p = kbase + 4 * lg + r;
-          sv[r] = (p <= lim && p < pos_end) ? s[r] * sl2 : -INFINITY;
-          tmax = fmaxf(tmax, sv[r]);
+          const uint16_t hb = f32_to_bf16(exp2f(sv[r] - m_new));
+          pf[r] = static_cast<short>(hb);
+          psum += bf16_to_f32(hb);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run[nt], tmax);
-        short4_t pf;
-        float psum = 0.f;
-        if (m_new == -INFINITY) {
-          pf = short4_t{0, 0, 0, 0};
-        } else {
-          const float alpha = exp2f(m_run[nt] - m_new);
+        l_run[nt] = l_run[nt] * alpha + psum;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint16_t hb = f32_to_bf16(exp2f(sv[r] - m_new));
-            pf[r] = static_cast<short>(hb);
-            psum += bf16_to_f32(hb);
-          }
-          l_run[nt] = l_run[nt] * alpha + psum;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] *= alpha;
-          m_run[nt] = m_new;
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const short4_t vf =
-              *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS + 16 * w + 4 * lg);
-          oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, oacc[nt][dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] *= alpha;
+        m_run[nt] = m_new;
       }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const short4_t vf =
+            *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS + 16 * w + 4 * lg);
+        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, oacc[nt][dt], 0, 0, 0);
+      }
+    }
   };
   // one tile: LDS store of its buffer, refill the buffer PF tiles ahead,
   // compute from LDS
-  auto consume = [&](int tile, uint4 (&kreg)[KPT], uint4 (&vreg)[KPT]) __attribute__((always_inline)) {
+  auto consume = [&](int tile, TileRegs<KPT>& slot) __attribute__((always_inline)) {
     __syncthreads();  // previous tile's LDS reads are done
-    write_lds(kreg, vreg);
+    write_lds(slot);
     __syncthreads();
-    load_tile(tile + PF, kreg, vreg);
+    slot = load_tile(tile + PF);
     compute_tile(tile);
   };
-  // The ring runs a whole number of PF-tile rounds; tiles past t_end are
-  // fully masked and read only the dummy row.
-  uint4 kr0[KPT], vr0[KPT], kr1[KPT], vr1[KPT], kr2[KPT], vr2[KPT], kr3[KPT], vr3[KPT];
-  load_tile(t_begin, kr0, vr0);
-  if constexpr (PF > 1) load_tile(t_begin + 1, kr1, vr1);
-  if constexpr (PF > 2) load_tile(t_begin + 2, kr2, vr2);
-  if constexpr (PF > 3) load_tile(t_begin + 3, kr3, vr3);
-  // Fully unrolled (no loop back edge: the compiler would drain every
-  // outstanding load there); uniform early exit once the split is done.
-#pragma unroll
-  for (int round = 0; round < kMaxTilesPerSplit / PF; ++round) {
-    const int tile = t_begin + round * PF;
-    if (tile >= t_end) break;
-    consume(tile, kr0, vr0);
-    if constexpr (PF > 1) consume(tile + 1, kr1, vr1);
-    if constexpr (PF > 2) consume(tile + 2, kr2, vr2);
-    if constexpr (PF > 3) consume(tile + 3, kr3, vr3);
-  }
-  if (bad_page) flag_error(a.err, SV_DERR_PAGE);
 
-  // ---- merge the four waves in a fixed order
-#pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    float l = l_run[nt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (lg == 0) {
-      wm[w][16 * nt + lr] = m_run[nt];
-      wl[w][16 * nt + lr] = l;
+  TileRegs<KPT> r0, r1, r2;
+
+  for (int t = t_lo; t < t_hi;) {
+    // ---- the piece: segment (b, g) tiles [lt_begin, lt_end)
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] <= t) lo = mid;
+      else hi = mid;
     }
-  }
-  __syncthreads();  // also: all LDS tile reads are done
-  float* R = reinterpret_cast<float*>(lds);  // [ROWS][D] fp32 (fits in the tile space)
-  float scale_w[NQT];
+    b = lo;
+    const int nt_b = (s_pre[b + 1] - s_pre[b]) / Hkv;
+    g = (t - s_pre[b]) / nt_b;
+    const int seg_start = s_pre[b] + g * nt_b;
+    const int lt_begin = t - seg_start;
+    const int lt_end = min(t_hi, seg_start + nt_b) - seg_start;
+    const int s = b * Hkv + g;
+    const bool whole = lt_begin == 0 && lt_end == nt_b;
+    if (lt_begin == 0 && tid == 0) {
+      a.seg_meta[2 * s] = wg;
+      a.seg_meta[2 * s + 1] = piece_wg(seg_start + nt_b - 1, W, N);
+    }
+    t = seg_start + lt_end;
+
+    x0 = a.cu[b];
+    T = a.cu[b + 1] - x0;
+    L = a.ctx_lens[b];
+    M = G * T;
+
+    // Q fragments (B operand of S^T = K Q^T): row 16 nt + lr, dims 32 s + 8 lg ..
 #pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    const int m = 16 * nt + lr;
-    float mm = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
-    scale_w[nt] = (wm[w][m] == -INFINITY) ? 0.f : exp2f(wm[w][m] - mm);
-  }
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+    for (int nt = 0; nt < NQT; ++nt) {
+      const int m = 16 * nt + lr;
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) {
+      for (int ks = 0; ks < NKS; ++ks) {
+        U16x8 tq;
+        if (m < M) {
+          const int j = m / G, hh = m - j * G;
+          const size_t off =
+              (static_cast<size_t>(x0 + j) * a.Hq + g * G + hh) * D + 32 * ks + 8 * lg;
+          tq.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+        } else {
+          tq.u = make_uint4(0, 0, 0, 0);
+        }
+        qf[nt][ks] = tq.v;
+      }
+    }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          float4* dst = reinterpret_cast<float4*>(R + (16 * nt + lr) * D + 16 * dt + 4 * lg);
-          const float4_t v = oacc[nt][dt] * scale_w[nt];
-          if (ww == 0) {
-            *dst = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            float4 c = *dst;
-            *dst = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
+    for (int nt = 0; nt < NQT; ++nt) {
+      m_run[nt] = -INFINITY;
+      l_run[nt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int c0 = lt_begin; c0 < lt_end; c0 += kChunkTiles) {
+      const int c1 = min(lt_end, c0 + kChunkTiles);
+      pos_end = min(c1 * kKT, L + T);  // keys at or past it are masked
+      first_page = (c0 * kKT) / P;
+      const int n_pages = (pos_end - 1) / P - first_page + 1;
+      __syncthreads();  // the previous chunk is done with s_ids and the tile LDS
+      for (int i = tid; i < n_pages; i += kThreads) {
+        int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + first_page + i];
+        if (pid < 0 || pid >= a.num_pages) {
+          bad_page = true;
+          pid = -1;
+        }
+        s_ids[i] = pid;
+      }
+      __syncthreads();
+
+      // write-through of the in-flight K/V rows that fall in this chunk (reads
+      // of those positions come from k_new / v_new)
+      if (a.write_kv) {
+        for (int idx = tid; idx < T * CPK; idx += kThreads) {
+          const int j = idx / CPK, c = idx - j * CPK;
+          const int p = L + j;
+          if (p < c0 * kKT || p >= pos_end) continue;
+          const int pid = s_ids[p / P - first_page];
+          if (pid < 0) continue;
+          const size_t off_c = ((static_cast<size_t>(pid) * Hkv + g) * P + (p % P)) * D + 8 * c;
+          const size_t off_n = (static_cast<size_t>(x0 + j) * Hkv + g) * D + 8 * c;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + off_c) =
+              *reinterpret_cast<const uint4*>(kn + off_n);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + off_c) =
+              *reinterpret_cast<const uint4*>(vn + off_n);
+        }
+      }
+
+      r0 = load_tile(c0);
+      if constexpr (PF > 1) r1 = load_tile(c0 + 1);
+      if constexpr (PF > 2) r2 = load_tile(c0 + 2);
+      // Rounds of kRound tiles are unrolled: inside a round the ring's wait
+      // counts are exact; the compiler drains outstanding loads only at the
+      // round's back edge, which the PF-deep prefetch has already covered.
+      for (int tile = c0; tile < c1; tile += kRound) {
+#pragma unroll
+        for (int u = 0; u < kRound; u += PF) {
+          if (tile + u >= c1) break;
+          consume(tile + u, r0);
+          if constexpr (PF > 1) {
+            if (tile + u + 1 >= c1) break;
+            consume(tile + u + 1, r1);
+          }
+          if constexpr (PF > 2) {
+            if (tile + u + 2 >= c1) break;
+            consume(tile + u + 2, r2);
           }
         }
       }
     }
-    __syncthreads();
-  }
 
-  // ---- this split's result: row m -> (token j, head g*G + hh)
-  for (int i = tid; i < M * (D / 4); i += kThreads) {
-    const int m = i / (D / 4), d4 = (i - m * (D / 4)) * 4;
-    const float mm = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
-    float ls = 0.f;
+    // ---- merge the four waves in a fixed order
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
-      if (wm[ww][m] != -INFINITY) ls += wl[ww][m] * exp2f(wm[ww][m] - mm);
-    const int j = m / G, hh = m - j * G;
-    const size_t row = static_cast<size_t>(x0 + j) * a.Hq + g * G + hh;
-    const float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
-    if (nsplit_b == 1) {
-      const float inv = 1.f / ls;
-      uint2 pk;
-      pk.x = f32_to_bf16(o.x * inv) | (static_cast<uint32_t>(f32_to_bf16(o.y * inv)) << 16);
-      pk.y = f32_to_bf16(o.z * inv) | (static_cast<uint32_t>(f32_to_bf16(o.w * inv)) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + d4) = pk;
-    } else {
-      const size_t pi = row * a.nsplit + split;
-      *reinterpret_cast<float4*>(a.part_o + pi * D + d4) = o;
-      if (d4 == 0) {
-        a.part_ml[2 * pi] = mm;
-        a.part_ml[2 * pi + 1] = ls;
+    for (int nt = 0; nt < NQT; ++nt) {
+      float l = l_run[nt];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      if (lg == 0) {
+        wm[w][16 * nt + lr] = m_run[nt];
+        wl[w][16 * nt + lr] = l;
+      }
+    }
+    __syncthreads();  // also: all LDS tile reads are done
+    float* R = reinterpret_cast<float*>(lds);  // [ROWS][D] fp32 (fits in the tile space)
+    float scale_w[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      const int m = 16 * nt + lr;
+      const float mm = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
+      scale_w[nt] = (wm[w][m] == -INFINITY) ? 0.f : exp2f(wm[w][m] - mm);
+    }
+    for (int ww = 0; ww < 4; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            float4* dst = reinterpret_cast<float4*>(R + (16 * nt + lr) * D + 16 * dt + 4 * lg);
+            const float4_t v = oacc[nt][dt] * scale_w[nt];
+            if (ww == 0) {
+              *dst = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              const float4 c = *dst;
+              *dst = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- the piece's result: row m -> (token m / G, head g * G + m % G)
+    for (int i = tid; i < M * (D / 4); i += kThreads) {
+      const int m = i / (D / 4), d4 = (i - m * (D / 4)) * 4;
+      const float mm = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
+      float ls = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+        if (wm[ww][m] != -INFINITY) ls += wl[ww][m] * exp2f(wm[ww][m] - mm);
+      const float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
+      if (whole) {
+        const int j = m / G, hh = m - j * G;
+        const size_t row = static_cast<size_t>(x0 + j) * a.Hq + g * G + hh;
+        const float inv = 1.f / ls;
+        uint2 pk;
+        pk.x = f32_to_bf16(o.x * inv) | (static_cast<uint32_t>(f32_to_bf16(o.y * inv)) << 16);
+        pk.y = f32_to_bf16(o.z * inv) | (static_cast<uint32_t>(f32_to_bf16(o.w * inv)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + d4) = pk;
+      } else {
+        const size_t pi = static_cast<size_t>(s + wg) * kMaxRows + m;
+        *reinterpret_cast<float4*>(a.part_o + pi * D + d4) = o;
+        if (d4 == 0) {
+          a.part_ml[2 * pi] = mm;
+          a.part_ml[2 * pi + 1] = ls;
+        }
       }
     }
   }
+  if (bad_page) flag_error(a.err, SV_DERR_PAGE);
 }
 
 // --------------------------------------------------------------------------
-// log-sum-exp combine of the splits (bf16 path).  A separate launch: the
-// kernel boundary makes every split's partial visible, where a device-scope
-// fence inside the split kernel would write back and invalidate the whole L2
-// of an XCD once per workgroup.
+// log-sum-exp merge of the pieces of a segment (bf16 path).  A separate
+// launch: the kernel boundary makes every piece visible, where a
+// device-scope fence inside the stream kernel would write back and
+// invalidate the whole L2 of an XCD once per workgroup.
+//   m = max_i m_i, l = sum_i e^(m_i - m) l_i, o = sum_i e^(m_i - m) O_i / l
 // --------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
@@ -404,25 +503,29 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   int x0, T, L;
   if (!attn_seq_ok(a, b, &x0, &T, &L, false)) return;
   if (j >= T) return;
-  const int ntiles = seq_tiles(L, T);
-  const int ns = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  if (ns == 1) return;  // written by the split kernel
-  const size_t row = static_cast<size_t>(x0 + j) * a.Hq + h;
-  const size_t pbase = row * a.nsplit;
+  const int G = a.Hq / a.Hkv;
+  const int g = h / G;
+  const int s = b * a.Hkv + g;
+  const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
+  if (wf >= wl_) return;  // one piece: written by the stream kernel
+  const int m = j * G + (h - g * G);
   float mm = -INFINITY;
-  for (int s = 0; s < ns; ++s) mm = fmaxf(mm, a.part_ml[2 * (pbase + s)]);
+  for (int wg = wf; wg <= wl_; ++wg)
+    mm = fmaxf(mm, a.part_ml[2 * (static_cast<size_t>(s + wg) * kMaxRows + m)]);
   float acc[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
   float ls = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = a.part_ml[2 * (pbase + s)];
+  for (int wg = wf; wg <= wl_; ++wg) {
+    const size_t pi = static_cast<size_t>(s + wg) * kMaxRows + m;
+    const float ms = a.part_ml[2 * pi];
     if (ms == -INFINITY) continue;
     const float f = exp2f(ms - mm);
-    ls += f * a.part_ml[2 * (pbase + s) + 1];
+    ls += f * a.part_ml[2 * pi + 1];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] += f * a.part_o[(pbase + s) * D + lane + 64 * e];
+    for (int e = 0; e < D / 64; ++e) acc[e] += f * a.part_o[pi * D + lane + 64 * e];
   }
+  const size_t row = static_cast<size_t>(x0 + j) * a.Hq + h;
   const float inv = 1.f / ls;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e)
@@ -517,52 +620,99 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
 }
 
 template <int D, int NQT>
-void launch_bf16(const AttnArgs& a, hipStream_t stream) {
+constexpr int ring_depth() {
   // deeper prefetch where the accumulators leave room for it
-  constexpr int PF = NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
-  hipLaunchKernelGGL((attn_split_bf16<D, NQT, PF>), dim3(a.nsplit, a.Hkv, a.B), dim3(kThreads), 0,
-                     stream, a);
+  return NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
+}
+
+template <int D, int NQT>
+const void* stream_kernel() {
+  return reinterpret_cast<const void*>(&attn_stream_bf16<D, NQT, ring_depth<D, NQT>()>);
+}
+
+int nqt_for(int G, int max_T) {
+  const int rows = G * max_T;
+  return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+}
+
+const void* stream_kernel_for(int D, int nqt) {
+  if (D == 128) {
+    if (nqt == 1) return stream_kernel<128, 1>();
+    if (nqt == 2) return stream_kernel<128, 2>();
+    return stream_kernel<128, 4>();
+  }
+  if (nqt == 1) return stream_kernel<64, 1>();
+  if (nqt == 2) return stream_kernel<64, 2>();
+  return stream_kernel<64, 4>();
+}
+
+// Resident workgroups of one stream-kernel instance on the current device:
+// the grid that keeps every CU busy without a second wave of workgroups.
+int stream_grid(int D, int nqt) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, D, nqt);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel_for(D, nqt), kThreads, 0) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int n = cus * per_cu;
+  cache[key] = n;
+  return n;
+}
+
+int stream_grid_max(int D) {
+  return std::max(stream_grid(D, 1), std::max(stream_grid(D, 2), stream_grid(D, 4)));
+}
+
+template <int D, int NQT>
+void launch_bf16(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_stream_bf16<D, NQT, ring_depth<D, NQT>()>), dim3(a.n_wg), dim3(kThreads),
+                     0, stream, a);
 }
 
 }  // namespace
 
-void attn_split_plan(int B, int Hkv, int max_pages, int P, int* nsplit, int* tiles_per_split) {
-  const long long max_pos = static_cast<long long>(max_pages) * P;
-  const int max_tiles = static_cast<int>((max_pos + kKT - 1) / kKT);
-  const long long pairs = static_cast<long long>(B) * Hkv;
-  const int want = static_cast<int>(std::max<long long>(1, (2048 + pairs - 1) / pairs));
-  int tps = (max_tiles + want - 1) / want;
-  tps = std::min(kMaxTilesPerSplit, std::max(4, tps));
-  *tiles_per_split = tps;
-  *nsplit = std::max(1, (max_tiles + tps - 1) / tps);
-}
-
 size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D, int max_pages, int P,
                             sv_dtype dtype) {
+  (void)total_T;
+  (void)Hq;
+  (void)max_pages;
+  (void)P;
   if (dtype != SV_BF16) return 0;
-  int ns, tps;
-  attn_split_plan(B, Hkv, max_pages, P, &ns, &tps);
-  const size_t rows = static_cast<size_t>(total_T) * Hq * ns;
-  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~size_t(255);
-  return o_bytes + rows * 2 * sizeof(float);
+  const size_t slots = static_cast<size_t>(B) * Hkv + stream_grid_max(D);
+  const size_t meta = (static_cast<size_t>(B) * Hkv * 2 * sizeof(int) + 255) & ~size_t(255);
+  const size_t o_bytes = (slots * kMaxRows * D * sizeof(float) + 255) & ~size_t(255);
+  return meta + o_bytes + slots * kMaxRows * 2 * sizeof(float);
 }
 
-void attn_workspace_carve(void* ws, int total_T, int Hq, int D, int nsplit, float** part_o,
-                          float** part_ml) {
-  const size_t rows = static_cast<size_t>(total_T) * Hq * nsplit;
-  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~size_t(255);
-  *part_o = static_cast<float*>(ws);
-  *part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_meta,
+                          float** part_o, float** part_ml) {
+  (void)n_wg;
+  const size_t slots = static_cast<size_t>(B) * Hkv + stream_grid_max(D);
+  const size_t meta = (static_cast<size_t>(B) * Hkv * 2 * sizeof(int) + 255) & ~size_t(255);
+  const size_t o_bytes = (slots * kMaxRows * D * sizeof(float) + 255) & ~size_t(255);
+  char* base = static_cast<char*>(ws);
+  *seg_meta = reinterpret_cast<int*>(base);
+  *part_o = reinterpret_cast<float*>(base + meta);
+  *part_ml = reinterpret_cast<float*>(base + meta + o_bytes);
 }
+
+int attn_stream_grid(int D, int G, int max_T) { return stream_grid(D, nqt_for(G, max_T)); }
 
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype, hipStream_t stream) {
   if (dtype == SV_F32) {
     hipLaunchKernelGGL(attn_f32, dim3(a.Hq, a.max_T, a.B), dim3(64), 0, stream, a);
     return hipGetLastError();
   }
-  const int G = a.Hq / a.Hkv;
-  const int rows = G * a.max_T;
-  const int nqt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const int nqt = nqt_for(a.Hq / a.Hkv, a.max_T);
   if (a.D == 128) {
     if (nqt == 1) launch_bf16<128, 1>(a, stream);
     else if (nqt == 2) launch_bf16<128, 2>(a, stream);

@@ -66,21 +66,20 @@ struct AttnArgs {
   float scale;                  // already resolved (never 0)
   int write_kv;
   int32_t* err;
-  // split-KV partials
-  float* part_o;                // [total_T, Hq, nsplit, D]
-  float* part_ml;               // [total_T, Hq, nsplit, 2]
-  int nsplit;                   // splits per sequence (grid.x)
-  int tiles_per_split;          // 64-key tiles per split
+  // stream-kernel grid and the pieces of segments cut by range boundaries
+  int n_wg;                     // workgroups (grid.x)
+  int* seg_meta;                // [B * Hkv][2]: first and last workgroup of a segment
+  float* part_o;                // [(B * Hkv + n_wg) * 64 rows][D]
+  float* part_ml;               // [(B * Hkv + n_wg) * 64 rows][2]
 };
 
-// Number of splits and tiles per split for a launch (host decision).
-void attn_split_plan(int B, int Hkv, int max_pages, int P, int* nsplit,
-                     int* tiles_per_split);
-// Workspace of one attention call: [partial O | partial (m, l)].
+// Workspace of one attention call: [segment meta | partial O | partial (m, l)].
 size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D,
                             int max_pages, int P, sv_dtype dtype);
-void attn_workspace_carve(void* ws, int total_T, int Hq, int D, int nsplit,
+void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_meta,
                           float** part_o, float** part_ml);
+// Grid of the stream kernel for these shapes on the current device.
+int attn_stream_grid(int D, int G, int max_T);
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype,
                             hipStream_t stream);
 
