@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+ATTN_SOURCE = os.path.join(ROOT, 'block_draft_verification_spec_amd', 'csrc', 'attention.hip')
+TRAFFIC_FILE = os.path.join(ROOT, 'profiles', 'attention_hybrid_step_64l_traffic.txt')
 
 
 def parse():
@@ -60,6 +62,24 @@ def calibrate_copy():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({'calibrate_copy_bytes': n, 'copies': 3}), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per attention launch (stream kernel + combine kernel) from the
+    committed FETCH_SIZE / WRITE_SIZE counter runs, already scaled by the copy
+    calibration; None when the attention source changed since they were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for ln in open(TRAFFIC_FILE):
+        parts = ln.split()
+        if len(parts) == 2 and not ln.startswith('#'):
+            vals[parts[0]] = parts[1]
+    sha = hashlib.sha256(open(ATTN_SOURCE, 'rb').read()).hexdigest()
+    if vals.get('source_sha256') != sha:
+        return None
+    return int(float(vals['fetch_bytes_per_launch']) + float(vals['write_bytes_per_launch']))
 
 
 def attn_bytes(w, batch):
@@ -331,10 +351,12 @@ def main():
                    'schedule': args.schedule},
         'step_hbm': {'algorithmic_bytes': b_step, 'GBps': round(gbs, 1),
                      'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4)},
-        'roofline': {'kernel': 'spec_verify_attention (split-KV verify attention, one layer)',
+        'roofline': {'kernel': 'spec_verify_attention, one layer '
+                               '(attn_stream_bf16 + attn_combine_bf16 launches)',
                      'bound': 'hbm', 'achieved': round(achieved, 1), 'peak': HBM_PEAK_GBS,
                      'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
-                     'traffic': None, 'bytes_per_launch': b_att,
+                     'traffic': measured_traffic(), 'traffic_unit': 'HBM bytes per launch',
+                     'bytes_per_launch': b_att,
                      'launch_ms': round(att_ms_mean, 4), 'launches': len(att_ms)},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4)},
