@@ -221,8 +221,11 @@ __global__ __launch_bounds__(kThreads) void attn_stream_bf16(AttnArgs a) {
           ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pc % P)) * D + 8 * dc;
       const size_t off_n =
           (static_cast<size_t>(x0 + min(max(p - L, 0), T - 1)) * Hkv + g) * D + 8 * dc;
-      r.k[i] = *reinterpret_cast<const u32x4_t*>(in_ctx ? kc + off_c : kn + off_n);
-      r.v[i] = *reinterpret_cast<const u32x4_t*>(in_ctx ? vc + off_c : vn + off_n);
+      // streaming loads: every context byte is read once per launch
+      r.k[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(in_ctx ? kc + off_c : kn + off_n));
+      r.v[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(in_ctx ? vc + off_c : vn + off_n));
     }
     return r;
   };

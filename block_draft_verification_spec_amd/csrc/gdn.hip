@@ -32,6 +32,8 @@ constexpr int kRowsPerBlock = 64;
 constexpr int kRowsPerThread = 4;
 constexpr int kMaxTok = 2 * kMaxT;
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float dot4(const float4& a, const float4& b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
@@ -209,8 +211,11 @@ __device__ __forceinline__ void gdn_tile(
       for (int r = 0; r < kRowsPerThread; ++r) {
         float* rowp = tile + static_cast<size_t>(row0 + rg + 16 * r) * DK;
 #pragma unroll
-        for (int vv = 0; vv < NV4; ++vv)
-          *reinterpret_cast<float4*>(rowp + vv * 64 + 4 * cl) = sr[r][vv];
+        for (int vv = 0; vv < NV4; ++vv) {
+          // streaming store: this launch does not read the state again
+          const f32x4_t t = {sr[r][vv].x, sr[r][vv].y, sr[r][vv].z, sr[r][vv].w};
+          __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(rowp + vv * 64 + 4 * cl));
+        }
       }
     }
   }
