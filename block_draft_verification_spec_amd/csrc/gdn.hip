@@ -15,11 +15,22 @@
 // commit runs after acceptance; onnxruntime-genai pull request 2457:
 // CommitPrefix keeps the accepted prefix without a snapshot).
 //
-// Layout of a block: 256 threads = 16 row groups x 16 column lanes.  Thread
-// (row group rg, lane c) holds rows rg + 16 r (r < 4) and, of each row, the
-// elements 64 v + 4 c .. 64 v + 4 c + 3 (v < dk / 64): sixteen consecutive
-// lanes read one 256-byte half row per instruction, fully coalesced.  Token
-// inputs (at most 8 pending + 8 current) are staged in LDS as fp32.
+// Layout of a block: 256 threads = 32 row groups x 8 column lanes.  Thread
+// (row group rg, lane c) holds rows rg and rg + 32 and, of each row, the
+// elements 32 j + 4 c .. 32 j + 4 c + 3 (j < dk / 32): eight consecutive
+// lanes read one 128-byte line of a row per instruction, and a row's dot
+// products reduce over 8 lanes in three DPP steps.  Token inputs (at most 8
+// pending + 8 current) are staged in LDS as fp32.
+//
+// The decay costs no per-element multiply: the registers hold S / g with a
+// block-uniform scale g (the product of the alphas since the last fold), so
+//   S_t = alpha g S' + w k^T = (alpha g) (S' + (w / (alpha g)) k^T),
+// i.e. g <- alpha g and one FMA per element.  If alpha g falls below 2^-20
+// (alpha = 0 included) the decay is applied to the registers instead.  The
+// scale is folded back (g = 1) after the last replayed pending token, so the
+// current tokens run exactly as from the committed state loaded afresh; the
+// stored state is g S' and storing never changes the registers, so outputs
+// do not depend on where (or whether) the state is stored.
 
 #include "device_common.h"
 #include "internal.h"
@@ -29,13 +40,28 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 64;
-constexpr int kRowsPerThread = 4;
+constexpr int kRowsPerThread = 2;
+constexpr int kLanesPerRow = 8;
+constexpr float kMinScale = 0x1p-20f;  // below it the decay is applied, not deferred
 constexpr int kMaxTok = 2 * kMaxT;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float dot4(const float4& a, const float4& b) {
-  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+// acc + a . b as a chain of fused multiply-adds
+__device__ __forceinline__ float fma4(const float4& a, const float4& b, float acc) {
+  acc = fmaf(a.x, b.x, acc);
+  acc = fmaf(a.y, b.y, acc);
+  acc = fmaf(a.z, b.z, acc);
+  return fmaf(a.w, b.w, acc);
+}
+
+// Sum over aligned groups of 8 lanes, result in every lane of the group:
+// mirror within the half row, then swap lane pairs 2 apart and 1 apart.
+__device__ __forceinline__ float lane8_sum(float v) {
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
+  return v;
 }
 
 template <int DK>
@@ -59,7 +85,7 @@ __device__ __forceinline__ void gdn_tile(
     const float* __restrict__ palpha, const float* __restrict__ pbeta, int b,
     int h, int rb, bool report) {
   using L = io<IO>;
-  constexpr int NV4 = DK / 64;
+  constexpr int NV4 = DK / 32;  // float4 per row per thread
   auto& k_s = sm.k_s;
   auto& q_s = sm.q_s;
   auto& v_s = sm.v_s;
@@ -112,18 +138,19 @@ __device__ __forceinline__ void gdn_tile(
   const int H = s.H;
   const int DV = s.dv;
   const int row0 = rb * kRowsPerBlock;
-  const int cl = tid & 15;
-  const int rg = tid >> 4;
+  const int cl = tid & (kLanesPerRow - 1);
+  const int rg = tid / kLanesPerRow;
+  constexpr int kRowStride = kThreads / kLanesPerRow;  // rows rg + kRowStride r
   float* tile = state + (static_cast<size_t>(slot) * H + h) * DV * DK;
 
   // ---- issue the state loads first: they are the long-latency traffic
   float4 sr[kRowsPerThread][NV4];
 #pragma unroll
   for (int r = 0; r < kRowsPerThread; ++r) {
-    const float* rowp = tile + static_cast<size_t>(row0 + rg + 16 * r) * DK;
+    const float* rowp = tile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
 #pragma unroll
-    for (int vv = 0; vv < NV4; ++vv)
-      sr[r][vv] = *reinterpret_cast<const float4*>(rowp + vv * 64 + 4 * cl);
+    for (int j = 0; j < NV4; ++j)
+      sr[r][j] = *reinterpret_cast<const float4*>(rowp + 32 * j + 4 * cl);
   }
 
   // ---- stage token inputs as fp32
@@ -152,69 +179,101 @@ __device__ __forceinline__ void gdn_tile(
   }
   __syncthreads();
 
-  // ---- the recurrence, one token at a time
+  // ---- the recurrence, one token at a time (registers hold S / g)
+  float g = 1.f;
   for (int i = 0; i < n_tot; ++i) {
     const bool emit = verify && i >= pc;
-    float4 kk[NV4];
-#pragma unroll
-    for (int vv = 0; vv < NV4; ++vv)
-      kk[vv] = *reinterpret_cast<const float4*>(&k_s[i][vv * 64 + 4 * cl]);
+    // Dot products of both rows with k_t (and q_t), one float4 of k / q at
+    // a time so that few registers besides the state are live.
     float uk[kRowsPerThread], uq[kRowsPerThread];
     float kq = 0.f;
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int vv = 0; vv < NV4; ++vv) acc += dot4(sr[r][vv], kk[vv]);
-      uk[r] = acc;
-    }
+    for (int r = 0; r < kRowsPerThread; ++r) uk[r] = uq[r] = 0.f;
     if (emit) {
-      float4 qq[NV4];
 #pragma unroll
-      for (int vv = 0; vv < NV4; ++vv)
-        qq[vv] = *reinterpret_cast<const float4*>(&q_s[i - pc][vv * 64 + 4 * cl]);
+      for (int j = 0; j < NV4; ++j) {
+        const float4 kj = *reinterpret_cast<const float4*>(&k_s[i][32 * j + 4 * cl]);
+        const float4 qj = *reinterpret_cast<const float4*>(&q_s[i - pc][32 * j + 4 * cl]);
+        kq = fma4(kj, qj, kq);
 #pragma unroll
-      for (int vv = 0; vv < NV4; ++vv) kq += dot4(kk[vv], qq[vv]);
+        for (int r = 0; r < kRowsPerThread; ++r) {
+          uk[r] = fma4(sr[r][j], kj, uk[r]);
+          uq[r] = fma4(sr[r][j], qj, uq[r]);
+        }
+      }
+      kq = lane8_sum(kq);
 #pragma unroll
-      for (int r = 0; r < kRowsPerThread; ++r) {
-        float acc = 0.f;
+      for (int r = 0; r < kRowsPerThread; ++r) uq[r] = lane8_sum(uq[r]);
+    } else {
 #pragma unroll
-        for (int vv = 0; vv < NV4; ++vv) acc += dot4(sr[r][vv], qq[vv]);
-        uq[r] = acc;
+      for (int j = 0; j < NV4; ++j) {
+        const float4 kj = *reinterpret_cast<const float4*>(&k_s[i][32 * j + 4 * cl]);
+#pragma unroll
+        for (int r = 0; r < kRowsPerThread; ++r) uk[r] = fma4(sr[r][j], kj, uk[r]);
       }
     }
-    // full-row dot products: sum over the 16 lanes that share the rows
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) uk[r] = row16_sum(uk[r]);
-    if (emit) {
-      kq = row16_sum(kq);
-#pragma unroll
-      for (int r = 0; r < kRowsPerThread; ++r) uq[r] = row16_sum(uq[r]);
-    }
+    for (int r = 0; r < kRowsPerThread; ++r) uk[r] = lane8_sum(uk[r]);
     const float al = a_s[i];
     const float be = b_s[i];
+    float g_new = al * g;  // scale of S_t
+    float w[kRowsPerThread];
 #pragma unroll
     for (int r = 0; r < kRowsPerThread; ++r) {
-      const int rl = rg + 16 * r;
-      const float w = be * (v_s[i][rl] - al * uk[r]);
+      const int rl = rg + kRowStride * r;
+      w[r] = be * (v_s[i][rl] - al * (g * uk[r]));
+      // o_t = S_t q_t = alpha S_{t-1} q_t + w (k_t . q_t)
+      if (emit && cl == 0) o_s[i - pc][rl] = g_new * uq[r] + w[r] * kq;
+    }
+    if (g_new < kMinScale) {  // block-uniform and rare: apply the decay now
 #pragma unroll
-      for (int vv = 0; vv < NV4; ++vv) {
-        sr[r][vv].x = al * sr[r][vv].x + w * kk[vv].x;
-        sr[r][vv].y = al * sr[r][vv].y + w * kk[vv].y;
-        sr[r][vv].z = al * sr[r][vv].z + w * kk[vv].z;
-        sr[r][vv].w = al * sr[r][vv].w + w * kk[vv].w;
+      for (int r = 0; r < kRowsPerThread; ++r)
+#pragma unroll
+        for (int j = 0; j < NV4; ++j) {
+          sr[r][j].x *= g_new;
+          sr[r][j].y *= g_new;
+          sr[r][j].z *= g_new;
+          sr[r][j].w *= g_new;
+        }
+      g_new = 1.f;
+    }
+    const float inv_g = 1.f / g_new;
+    float wg[kRowsPerThread];
+#pragma unroll
+    for (int r = 0; r < kRowsPerThread; ++r) wg[r] = w[r] * inv_g;
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) {
+      const float4 kj = *reinterpret_cast<const float4*>(&k_s[i][32 * j + 4 * cl]);
+#pragma unroll
+      for (int r = 0; r < kRowsPerThread; ++r) {
+        sr[r][j].x = fmaf(wg[r], kj.x, sr[r][j].x);
+        sr[r][j].y = fmaf(wg[r], kj.y, sr[r][j].y);
+        sr[r][j].z = fmaf(wg[r], kj.z, sr[r][j].z);
+        sr[r][j].w = fmaf(wg[r], kj.w, sr[r][j].w);
       }
-      if (emit && cl == 0) o_s[i - pc][rl] = al * uq[r] + w * kq;
+    }
+    g = g_new;
+    if (i == pc - 1) {  // end of the replayed tokens: fold the scale
+#pragma unroll
+      for (int r = 0; r < kRowsPerThread; ++r)
+#pragma unroll
+        for (int j = 0; j < NV4; ++j) {
+          sr[r][j].x *= g;
+          sr[r][j].y *= g;
+          sr[r][j].z *= g;
+          sr[r][j].w *= g;
+        }
+      g = 1.f;
     }
     if (i == store_at) {
 #pragma unroll
       for (int r = 0; r < kRowsPerThread; ++r) {
-        float* rowp = tile + static_cast<size_t>(row0 + rg + 16 * r) * DK;
+        float* rowp = tile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
 #pragma unroll
-        for (int vv = 0; vv < NV4; ++vv) {
+        for (int j = 0; j < NV4; ++j) {
           // streaming store: this launch does not read the state again
-          const f32x4_t t = {sr[r][vv].x, sr[r][vv].y, sr[r][vv].z, sr[r][vv].w};
-          __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(rowp + vv * 64 + 4 * cl));
+          const f32x4_t t = {g * sr[r][j].x, g * sr[r][j].y, g * sr[r][j].z, g * sr[r][j].w};
+          __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(rowp + 32 * j + 4 * cl));
         }
       }
     }
