@@ -18,10 +18,10 @@
 //     16-row tiles; one KV read serves all of them;
 //   * the page ids of up to 256 tiles are staged in LDS at a time, so a
 //     tile's K/V loads never wait on a block-table load;
-//   * a 64-key tile of K and V is loaded with coalesced 16-byte loads into a
-//     ring of register buffers (up to 3 tiles ahead), K is stored row-major
-//     in LDS and V transposed (4 keys x 8 dims per thread, transposed in
-//     registers);
+//   * a 64-key tile of K and V is loaded with coalesced 16-byte streaming
+//     loads into registers one tile ahead of the compute (three workgroups
+//     per CU keep enough tiles in flight), K is stored row-major in LDS and
+//     V transposed (4 keys x 8 dims per thread, transposed in registers);
 //   * wave w owns keys 16 w .. 16 w + 15 of every tile:
 //       S^T (16 keys x 16 rows) = K Q^T   with mfma_f32_16x16x32_bf16
 //       O^T (16 dims x 16 rows) += V^T P^T with mfma_f32_16x16x16bf16_1k
@@ -128,8 +128,11 @@ __host__ __device__ inline int piece_wg(int t, int W, int N) {
 
 // PF: tiles in flight per workgroup (a ring of register buffers; registers
 // are the largest staging store of a CU).
-template <int D, int NQT, int PF>
-__global__ __launch_bounds__(kThreads) void attn_stream_bf16(AttnArgs a) {
+// WPE: waves per SIMD the register allocation is held to (workgroups per
+// CU; the LDS of three fits in one CU).
+template <int D, int NQT, int PF, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_stream_bf16(AttnArgs a) {
   constexpr int CPK = D / 8;        // 16-byte chunks per key row
   constexpr int KPT = CPK / 4;      // keys per thread per tile (4 or 2)
   constexpr int KS = D + 8;         // K row stride in LDS (bf16 elements)
@@ -622,15 +625,22 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
   if (lane + 64 < D) out[lane + 64] = o[1] * inv;
 }
 
+// One tile in flight per workgroup and as many resident workgroups as the
+// registers allow measured fastest: more workgroups hide latency better than
+// a deeper ring in fewer of them.
 template <int D, int NQT>
 constexpr int ring_depth() {
-  // deeper prefetch where the accumulators leave room for it
+  return 1;
+}
+template <int D, int NQT>
+constexpr int waves_per_simd() {
   return NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
 }
 
 template <int D, int NQT>
 const void* stream_kernel() {
-  return reinterpret_cast<const void*>(&attn_stream_bf16<D, NQT, ring_depth<D, NQT>()>);
+  return reinterpret_cast<const void*>(
+      &attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>);
 }
 
 int nqt_for(int G, int max_T) {
@@ -677,7 +687,8 @@ int stream_grid_max(int D) {
 
 template <int D, int NQT>
 void launch_bf16(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_stream_bf16<D, NQT, ring_depth<D, NQT>()>), dim3(a.n_wg), dim3(kThreads),
+  hipLaunchKernelGGL((attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>),
+                     dim3(a.n_wg), dim3(kThreads),
                      0, stream, a);
 }
 
