@@ -72,6 +72,7 @@ struct GdnSmem {
   float a_s[kMaxTok];
   float b_s[kMaxTok];
   float o_s[kMaxT][kRowsPerBlock];
+  float kq_s[kMaxT];  // k_t . q_t of the current tokens
 };
 
 // COMMIT_ONLY_NP: compile-time COMMIT_ONLY without pending tokens (the
@@ -92,6 +93,7 @@ __device__ __forceinline__ void gdn_tile(
   auto& a_s = sm.a_s;
   auto& b_s = sm.b_s;
   auto& o_s = sm.o_s;
+  auto& kq_s = sm.kq_s;
 
   const int tid = threadIdx.x;
   // ---- validate the sequence (uniform over the block)
@@ -178,6 +180,17 @@ __device__ __forceinline__ void gdn_tile(
     b_s[t] = t < pc ? pbeta[gi] : beta[gi];
   }
   __syncthreads();
+  // k_t . q_t of every current token, once per block: 16 lanes per token
+  if (verify && tid < 16 * T) {
+    const int t = tid >> 4, c16 = tid & 15;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DK / 16; ++e)
+      acc = fmaf(k_s[pc + t][16 * e + c16], q_s[t][16 * e + c16], acc);
+    acc = row16_sum(acc);
+    if (c16 == 0) kq_s[t] = acc;
+  }
+  __syncthreads();
 
   // ---- the recurrence, one token at a time (registers hold S / g)
   float g = 1.f;
@@ -194,14 +207,13 @@ __device__ __forceinline__ void gdn_tile(
       for (int j = 0; j < NV4; ++j) {
         const float4 kj = *reinterpret_cast<const float4*>(&k_s[i][32 * j + 4 * cl]);
         const float4 qj = *reinterpret_cast<const float4*>(&q_s[i - pc][32 * j + 4 * cl]);
-        kq = fma4(kj, qj, kq);
 #pragma unroll
         for (int r = 0; r < kRowsPerThread; ++r) {
           uk[r] = fma4(sr[r][j], kj, uk[r]);
           uq[r] = fma4(sr[r][j], qj, uq[r]);
         }
       }
-      kq = lane8_sum(kq);
+      kq = kq_s[i - pc];
 #pragma unroll
       for (int r = 0; r < kRowsPerThread; ++r) uq[r] = lane8_sum(uq[r]);
     } else {
@@ -237,7 +249,8 @@ __device__ __forceinline__ void gdn_tile(
         }
       g_new = 1.f;
     }
-    const float inv_g = 1.f / g_new;
+    // any fixed reciprocal keeps S = g S' consistent: the hardware one
+    const float inv_g = __builtin_amdgcn_rcpf(g_new);
     float wg[kRowsPerThread];
 #pragma unroll
     for (int r = 0; r < kRowsPerThread; ++r) wg[r] = w[r] * inv_g;
