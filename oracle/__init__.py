@@ -46,11 +46,13 @@ library routines, brute force, exact enumeration or Monte-Carlo); see
 from .attention import append_kv, gather_context, verify_attention
 from .gdn import GDN_COMMIT_ONLY, GDN_VERIFY_COMMIT, GDN_VERIFY_ONLY, gdn_step
 from .accept import greedy_accept, icdf, rejection_accept, softmax64
+from .short_conv import CONV_COMMIT_ONLY, CONV_VERIFY_COMMIT, CONV_VERIFY_ONLY, conv_step
 from .step import verify_step
 
 __all__ = [
     "append_kv", "gather_context", "verify_attention",
     "GDN_VERIFY_COMMIT", "GDN_VERIFY_ONLY", "GDN_COMMIT_ONLY", "gdn_step",
     "greedy_accept", "rejection_accept", "softmax64", "icdf",
+    "CONV_VERIFY_COMMIT", "CONV_VERIFY_ONLY", "CONV_COMMIT_ONLY", "conv_step",
     "verify_step",
 ]

@@ -60,6 +60,12 @@ class Workload:
     accept_modes: Tuple[str, ...] = ()
     pool_factor: float = 1.0   # physical pages / pages needed
     min_pool_pages: int = 0
+    conv_K: int = 4            # short-convolution width of the linear-attention layers
+
+    @property
+    def conv_C(self):
+        """Channels through the short convolution: the q, k and v features."""
+        return self.H * (2 * self.dk + self.dv)
 
     @property
     def max_T(self):
@@ -217,6 +223,24 @@ def make_gdn_layer(w: Workload, batch: Batch, seed: int, device='cpu',
         'state': state,
         'q': q.to(w.gdn_dtype), 'k': k.to(w.gdn_dtype), 'v': v.to(w.gdn_dtype),
         'alpha': alpha.float().contiguous(), 'beta': beta.float().contiguous(),
+    }
+
+
+def make_conv_layer(w: Workload, batch: Batch, seed: int, device='cpu',
+                    num_slots=None, bias=True):
+    """Short-convolution inputs: rolling state and inputs ~N(0, 1) in the GDN
+    I/O dtype, taps ~N(0, 1/K) and bias ~N(0, 0.1) in fp32."""
+    g = generator(seed, device)
+    Tt, C, K = batch.total_T, w.conv_C, w.conv_K
+    ns = batch.B if num_slots is None else num_slots
+    state = torch.randn((ns, K - 1, C), generator=g, device=device)
+    x = torch.randn((Tt, C), generator=g, device=device)
+    weight = torch.randn((C, K), generator=g, device=device).mul_(K ** -0.5)
+    b = torch.randn((C,), generator=g, device=device).mul_(0.1) if bias else None
+    return {
+        'state': state.to(w.gdn_dtype), 'x': x.to(w.gdn_dtype),
+        'weight': weight.float().contiguous(),
+        'bias': None if b is None else b.float().contiguous(),
     }
 
 
