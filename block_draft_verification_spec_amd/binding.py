@@ -37,6 +37,10 @@ class SvGdnPending(ctypes.Structure):
                 ('beta', _vp), ('commit_len', _vp)]
 
 
+class SvConvPending(ctypes.Structure):
+    _fields_ = [('batch', SvBatch), ('x', _vp), ('commit_len', _vp)]
+
+
 class SvAttnLayer(ctypes.Structure):
     _fields_ = [('q', _vp), ('k_new', _vp), ('v_new', _vp), ('k_cache', _vp),
                 ('v_cache', _vp), ('out', _vp)]
@@ -84,6 +88,10 @@ _SIGS = {
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, _c_i32, _vp, _vp,
          _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
          ctypes.POINTER(SvGdnPending), _vp, _vp], ctypes.c_int),
+    'short_conv_verify_commit': (
+        [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, _c_i32, _vp, _vp, _vp,
+         ctypes.c_int, _c_i32, _vp, _vp, _c_i32, _c_i32, ctypes.POINTER(SvConvPending),
+         _vp, _vp], ctypes.c_int),
     'spec_accept_workspace_bytes': ([_c_i32, _c_i32, _c_i32, ctypes.c_int], _sz),
     'spec_accept': (
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, ctypes.c_int, _c_i32,
@@ -221,6 +229,34 @@ def gdn_verify_commit(batch, mode, state, q, k, v, alpha, beta, commit_len,
 def make_gdn_pending(batch, k, v, alpha, beta, commit_len):
     return SvGdnPending(batch, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                         _i32(commit_len, 'commit_len'))
+
+
+SV_ACT_NONE = 0
+SV_ACT_SILU = 1
+
+
+def short_conv_verify_commit(batch, mode, state, x, weight, bias, commit_len, out,
+                             state_slot=None, activation=SV_ACT_NONE, pending=None, err=None,
+                             stream=None):
+    """Short causal convolution verify / commit (``short_conv_verify_commit``).
+
+    state [num_slots, K-1, C] and x / out [total_T, C] in one I/O dtype;
+    weight fp32 [C, K]; bias fp32 [C] or None; commit_len int32 [B].
+    ``pending``: an ``SvConvPending`` or None.
+    """
+    num_slots, Km1, C = state.shape
+    if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError('weight and bias must be float32')
+    _check(lib().short_conv_verify_commit(
+        ctypes.byref(batch), int(mode), _ptr(state), _i32(state_slot, 'state_slot'),
+        num_slots, _ptr(x), _ptr(weight), _ptr(bias), _dtype(x), int(activation),
+        _i32(commit_len, 'commit_len'), _ptr(out), C, Km1 + 1,
+        ctypes.byref(pending) if pending is not None else None,
+        _i32(err, 'err'), _stream(stream)))
+
+
+def make_conv_pending(batch, x, commit_len):
+    return SvConvPending(batch, _ptr(x), _i32(commit_len, 'commit_len'))
 
 
 def spec_accept_workspace_bytes(B, total_T, V, mode):

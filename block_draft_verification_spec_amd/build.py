@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, 'csrc')
 INCLUDE = os.path.join(ROOT, 'include')
 BUILD = os.path.join(ROOT, '_build')
 LIB = os.path.join(PKG, 'libspecverify.so')
-SOURCES = ['api.cpp', 'gdn.hip', 'accept.hip', 'attention.hip']
+SOURCES = ['api.cpp', 'gdn.hip', 'conv.hip', 'accept.hip', 'attention.hip']
 
 HIPCC = shutil.which('hipcc') or '/opt/rocm/bin/hipcc'
 FLAGS = [

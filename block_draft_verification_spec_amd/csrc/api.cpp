@@ -233,6 +233,67 @@ sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, float* stat
   return hip_status(sv::launch_gdn(s, p, io_dtype, stream), who);
 }
 
+sv_status short_conv_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state,
+                                   const int32_t* state_slot, int32_t num_slots, const void* x,
+                                   const float* weight, const float* bias, sv_dtype io_dtype,
+                                   int32_t activation, const int32_t* commit_len, void* out,
+                                   int32_t C, int32_t K, const sv_conv_pending* pending,
+                                   int32_t* err, hipStream_t stream) {
+  const char* who = "short_conv_verify_commit";
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  if (mode != SV_GDN_VERIFY_COMMIT && mode != SV_GDN_VERIFY_ONLY && mode != SV_GDN_COMMIT_ONLY)
+    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
+  if (io_dtype != SV_F32 && io_dtype != SV_BF16)
+    return fail(SV_EDTYPE, "%s: unsupported io dtype %d", who, static_cast<int>(io_dtype));
+  if (K < 2 || K > 8) return fail(SV_EINVAL, "%s: K must be in 2..8 (got %d)", who, K);
+  if (C < 1) return fail(SV_EINVAL, "%s: C must be >= 1", who);
+  if (activation != SV_ACT_NONE && activation != SV_ACT_SILU)
+    return fail(SV_EINVAL, "%s: unknown activation %d", who, activation);
+  if (!state || !x || !weight) return fail(SV_EINVAL, "%s: state, x and weight are required", who);
+  if (num_slots < 1) return fail(SV_EINVAL, "%s: num_slots must be >= 1", who);
+  if (!state_slot && num_slots < batch->B)
+    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  if (mode != SV_GDN_COMMIT_ONLY && !out)
+    return fail(SV_EINVAL, "%s: out is required unless COMMIT_ONLY", who);
+  if (mode != SV_GDN_VERIFY_ONLY && !commit_len)
+    return fail(SV_EINVAL, "%s: commit_len is required unless VERIFY_ONLY", who);
+  sv::ConvArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.mode = mode;
+  a.state_slot = state_slot;
+  a.num_slots = num_slots;
+  a.commit_len = commit_len;
+  a.C = C;
+  a.K = K;
+  a.activation = activation;
+  a.state = state;
+  a.x = x;
+  a.weight = weight;
+  a.bias = bias;
+  a.out = out;
+  a.err = err;
+  if (pending) {
+    st = check_batch(&pending->batch, "short_conv_verify_commit (pending)");
+    if (st != SV_OK) return st;
+    if (pending->batch.B != batch->B)
+      return fail(SV_EINVAL, "%s: pending batch has B=%d, this batch B=%d", who,
+                  pending->batch.B, batch->B);
+    if (!pending->x || !pending->commit_len)
+      return fail(SV_EINVAL, "%s: pending x and commit_len are required", who);
+    a.has_pending = 1;
+    a.p_total_T = pending->batch.total_T;
+    a.p_max_T = pending->batch.max_T;
+    a.p_cu = pending->batch.cu_seqlens;
+    a.p_commit = pending->commit_len;
+    a.px = pending->x;
+  }
+  return hip_status(sv::launch_conv(a, io_dtype, stream), who);
+}
+
 size_t spec_accept_workspace_bytes(int32_t B, int32_t total_T, int32_t V, sv_accept_mode mode) {
   if (B < 1 || total_T < 1 || V < 1) return 0;
   return sv::accept_workspace_bytes(B, total_T, V, mode);

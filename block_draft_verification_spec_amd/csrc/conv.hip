@@ -1,0 +1,146 @@
+// Short causal convolution of the linear-attention layers: verify and commit.
+//
+// The packed varlen operator of onnxruntime-genai pull request 2457 (commit
+// message on the VarlenCausalConvWithState prefix states) keeps a rolling
+// state of the last K-1 inputs per sequence and publishes the state after
+// every token (slot j = state after local token j).  Per channel c, with
+// z = [state_0 .. state_{K-2}, x_0 .. x_{T-1}] (oldest first):
+//   y_t[c] = act( sum_{i<K} w[c, i] z_{t+i}[c] + bias[c] ),   act = id or SiLU
+// Commit keeps the last K-1 rows of [state, x_0 .. x_{c_b-1}]: the state a run
+// over only the accepted prefix leaves; rejected tokens are never applied.
+// With pending tokens (deferred schedule) the window first advances over the
+// previous step's c_b pending inputs and that state is stored.
+//
+// One thread per (sequence, channel): the window lives in registers, every
+// access is a coalesced row of C channels, and the stored state is a copy of
+// inputs (no arithmetic), so it is exact.
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxTokC = 2 * kMaxT;
+
+template <typename IO, int K>
+__global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs a) {
+  using L = io<IO>;
+  const int b = blockIdx.y;
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const bool report = blockIdx.x == 0 && threadIdx.x == 0;
+  // ---- validate the sequence (uniform over the block)
+  const int x0 = a.cu[b];
+  const int T = a.cu[b + 1] - x0;
+  if (T < 1 || T > a.max_T || x0 < 0 || x0 + T > a.total_T) {
+    if (report) flag_error(a.err, SV_DERR_SEQLEN);
+    return;
+  }
+  const int slot = a.state_slot ? a.state_slot[b] : b;
+  if (slot < 0 || slot >= a.num_slots) {
+    if (report) flag_error(a.err, SV_DERR_SLOT);
+    return;
+  }
+  int cm = 0;
+  if (a.mode != SV_GDN_VERIFY_ONLY) {
+    cm = a.commit_len[b];
+    if (cm < 0 || cm > T) {
+      if (report) flag_error(a.err, SV_DERR_COMMIT);
+      return;
+    }
+  }
+  int px0 = 0, pc = 0;
+  if (a.has_pending) {
+    px0 = a.p_cu[b];
+    const int pT = a.p_cu[b + 1] - px0;
+    if (pT < 1 || pT > a.p_max_T || px0 < 0 || px0 + pT > a.p_total_T) {
+      if (report) flag_error(a.err, SV_DERR_SEQLEN);
+      return;
+    }
+    pc = a.p_commit[b];
+    if (pc < 0 || pc > pT) {
+      if (report) flag_error(a.err, SV_DERR_COMMIT);
+      return;
+    }
+  }
+  if (c >= a.C) return;
+  const int C = a.C;
+  const size_t srow = static_cast<size_t>(slot) * (K - 1);
+
+  // ---- window: the last K-1 inputs, then the pending ones shifted in
+  float win[K - 1];
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) win[i] = L::load(a.state, (srow + i) * C + c);
+  for (int t = 0; t < pc; ++t) {
+#pragma unroll
+    for (int i = 0; i < K - 2; ++i) win[i] = win[i + 1];
+    win[K - 2] = L::load(a.px, static_cast<size_t>(px0 + t) * C + c);
+  }
+
+  const bool verify = a.mode != SV_GDN_COMMIT_ONLY;
+  const int n = verify ? T : cm;  // current tokens read
+  float z[K - 1 + kMaxT];
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) z[i] = win[i];
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t)
+    z[K - 1 + t] = t < n ? L::load(a.x, static_cast<size_t>(x0 + t) * C + c) : 0.f;
+
+  if (verify) {
+    float w[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) w[i] = a.weight[static_cast<size_t>(c) * K + i];
+    const float bias = a.bias ? a.bias[c] : 0.f;
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t >= T) break;
+      float u = 0.f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) u = fmaf(w[i], z[t + i], u);
+      u += bias;
+      if (a.activation == SV_ACT_SILU) u = u / (1.f + expf(-u));
+      L::store(a.out, static_cast<size_t>(x0 + t) * C + c, u);
+    }
+  }
+
+  // ---- store the committed window (a copy of inputs: exact)
+  if (a.mode == SV_GDN_VERIFY_ONLY) {
+    if (pc > 0) {
+#pragma unroll
+      for (int i = 0; i < K - 1; ++i) L::store(a.state, (srow + i) * C + c, win[i]);
+    }
+  } else if (pc > 0 || cm > 0) {
+#pragma unroll
+    for (int i = 0; i < K - 1; ++i) {
+      float v = z[0];
+#pragma unroll
+      for (int s = 0; s <= kMaxT; ++s)  // z[cm + i] with cm a runtime value
+        if (s == cm) v = z[s + i];
+      L::store(a.state, (srow + i) * C + c, v);
+    }
+  }
+}
+
+template <typename IO>
+hipError_t launch_conv_io(const ConvArgs& a, hipStream_t stream) {
+  const dim3 grid((a.C + kThreads - 1) / kThreads, a.B);
+  switch (a.K) {
+    case 2: hipLaunchKernelGGL((conv_kernel<IO, 2>), grid, dim3(kThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((conv_kernel<IO, 3>), grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((conv_kernel<IO, 4>), grid, dim3(kThreads), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((conv_kernel<IO, 5>), grid, dim3(kThreads), 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((conv_kernel<IO, 6>), grid, dim3(kThreads), 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((conv_kernel<IO, 7>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((conv_kernel<IO, 8>), grid, dim3(kThreads), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvArgs& a, sv_dtype io_dt, hipStream_t stream) {
+  return io_dt == SV_BF16 ? launch_conv_io<bf16_t>(a, stream) : launch_conv_io<float>(a, stream);
+}
+
+}  // namespace sv

@@ -28,6 +28,28 @@ struct GdnScalars {
   int32_t* err;
 };
 
+struct ConvArgs {
+  int B, total_T, max_T;
+  const int32_t* cu;            // [B+1]
+  int mode;                     // sv_gdn_mode
+  const int32_t* state_slot;    // [B] or null
+  int num_slots;
+  const int32_t* commit_len;    // [B] or null (VERIFY_ONLY)
+  int C, K, activation;
+  void* state;                  // [num_slots][K-1][C] io dtype
+  const void* x;                // [total_T][C]
+  const float* weight;          // [C][K]
+  const float* bias;            // [C] or null
+  void* out;                    // [total_T][C]
+  int has_pending;
+  int p_total_T, p_max_T;
+  const int32_t* p_cu;          // [B+1]
+  const int32_t* p_commit;      // [B]
+  const void* px;               // [p_total_T][C]
+  int32_t* err;
+};
+hipError_t launch_conv(const ConvArgs& a, sv_dtype io_dtype, hipStream_t stream);
+
 struct GdnFullPtrs {
   float* state;
   const void* q; const void* k; const void* v;

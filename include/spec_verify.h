@@ -168,6 +168,45 @@ SV_API sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode,
     const sv_gdn_pending* pending, int32_t* err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Short causal convolution of the linear-attention layers: verify and commit.
+ *
+ * The packed varlen operator keeps a rolling state of the last K-1 inputs
+ * per sequence and publishes the state after every token (onnxruntime-genai
+ * #2457, VarlenCausalConvWithState prefix states: slot j is the state after
+ * local token j).  Per channel c, with z = [state rows, x_0 .. x_{T_b-1}]
+ * (oldest first):
+ *   y_t[c] = act( sum_{i<K} weight[c][i] * z_{t+i}[c] + bias[c] )
+ * so weight[c][K-1] multiplies the newest input; act is the identity
+ * (SV_ACT_NONE) or SiLU (SV_ACT_SILU).  Commit keeps the last K-1 rows of
+ * [state, x_0 .. x_{c_b - 1}] -- the state a run over only the accepted
+ * prefix leaves (c_b = 0 keeps it).  Modes as for gdn_verify_commit.
+ *   state      [num_slots, K-1, C] io_dtype, oldest first, updated in place
+ *   state_slot int32 [B] or NULL (slot b)
+ *   x, out     [total_T, C] io_dtype (out unused by COMMIT_ONLY)
+ *   weight     fp32 [C, K];   bias fp32 [C] or NULL
+ *   commit_len int32 [B] (unused by VERIFY_ONLY)
+ *   pending    NULL, or the previous step's inputs and commit lengths
+ *              (deferred commit): the window first advances over the first
+ *              pending->commit_len[b] pending inputs and that state is
+ *              stored, then this call's tokens run from it.
+ * K in 2..8, C >= 1.  Stored states are copies of inputs (exact).
+ * ------------------------------------------------------------------------ */
+#define SV_ACT_NONE 0
+#define SV_ACT_SILU 1
+
+typedef struct {
+  sv_batch batch;              /* the pending step's batch (same B) */
+  const void* x;               /* [batch.total_T, C] io_dtype */
+  const int32_t* commit_len;   /* [B], 0..T_b of the pending step */
+} sv_conv_pending;
+
+SV_API sv_status short_conv_verify_commit(const sv_batch* batch, sv_gdn_mode mode,
+    void* state, const int32_t* state_slot, int32_t num_slots, const void* x,
+    const float* weight, const float* bias, sv_dtype io_dtype, int32_t activation,
+    const int32_t* commit_len, void* out, int32_t C, int32_t K,
+    const sv_conv_pending* pending, int32_t* err, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Acceptance.
  *
  * Greedy (onnxruntime-genai #2457, greedy MTP step and device argmax of the

@@ -99,6 +99,27 @@ def test_gdn_validation():
     assert call(state=20) == bd.SV_EINVAL                    # misaligned state
 
 
+def test_short_conv_validation():
+    L = bd.lib()
+    b = _batch()
+
+    def call(mode=0, state=16, x=16, w=16, K=4, C=64, act=0, commit=16, out=16, slots=2,
+             io=bd.SV_BF16):
+        return L.short_conv_verify_commit(ctypes.byref(b), mode, state, None, slots, x, w,
+                                          None, io, act, commit, out, C, K, None, None, None)
+    assert call(K=1) == bd.SV_EINVAL
+    assert call(K=9) == bd.SV_EINVAL
+    assert call(C=0) == bd.SV_EINVAL
+    assert call(act=2) == bd.SV_EINVAL
+    assert call(io=2) == bd.SV_EDTYPE
+    assert call(state=None) == bd.SV_EINVAL
+    assert call(w=None) == bd.SV_EINVAL
+    assert call(mode=0, commit=None) == bd.SV_EINVAL         # commit_len required
+    assert call(mode=1, out=None) == bd.SV_EINVAL            # out required
+    assert call(slots=1) == bd.SV_EINVAL                     # slots < B without a map
+    assert call(mode=7) == bd.SV_EINVAL
+
+
 def test_accept_validation():
     L = bd.lib()
     b = _batch()

@@ -1,0 +1,152 @@
+"""GPU parity of short_conv_verify_commit against the oracle (through the C ABI).
+
+Outputs: <= 2e-3 (fp32 I/O), <= 1e-2 + half a bf16 ulp of |y_ref| (bf16 I/O,
+the output is rounded once).  The committed state is a copy of inputs, so it
+must equal the oracle's bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from block_draft_verification_spec_amd import binding as bd
+from gpu_helpers import DEV, bits, check_gdn_out, err_word, np64, npi, say, sv_batch
+
+pytestmark = pytest.mark.gpu
+
+MODES = [bd.SV_GDN_VERIFY_COMMIT, bd.SV_GDN_VERIFY_ONLY, bd.SV_GDN_COMMIT_ONLY]
+
+
+def _run(batch, c, mode, commit, silu=False, slots=None, pending=None, state=None):
+    st = (c['state'] if state is None else state).clone()
+    out = torch.full_like(c['x'], float('nan'))
+    err = err_word()
+    bd.short_conv_verify_commit(sv_batch(batch), mode, st, c['x'], c['weight'], c['bias'],
+                                commit, out, state_slot=slots,
+                                activation=bd.SV_ACT_SILU if silu else bd.SV_ACT_NONE,
+                                pending=pending, err=err)
+    torch.cuda.synchronize()
+    return out, st, int(err.item())
+
+
+def _oracle(batch, c, mode, commit, silu=False, slots=None, state=None):
+    st = c['state'] if state is None else state
+    return oracle.conv_step(np64(st), None if slots is None else npi(slots), np64(c['x']),
+                            np64(c['weight']), None if c['bias'] is None else np64(c['bias']),
+                            npi(batch.cu_seqlens), None if commit is None else npi(commit),
+                            mode, silu=silu)
+
+
+def _expect_state(gpu_state, ref64):
+    ref = torch.from_numpy(ref64).to(gpu_state.dtype)
+    assert np.array_equal(bits(gpu_state), bits(ref))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("silu", [False, True])
+def test_tiny_fp32(mode, silu):
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 0, DEV)
+    c = wl.make_conv_layer(w, batch, 1, DEV)
+    commit = wl.make_commit_len(batch, 2, device=DEV)
+    cm = None if mode == bd.SV_GDN_VERIFY_ONLY else commit
+    say('conv tiny fp32 mode', mode, 'silu', silu)
+    out, st, err = _run(batch, c, mode, cm, silu)
+    assert err == 0
+    y, S = _oracle(batch, c, mode, cm, silu)
+    if mode != bd.SV_GDN_COMMIT_ONLY:
+        check_gdn_out(np64(out), y, torch.float32)
+    _expect_state(st, S)
+
+
+@pytest.mark.parametrize("wi,seed", [(3, 5), (4, 6)])
+def test_full_size_bf16(wi, seed):
+    """The GDN layers' short conv of the hybrid step (B = 64, C = 12288) and of
+    the ragged stress step (B = 256, k_b up to 7), with a slot map."""
+    w = wl.WORKLOADS[wi]
+    batch = wl.make_batch(w, seed, DEV)
+    ns = batch.B + 7
+    c = wl.make_conv_layer(w, batch, seed + 1, DEV, num_slots=ns)
+    slots = wl.make_state_slots(batch, ns, seed + 2, DEV)
+    commit = wl.make_commit_len(batch, seed + 3, device=DEV)
+    say('conv full size', w.name, 'C', w.conv_C)
+    out, st, err = _run(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit, silu=True, slots=slots)
+    assert err == 0
+    y, S = _oracle(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit, silu=True, slots=slots)
+    e = check_gdn_out(np64(out), y, torch.bfloat16)
+    _expect_state(st, S)
+    say(f'  max abs err {e:.2e}')
+
+
+@pytest.mark.parametrize("K", [2, 3, 8])
+def test_widths(K):
+    w = wl.Workload(**{**wl.WORKLOADS[0].__dict__, 'conv_K': K, 'B': 5, 'k': 7,
+                       'ragged_k': True, 'ctx_fixed': None, 'ctx': (10, 20)})
+    batch = wl.make_batch(w, 11, DEV)
+    c = wl.make_conv_layer(w, batch, 12, DEV, bias=False)
+    commit = wl.make_commit_len(batch, 13, device=DEV)
+    out, st, err = _run(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert err == 0
+    y, S = _oracle(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit)
+    check_gdn_out(np64(out), y, torch.float32)
+    _expect_state(st, S)
+
+
+def test_modes_agree_and_zero_commit_keeps_state():
+    w = wl.WORKLOADS[3]
+    batch = wl.make_batch(w, 21, DEV)
+    c = wl.make_conv_layer(w, batch, 22, DEV)
+    commit = wl.make_commit_len(batch, 23, device=DEV)
+    o_vc, s_vc, _ = _run(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit)
+    o_vo, s_vo, _ = _run(batch, c, bd.SV_GDN_VERIFY_ONLY, None)
+    _, s_co, _ = _run(batch, c, bd.SV_GDN_COMMIT_ONLY, commit)
+    assert torch.equal(o_vc, o_vo)
+    assert torch.equal(s_vc, s_co)
+    assert torch.equal(s_vo, c['state'])
+    zero = torch.zeros_like(commit)
+    _, s_0, _ = _run(batch, c, bd.SV_GDN_VERIFY_COMMIT, zero)
+    assert torch.equal(s_0, c['state'])
+
+
+def test_deferred_pending_equals_two_phase():
+    """Step 1 verifies, step 2 replays step 1's accepted inputs then verifies
+    its own: outputs and state equal committing step 1 first, bit for bit, and
+    the oracle run in two phases."""
+    w = wl.WORKLOADS[4]
+    batch = wl.make_batch(w, 31, DEV)
+    c1 = wl.make_conv_layer(w, batch, 32, DEV)
+    c2 = wl.make_conv_layer(w, batch, 33, DEV)
+    c2['state'] = c1['state']
+    commit1 = wl.make_commit_len(batch, 34, device=DEV)
+    commit2 = wl.make_commit_len(batch, 35, device=DEV)
+    # two-phase: commit step 1, then verify + commit step 2
+    _, s1, _ = _run(batch, c1, bd.SV_GDN_COMMIT_ONLY, commit1)
+    o2, s2, _ = _run(batch, c2, bd.SV_GDN_VERIFY_COMMIT, commit2, state=s1)
+    # deferred: step 2 with step 1 pending, verify only, then flush step 2
+    pend = bd.make_conv_pending(sv_batch(batch), c1['x'], commit1)
+    o2d, s1d, err = _run(batch, c2, bd.SV_GDN_VERIFY_ONLY, None, pending=pend)
+    assert err == 0
+    assert torch.equal(o2d, o2)
+    assert torch.equal(s1d, s1)
+    _, s2d, _ = _run(batch, c2, bd.SV_GDN_COMMIT_ONLY, commit2, state=s1d)
+    assert torch.equal(s2d, s2)
+    # and the oracle
+    _, S1 = _oracle(batch, c1, oracle.CONV_COMMIT_ONLY, commit1)
+    y2, S2 = oracle.conv_step(S1, None, np64(c2['x']), np64(c2['weight']), np64(c2['bias']),
+                              npi(batch.cu_seqlens), npi(commit2), oracle.CONV_VERIFY_COMMIT)
+    check_gdn_out(np64(o2d), y2, torch.bfloat16)
+    _expect_state(s2d, S2)
+
+
+def test_bad_commit_is_flagged_and_skipped():
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 41, DEV)
+    c = wl.make_conv_layer(w, batch, 42, DEV)
+    commit = torch.tensor([1, 9], dtype=torch.int32, device=DEV)   # 9 > T_1
+    out, st, err = _run(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert err & 8
+    rows = slice(int(batch.cu_seqlens[1]), int(batch.cu_seqlens[2]))
+    assert torch.isnan(out[rows]).all()
+    assert torch.equal(st[1], c['state'][1])
