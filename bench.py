@@ -64,6 +64,45 @@ def calibrate_copy():
     print(json.dumps({'calibrate_copy_bytes': n, 'copies': 3}), flush=True)
 
 
+def short_conv_timing(w, batch, sb, commit, stream, dev, reps=20):
+    """One short-convolution layer of the linear-attention layers (C = the q,
+    k and v features, K = 4, SiLU), deferred schedule: replay the previous
+    step's accepted inputs, verify this step's.  Four independent layers are
+    cycled so the timing is not an L2 replay."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    layers = [wl.make_conv_layer(w, batch, 3000 + i, dev) for i in range(4)]
+    for c in layers:
+        c['out'] = torch.empty_like(c['x'])
+        c['pend'] = bd.make_conv_pending(sb, c['x'], commit)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def run(c):
+        bd.short_conv_verify_commit(sb, bd.SV_GDN_VERIFY_ONLY, c['state'], c['x'], c['weight'],
+                                    c['bias'], None, c['out'], activation=bd.SV_ACT_SILU,
+                                    pending=c['pend'], stream=stream)
+    for c in layers:
+        run(c)
+    e0.record(stream)
+    for _ in range(reps):
+        for c in layers:
+            run(c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * len(layers))
+    s, C, K, T, B = 2, w.conv_C, w.conv_K, batch.total_T, batch.B
+    # state read + write, current inputs and outputs, the replayed (accepted)
+    # pending inputs, taps and bias
+    pend_rows = int(commit.sum().item())
+    nbytes = 2 * B * (K - 1) * C * s + 2 * T * C * s + pend_rows * C * s + C * K * 4 + C * 4
+    return {'layer_ms': round(ms, 4), 'bytes': nbytes,
+            'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1), 'C': C, 'K': K,
+            'schedule': 'deferred (pending replay + verify)'}
+
+
 def measured_traffic():
     """HBM bytes per attention launch (stream kernel + combine kernel) from the
     committed FETCH_SIZE / WRITE_SIZE counter runs, already scaled by the copy
@@ -328,6 +367,8 @@ def main():
     torch.cuda.synchronize()
     gdn_ms = g0.elapsed_time(g1) / max(1, len(gdn_l))
 
+    conv = short_conv_timing(w, batch, sb, commits[0], stream, dev)
+
     T = batch.total_T
     n_att, n_gdn = len(att_layers), len(gdn_l)
     draft_per_step = T - batch.B
@@ -362,6 +403,7 @@ def main():
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4)},
+        'next_rows': {'short_conv': conv},
         'mean_accept_len': round(accepted, 3),
         'dtype_detail': 'bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance',
     }
