@@ -56,8 +56,14 @@ def _layout(B, max_T):
     return np.zeros(B, dtype=np.int32), np.full((B, max_T), -1, dtype=np.int32)
 
 
-def greedy_accept(target_logits, draft_tokens, cu_seqlens, max_T):
-    """Greedy acceptance.  Returns ``(accept_len[B], out_tokens[B, max_T])``."""
+def greedy_accept(target_logits, draft_tokens, cu_seqlens, max_T, bonus_tokens=None):
+    """Greedy acceptance.  Returns ``(accept_len[B], out_tokens[B, max_T])``.
+
+    ``bonus_tokens`` (optional, one per sequence): when every draft is
+    accepted the emitted bonus token is the supplied one instead of the last
+    row's argmax (lmdeploy PR 3945, ``reject_sampler.py``: pre-sampled
+    ``bonus_token_ids``).
+    """
     target_logits = np.asarray(target_logits, dtype=np.float64)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     B = len(cu) - 1
@@ -71,14 +77,23 @@ def greedy_accept(target_logits, draft_tokens, cu_seqlens, max_T):
         while a < k and int(draft_tokens[d0 + a]) == g[a]:
             a += 1
         out[b, :a] = draft_tokens[d0:d0 + a]
-        out[b, a] = g[a]
+        out[b, a] = int(bonus_tokens[b]) if (bonus_tokens is not None and a == k) else g[a]
         accept_len[b] = a
     return accept_len, out
 
 
 def rejection_accept(target_logits, draft_logits, draft_tokens, u_accept,
-                     u_final, cu_seqlens, max_T, return_margins=False):
+                     u_final, cu_seqlens, max_T, return_margins=False,
+                     bonus_tokens=None):
     """Speculative (rejection) sampling acceptance.
+
+    ``draft_logits = None``: the draft distribution of each position is the
+    point mass on the draft token (lmdeploy PR 3945, ``reject_sampler.py``
+    with ``draft_probs = None``); Algorithm 1 then accepts iff ``u < p(x)``
+    and the residual is ``p`` with ``x`` removed.  ``bonus_tokens``
+    (optional): when every draft is accepted the supplied token is emitted
+    instead of a draw from the last target row (pre-sampled
+    ``bonus_token_ids`` of the same file).
 
     Returns ``(accept_len[B], out_tokens[B, max_T])`` and, with
     ``return_margins``, a list per sequence of the distances of each decision
@@ -87,9 +102,11 @@ def rejection_accept(target_logits, draft_logits, draft_tokens, u_accept,
     differs must sit inside float64 rounding of one of these).
     """
     target_logits = np.asarray(target_logits, dtype=np.float64)
-    draft_logits = np.asarray(draft_logits, dtype=np.float64)
+    if draft_logits is not None:
+        draft_logits = np.asarray(draft_logits, dtype=np.float64)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     B = len(cu) - 1
+    V = target_logits.shape[1]
     accept_len, out = _layout(B, max_T)
     margins = []
     for b in range(B):
@@ -100,8 +117,12 @@ def rejection_accept(target_logits, draft_logits, draft_tokens, u_accept,
         a, w = k, None
         for i in range(k):
             p = softmax64(target_logits[cu[b] + i])
-            q = softmax64(draft_logits[d0 + i])
             x = int(draft_tokens[d0 + i])
+            if draft_logits is None:
+                q = np.zeros(V)
+                q[x] = 1.0
+            else:
+                q = softmax64(draft_logits[d0 + i])
             lhs = float(np.float64(u_accept[d0 + i]) * q[x])
             m_b.append(abs(lhs - p[x]))
             if lhs < p[x]:
@@ -111,13 +132,17 @@ def rejection_accept(target_logits, draft_logits, draft_tokens, u_accept,
                 r = p          # p == q up to rounding: fall back to p
             a, w = i, r
             break
-        if w is None:
-            w = softmax64(target_logits[cu[b] + k])
-        y = icdf(w, u_final[b])
-        C = np.cumsum(w)
-        t = float(u_final[b]) * C[-1]
-        lo = C[y - 1] if y > 0 else 0.0
-        m_b.append(min(abs(t - lo), abs(C[y] - t)))
+        if w is None and bonus_tokens is not None:
+            y = int(bonus_tokens[b])
+            m_b.append(float('inf'))      # no draw: nothing to be near
+        else:
+            if w is None:
+                w = softmax64(target_logits[cu[b] + k])
+            y = icdf(w, u_final[b])
+            C = np.cumsum(w)
+            t = float(u_final[b]) * C[-1]
+            lo = C[y - 1] if y > 0 else 0.0
+            m_b.append(min(abs(t - lo), abs(C[y] - t)))
         margins.append(m_b)
         out[b, :a] = draft_tokens[d0:d0 + a]
         out[b, a] = y

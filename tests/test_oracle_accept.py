@@ -323,3 +323,101 @@ def test_rejection_monte_carlo(seed):
             alpha = np.minimum(p[i], q[i]).sum()
             se = np.sqrt(alpha * (1 - alpha) / sel.sum())
             assert abs(rate - alpha) < 4 * se
+
+
+# ------------------------------------------------ one-hot drafts, supplied bonus
+def _run_one_hot(target, x, u_acc, u_fin):
+    k = len(x)
+    acc, out = oracle.rejection_accept(target, None, np.array(x), np.array(u_acc),
+                                       np.array([u_fin]), [0, k + 1], k + 1)
+    return int(acc[0]), tuple(int(t) for t in out[0, :acc[0] + 1])
+
+
+@pytest.mark.parametrize("seed,V,k", [(5, 3, 1), (6, 4, 2), (7, 3, 2)])
+def test_one_hot_drafts_exact_enumeration(seed, V, k):
+    """Deterministic drafts (point-mass draft distributions): emitted token i,
+    given the chain reached i, is distributed as p_i exactly, and the chain
+    reaches i with probability prod_{j<i} p_j(x_j) -- Theorem 1 of Leviathan
+    et al. with q_i the point mass, measured exactly over the uniforms."""
+    rng = np.random.default_rng(seed)
+    target = 1.5 * rng.standard_normal((k + 1, V))
+    p = [special.softmax(target[i]) for i in range(k + 1)]
+    for x in itertools.product(range(V), repeat=k):
+        taus = []
+        for i in range(k):
+            def acc_at(u, i=i):
+                ua = [0.0] * k
+                ua[i] = u
+                return _run_one_hot(target, list(x), ua, 0.5)[0] > i
+            taus.append(_threshold(acc_at))
+        np.testing.assert_allclose(taus, [p[i][x[i]] for i in range(k)], rtol=0, atol=1e-12)
+        dist = defaultdict(float)
+        for a in range(k + 1):
+            pa = float(np.prod(taus[:a])) * ((1.0 - taus[a]) if a < k else 1.0)
+            if pa <= 0.0:
+                continue
+            ua = [t * 0.5 for t in taus[:a]] + \
+                 ([0.5 * (1.0 + taus[a])] if a < k else []) + [0.0] * (k - a - 1)
+            meas = _step_measure(lambda u: _run_one_hot(target, list(x), ua, u)[1])
+            for tokens, m in meas.items():
+                dist[tokens] += pa * m
+        reach = 1.0
+        for i in range(k + 1):
+            marg = np.zeros(V)
+            for tokens, m in dist.items():
+                if len(tokens) > i:
+                    marg[tokens[i]] += m
+            np.testing.assert_allclose(marg.sum(), reach, rtol=0, atol=1e-9)
+            np.testing.assert_allclose(marg / marg.sum(), p[i], rtol=0, atol=1e-9)
+            if i < k:
+                reach *= p[i][x[i]]
+
+
+def test_one_hot_equals_point_mass_draft_logits():
+    """draft_logits = None is the general path with draft rows that are
+    -inf everywhere but the draft token."""
+    rng = np.random.default_rng(8)
+    V, B = 7, 12
+    T = rng.integers(1, 5, B)
+    cu = np.concatenate([[0], np.cumsum(T)])
+    target = 2.0 * rng.standard_normal((cu[-1], V))
+    nd = cu[-1] - B
+    drafts = rng.integers(0, V, nd)
+    point = np.full((nd, V), NEG)
+    point[np.arange(nd), drafts] = 0.0
+    for trial in range(20):
+        ua, uf = rng.random(nd), rng.random(B)
+        a1, o1 = oracle.rejection_accept(target, None, drafts, ua, uf, cu, 5)
+        a2, o2 = oracle.rejection_accept(target, point, drafts, ua, uf, cu, 5)
+        np.testing.assert_array_equal(a1, a2)
+        np.testing.assert_array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("mode", ['greedy', 'rejection'])
+def test_supplied_bonus_replaces_only_the_bonus(mode):
+    rng = np.random.default_rng(9)
+    V, B, k = 9, 30, 2
+    cu = np.arange(B + 1) * (k + 1)
+    target = 2.0 * rng.standard_normal((cu[-1], V))
+    if mode == 'greedy':
+        g = target.argmax(axis=1)
+        drafts = np.array([g[cu[b] + i] if rng.random() < 0.8 else (g[cu[b] + i] + 1) % V
+                           for b in range(B) for i in range(k)])
+    else:
+        drafts = rng.integers(0, V, B * k)
+    draft = 2.0 * rng.standard_normal((B * k, V))
+    ua, uf = 0.5 * rng.random(B * k), rng.random(B)
+    bonus = rng.integers(0, V, B)
+    if mode == 'greedy':
+        a0, o0 = oracle.greedy_accept(target, drafts, cu, k + 1)
+        a1, o1 = oracle.greedy_accept(target, drafts, cu, k + 1, bonus_tokens=bonus)
+    else:
+        a0, o0 = oracle.rejection_accept(target, draft, drafts, ua, uf, cu, k + 1)
+        a1, o1 = oracle.rejection_accept(target, draft, drafts, ua, uf, cu, k + 1,
+                                         bonus_tokens=bonus)
+    np.testing.assert_array_equal(a0, a1)
+    full = a0 == k
+    assert full.any() and (~full).any()
+    np.testing.assert_array_equal(o1[full, k], bonus[full])
+    np.testing.assert_array_equal(o1[~full], o0[~full])
+    np.testing.assert_array_equal(o1[:, :k], o0[:, :k])
