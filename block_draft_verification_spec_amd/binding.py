@@ -67,7 +67,8 @@ class SvGdnConfig(ctypes.Structure):
 class SvAcceptArgs(ctypes.Structure):
     _fields_ = [('mode', ctypes.c_int), ('logit_dtype', ctypes.c_int),
                 ('V', _c_i32), ('target_logits', _vp), ('draft_logits', _vp),
-                ('draft_tokens', _vp), ('u_accept', _vp), ('u_final', _vp)]
+                ('draft_tokens', _vp), ('u_accept', _vp), ('u_final', _vp),
+                ('bonus_tokens', _vp)]
 
 
 class SvStepPending(ctypes.Structure):
@@ -93,6 +94,9 @@ _SIGS = {
          ctypes.c_int, _c_i32, _vp, _vp, _c_i32, _c_i32, ctypes.POINTER(SvConvPending),
          _vp, _vp], ctypes.c_int),
     'spec_accept_workspace_bytes': ([_c_i32, _c_i32, _c_i32, ctypes.c_int], _sz),
+    'spec_accept_args': (
+        [ctypes.POINTER(SvBatch), ctypes.POINTER(SvAcceptArgs), _vp, _vp, _vp, _vp, _sz, _vp,
+         _vp], ctypes.c_int),
     'spec_accept': (
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, ctypes.c_int, _c_i32,
          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
@@ -266,10 +270,20 @@ def spec_accept_workspace_bytes(B, total_T, V, mode):
 def spec_accept(batch, mode, target_logits, draft_tokens, result,
                 draft_logits=None, u_accept=None, u_final=None,
                 commit_len_out=None, ctx_lens_inout=None, workspace=None,
-                err=None, stream=None):
-    """Acceptance (``spec_accept``).  ``result`` int32 [B * (1 + max_T)]."""
+                err=None, stream=None, bonus_tokens=None):
+    """Acceptance.  ``result`` int32 [B * (1 + max_T)].  Rejection without
+    ``draft_logits`` treats each draft as a point mass; ``bonus_tokens``
+    (int32 [B]) goes through ``spec_accept_args``."""
     V = target_logits.shape[1]
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if bonus_tokens is not None:
+        acc = accept_args(mode, target_logits, draft_tokens, draft_logits, u_accept, u_final,
+                          bonus_tokens)
+        _check(lib().spec_accept_args(
+            ctypes.byref(batch), ctypes.byref(acc), _i32(result, 'result'),
+            _i32(commit_len_out, 'commit_len_out'), _i32(ctx_lens_inout, 'ctx_lens'),
+            _ptr(workspace), ws_n, _i32(err, 'err'), _stream(stream)))
+        return
     _check(lib().spec_accept(
         ctypes.byref(batch), int(mode), _ptr(target_logits), _ptr(draft_logits),
         _dtype(target_logits), V, _i32(draft_tokens, 'draft_tokens'),
@@ -316,11 +330,11 @@ def gdn_layer(state, q, k, v, alpha, beta, out):
 
 
 def accept_args(mode, target_logits, draft_tokens, draft_logits=None,
-                u_accept=None, u_final=None):
+                u_accept=None, u_final=None, bonus_tokens=None):
     return SvAcceptArgs(int(mode), _dtype(target_logits), target_logits.shape[1],
                         _ptr(target_logits), _ptr(draft_logits),
                         _i32(draft_tokens, 'draft_tokens'), _ptr(u_accept),
-                        _ptr(u_final))
+                        _ptr(u_final), _i32(bonus_tokens, 'bonus_tokens'))
 
 
 def spec_verify_step_workspace_bytes(batch, step_args):

@@ -9,7 +9,11 @@
 // zero), and after k passes from p_k, by inverse CDF in vocabulary order with
 // the supplied uniform: y = first index whose running sum exceeds u * total.
 // Output rows follow the lmdeploy reject sampler (pull request 3945, review of
-// reject_sampler.py): accepted drafts, then y, padded with -1.
+// reject_sampler.py): accepted drafts, then y, padded with -1.  As there,
+// the draft distribution may be absent (point mass on the draft token:
+// accept iff u < p(x), residual p without x) and the bonus token may be
+// supplied (used when every draft passes, in place of the last row's argmax
+// or draw).
 //
 // Kernels (all reductions that decide an integer run in fp64, so that the
 // decisions agree with an fp64 reference except on a set of uniforms of
@@ -170,6 +174,13 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
       break;
     }
   }
+  if (acc == T - 1 && a.bonus) {  // every draft accepted: the supplied bonus
+    y = a.bonus[b];
+    if (y < 0 || y >= a.V) {
+      if (lane == 0) flag_error(a.err, SV_DERR_TOKEN);
+      return;
+    }
+  }
   if (lane == 0) write_outputs(a, b, x0, acc, y);
 }
 
@@ -260,17 +271,31 @@ __global__ __launch_bounds__(64) void decide_reject(AcceptArgs a) {
   for (int i = 0; i + 1 < tn; ++i) {
     const int x = a.draft_tokens[d0 + i];
     const double2 nt = row_norm(stats, x0 + i, nc, lane);
-    const double2 nd = row_norm(stats, a.total_T + d0 + i, nc, lane);
     const double p = exp(static_cast<double>(ld<T>(a.target, static_cast<size_t>(x0 + i) * a.V + x)) - nt.x) / nt.y;
-    const double q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(d0 + i) * a.V + x)) - nd.x) / nd.y;
+    double q = 1.0;  // point-mass draft distribution when no draft logits are given
+    double2 nd = make_double2(0.0, 0.0);
+    if (a.draft) {
+      nd = row_norm(stats, a.total_T + d0 + i, nc, lane);
+      q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(d0 + i) * a.V + x)) - nd.x) / nd.y;
+    }
     const double u = static_cast<double>(a.u_accept[d0 + i]);
     if (!(u * q < p)) {
       if (lane == 0) {
-        dec[b] = make_int4(i, 1, x0 + i, d0 + i);   // kind 1: residual
+        // kind 1: residual max(0, p - q); kind 2: p without the draft token
+        dec[b] = a.draft ? make_int4(i, 1, x0 + i, d0 + i) : make_int4(i, 2, x0 + i, x);
         fin[b] = make_double4(nt.x, nt.y, nd.x, nd.y);
       }
       return;
     }
+  }
+  if (a.bonus) {  // every draft accepted: the supplied bonus, no draw
+    const int y = a.bonus[b];
+    if (lane == 0) {
+      if (y < 0 || y >= a.V) flag_error(a.err, SV_DERR_TOKEN);
+      else write_outputs(a, b, x0, tn - 1, y);
+      dec[b] = make_int4(-1, -1, -1, -1);
+    }
+    return;
   }
   const double2 nt = row_norm(stats, x0 + tn - 1, nc, lane);
   if (lane == 0) {
@@ -285,6 +310,7 @@ __device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int
                                               const double4& f, int y) {
   const double p = exp(static_cast<double>(ld<T>(a.target, static_cast<size_t>(rt) * a.V + y)) - f.x) / f.y;
   if (kind == 0) return p;
+  if (kind == 2) return y == rd ? 0.0 : p;  // point-mass draft at rd
   const double q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(rd) * a.V + y)) - f.z) / f.w;
   return fmax(p - q, 0.0);
 }
@@ -380,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   }
   __syncthreads();
   double total = total_s;
-  if (d.y == 1 && !(total > 0.0)) {
+  if (d.y != 0 && !(total > 0.0)) {
     // p == q up to rounding: the residual is empty, draw from p instead.
     d.y = 0;
     __syncthreads();
@@ -458,7 +484,7 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((row_argmax_partial<T>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
   } else {
-    const int rows = 2 * a.total_T - a.B;
+    const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
     hipLaunchKernelGGL((row_stats_partial<T>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(64), 0, stream, a);
     hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);

@@ -135,6 +135,51 @@ sv_status check_gdn_common(const sv_batch* batch, float* state, int32_t num_slot
   return SV_OK;
 }
 
+sv_status accept_impl(const sv_batch* batch, const sv_accept_args* acc, int32_t* result,
+                      int32_t* commit_len_out, int32_t* ctx_lens_inout, void* workspace,
+                      size_t workspace_bytes, int32_t* err, hipStream_t stream, const char* who) {
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  const sv_accept_mode mode = acc->mode;
+  if (mode != SV_ACCEPT_GREEDY && mode != SV_ACCEPT_REJECTION)
+    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
+  if (acc->logit_dtype != SV_F32 && acc->logit_dtype != SV_BF16)
+    return fail(SV_EDTYPE, "%s: unsupported logit dtype %d", who,
+                static_cast<int>(acc->logit_dtype));
+  const int32_t V = acc->V;
+  if (V < 1) return fail(SV_EINVAL, "%s: V must be >= 1", who);
+  if (!acc->target_logits || !result)
+    return fail(SV_EINVAL, "%s: target_logits and result are required", who);
+  if (batch->total_T > batch->B && !acc->draft_tokens)
+    return fail(SV_EINVAL, "%s: draft_tokens is required when there are drafts", who);
+  if (mode == SV_ACCEPT_REJECTION &&
+      (!acc->u_final || (batch->total_T > batch->B && !acc->u_accept)))
+    return fail(SV_EINVAL, "%s: rejection needs u_accept and u_final", who);
+  const size_t need = sv::accept_workspace_bytes(batch->B, batch->total_T, V, mode);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
+                workspace ? workspace_bytes : size_t(0));
+  sv::AcceptArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.mode = mode;
+  a.target = acc->target_logits;
+  a.draft = mode == SV_ACCEPT_REJECTION ? acc->draft_logits : nullptr;
+  a.V = V;
+  a.draft_tokens = acc->draft_tokens;
+  a.u_accept = acc->u_accept;
+  a.u_final = acc->u_final;
+  a.bonus = acc->bonus_tokens;
+  a.result = result;
+  a.commit_len_out = commit_len_out;
+  a.ctx_lens = ctx_lens_inout;
+  a.err = err;
+  a.ws = workspace;
+  return hip_status(sv::launch_accept(a, acc->logit_dtype, stream), who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,41 +350,26 @@ sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode, const void* ta
                       int32_t* result, int32_t* commit_len_out, int32_t* ctx_lens_inout,
                       void* workspace, size_t workspace_bytes, int32_t* err,
                       hipStream_t stream) {
-  const char* who = "spec_accept";
-  sv_status st = check_batch(batch, who);
-  if (st != SV_OK) return st;
-  if (mode != SV_ACCEPT_GREEDY && mode != SV_ACCEPT_REJECTION)
-    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
-  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
-    return fail(SV_EDTYPE, "%s: unsupported logit dtype %d", who, static_cast<int>(logit_dtype));
-  if (V < 1) return fail(SV_EINVAL, "%s: V must be >= 1", who);
-  if (!target_logits || !result) return fail(SV_EINVAL, "%s: target_logits and result are required", who);
-  if (batch->total_T > batch->B && !draft_tokens)
-    return fail(SV_EINVAL, "%s: draft_tokens is required when there are drafts", who);
-  if (mode == SV_ACCEPT_REJECTION && (!u_final || (batch->total_T > batch->B && (!draft_logits || !u_accept))))
-    return fail(SV_EINVAL, "%s: rejection needs draft_logits, u_accept and u_final", who);
-  const size_t need = sv::accept_workspace_bytes(batch->B, batch->total_T, V, mode);
-  if (!workspace || workspace_bytes < need)
-    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
-                workspace ? workspace_bytes : size_t(0));
-  sv::AcceptArgs a{};
-  a.B = batch->B;
-  a.total_T = batch->total_T;
-  a.max_T = batch->max_T;
-  a.cu = batch->cu_seqlens;
-  a.mode = mode;
-  a.target = target_logits;
-  a.draft = draft_logits;
-  a.V = V;
-  a.draft_tokens = draft_tokens;
-  a.u_accept = u_accept;
-  a.u_final = u_final;
-  a.result = result;
-  a.commit_len_out = commit_len_out;
-  a.ctx_lens = ctx_lens_inout;
-  a.err = err;
-  a.ws = workspace;
-  return hip_status(sv::launch_accept(a, logit_dtype, stream), who);
+  sv_accept_args acc{};
+  acc.mode = mode;
+  acc.logit_dtype = logit_dtype;
+  acc.V = V;
+  acc.target_logits = target_logits;
+  acc.draft_logits = draft_logits;
+  acc.draft_tokens = draft_tokens;
+  acc.u_accept = u_accept;
+  acc.u_final = u_final;
+  acc.bonus_tokens = nullptr;
+  return accept_impl(batch, &acc, result, commit_len_out, ctx_lens_inout, workspace,
+                     workspace_bytes, err, stream, "spec_accept");
+}
+
+sv_status spec_accept_args(const sv_batch* batch, const sv_accept_args* acc, int32_t* result,
+                           int32_t* commit_len_out, int32_t* ctx_lens_inout, void* workspace,
+                           size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  if (!acc) return fail(SV_EINVAL, "spec_accept_args: acc is null");
+  return accept_impl(batch, acc, result, commit_len_out, ctx_lens_inout, workspace,
+                     workspace_bytes, err, stream, "spec_accept_args");
 }
 
 size_t spec_verify_step_workspace_bytes(const sv_batch* batch, const sv_attn_config* acfg,
@@ -420,9 +450,8 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
     if (st != SV_OK) return st;
   }
   // 2. acceptance (ctx_lens is advanced by a+1 here, after every attention layer)
-  st = spec_accept(batch, acc->mode, acc->target_logits, acc->draft_logits, acc->logit_dtype,
-                   acc->V, acc->draft_tokens, acc->u_accept, acc->u_final, result, commit_len,
-                   ctx_lens, workspace, workspace_bytes, err, stream);
+  st = accept_impl(batch, acc, result, commit_len, ctx_lens, workspace, workspace_bytes, err,
+                   stream, who);
   if (st != SV_OK) return st;
   // 3. two-phase: commit the first a+1 tokens of every GDN layer
   if (schedule == SV_SCHEDULE_TWO_PHASE && n_gdn > 0) {

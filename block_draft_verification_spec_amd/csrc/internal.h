@@ -114,6 +114,7 @@ struct AcceptArgs {
   int V;
   const int32_t* draft_tokens;
   const float* u_accept; const float* u_final;
+  const int32_t* bonus;         // [B] supplied bonus tokens, or null
   int32_t* result;
   int32_t* commit_len_out;
   int32_t* ctx_lens;

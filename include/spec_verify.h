@@ -221,7 +221,11 @@ SV_API sv_status short_conv_verify_commit(const sv_batch* batch, sv_gdn_mode mod
  * (first y whose running sum exceeds u_final * total).
  *
  *   target_logits  [total_T, V] logit_dtype
- *   draft_logits   [total_T - B, V] logit_dtype (rejection; NULL for greedy)
+ *   draft_logits   [total_T - B, V] logit_dtype; unused by greedy.  NULL in
+ *                  rejection mode: each draft distribution is the point mass
+ *                  on its draft token (lmdeploy #3945 reject_sampler.py with
+ *                  draft_probs = None): x_i passes iff u_accept < p_i(x_i) and
+ *                  the residual is p_i without x_i
  *   draft_tokens   int32 [total_T - B]
  *   u_accept       fp32 [total_T - B], u_final fp32 [B] (rejection only)
  *   result         int32 [B * (1 + max_T)]: accept_len[B] followed by the
@@ -229,12 +233,31 @@ SV_API sv_status short_conv_verify_commit(const sv_batch* batch, sv_gdn_mode mod
  *                  reject_sampler.py layout), one buffer for one readback
  *   commit_len_out int32 [B] = accept_len + 1, or NULL
  *   ctx_lens_inout int32 [B] += accept_len + 1 (the KV commit), or NULL
+ *   bonus_tokens   (spec_accept_args only) int32 [B] or NULL: when every
+ *                  draft of sequence b passes, bonus_tokens[b] is emitted in
+ *                  place of the last row's argmax / draw (pre-sampled
+ *                  bonus_token_ids of the same file); an id outside 0..V-1
+ *                  flags SV_DERR_TOKEN and skips the sequence
  * Workspace: spec_accept_workspace_bytes().
  * ------------------------------------------------------------------------ */
 typedef enum { SV_ACCEPT_GREEDY = 0, SV_ACCEPT_REJECTION = 1 } sv_accept_mode;
 
 SV_API size_t spec_accept_workspace_bytes(int32_t B, int32_t total_T, int32_t V,
                                    sv_accept_mode mode);
+
+/* The acceptance inputs of spec_accept_args and spec_verify_step. */
+typedef struct {
+  sv_accept_mode mode;
+  sv_dtype logit_dtype;
+  int32_t V;
+  const void* target_logits; const void* draft_logits;
+  const int32_t* draft_tokens; const float* u_accept; const float* u_final;
+  const int32_t* bonus_tokens;   /* [B] or NULL */
+} sv_accept_args;
+
+SV_API sv_status spec_accept_args(const sv_batch* batch, const sv_accept_args* acc,
+    int32_t* result, int32_t* commit_len_out, int32_t* ctx_lens_inout,
+    void* workspace, size_t workspace_bytes, int32_t* err, hipStream_t stream);
 
 SV_API sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode,
     const void* target_logits, const void* draft_logits, sv_dtype logit_dtype,
@@ -286,13 +309,7 @@ typedef struct {
   sv_dtype io_dtype;
 } sv_gdn_config;
 
-typedef struct {
-  sv_accept_mode mode;
-  sv_dtype logit_dtype;
-  int32_t V;
-  const void* target_logits; const void* draft_logits;
-  const int32_t* draft_tokens; const float* u_accept; const float* u_final;
-} sv_accept_args;
+
 
 /* Pending tokens of every GDN layer for the deferred schedule (host struct;
  * `layers` is a host array of n_gdn entries whose k, v, alpha, beta point at

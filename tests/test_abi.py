@@ -129,13 +129,19 @@ def test_accept_validation():
         return L.spec_accept(ctypes.byref(b), mode, target, draft, dtype, V,
                              16 if dt is None else dt, ua, uf, res, None, None, ws,
                              wsn, None, None)
-    assert call(draft=None) == bd.SV_EINVAL
+    assert call(ua=None) == bd.SV_EINVAL                     # rejection needs u_accept
     assert call(uf=None) == bd.SV_EINVAL
     assert call(mode=0, draft=None, ua=None, uf=None, wsn=4) == bd.SV_EWORKSPACE
     assert call(res=None) == bd.SV_EINVAL
     assert call(V=0) == bd.SV_EINVAL
     assert call(dtype=9) == bd.SV_EDTYPE
     assert call(mode=4) == bd.SV_EINVAL
+    # the struct entry point validates the same way
+    acc = bd.SvAcceptArgs(1, bd.SV_BF16, 100, 16, None, 16, None, 16, None)
+    assert L.spec_accept_args(ctypes.byref(b), ctypes.byref(acc), 16, None, None, 16, 1 << 30,
+                              None, None) == bd.SV_EINVAL
+    assert L.spec_accept_args(ctypes.byref(b), None, 16, None, None, 16, 1 << 30,
+                              None, None) == bd.SV_EINVAL
 
 
 def test_step_validation():

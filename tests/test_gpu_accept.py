@@ -17,7 +17,7 @@ from gpu_helpers import DEV, err_word, np64, npi, say, sv_batch
 pytestmark = pytest.mark.gpu
 
 
-def _run(batch, a, mode, ctx=None):
+def _run(batch, a, mode, ctx=None, bonus=None):
     B, mT = batch.B, batch.max_T
     result = torch.full((B * (1 + mT),), -7, dtype=torch.int32, device=DEV)
     commit = torch.full((B,), -7, dtype=torch.int32, device=DEV)
@@ -28,26 +28,29 @@ def _run(batch, a, mode, ctx=None):
     bd.spec_accept(sv_batch(batch), mode, a['target_logits'], a['draft_tokens'], result,
                    draft_logits=a.get('draft_logits'), u_accept=a.get('u_accept'),
                    u_final=a.get('u_final'), commit_len_out=commit, ctx_lens_inout=ctx,
-                   workspace=ws, err=err)
+                   workspace=ws, err=err, bonus_tokens=bonus)
     torch.cuda.synchronize()
     r = npi(result)
     return r[:B], r[B:].reshape(B, mT), npi(commit), npi(ctx), int(err.item())
 
 
-def _oracle(batch, a, mode):
+def _oracle(batch, a, mode, bonus=None):
     cu = npi(batch.cu_seqlens)
+    bn = None if bonus is None else npi(bonus)
     if mode == bd.SV_ACCEPT_GREEDY:
         return oracle.greedy_accept(np64(a['target_logits']), npi(a['draft_tokens']), cu,
-                                    batch.max_T) + (None,)
-    return oracle.rejection_accept(np64(a['target_logits']), np64(a['draft_logits']),
+                                    batch.max_T, bonus_tokens=bn) + (None,)
+    dl = a.get('draft_logits')
+    return oracle.rejection_accept(np64(a['target_logits']), None if dl is None else np64(dl),
                                    npi(a['draft_tokens']), np64(a['u_accept']),
-                                   np64(a['u_final']), cu, batch.max_T, return_margins=True)
+                                   np64(a['u_final']), cu, batch.max_T, return_margins=True,
+                                   bonus_tokens=bn)
 
 
-def _check(batch, a, mode):
-    acc, out, commit, ctx, err = _run(batch, a, mode)
+def _check(batch, a, mode, bonus=None):
+    acc, out, commit, ctx, err = _run(batch, a, mode, bonus=bonus)
     assert err == 0
-    acc_r, out_r, margins = _oracle(batch, a, mode)
+    acc_r, out_r, margins = _oracle(batch, a, mode, bonus)
     if not (np.array_equal(acc, acc_r) and np.array_equal(out, out_r)):
         bad = np.nonzero((acc != acc_r) | (out != out_r).any(1))[0]
         msg = [f'seq {b}: gpu {acc[b]} {out[b].tolist()} oracle {acc_r[b]} {out_r[b].tolist()}'
@@ -152,3 +155,49 @@ def test_bad_draft_token_is_flagged():
     acc, out, commit, ctx, err = _run(batch, a, bd.SV_ACCEPT_REJECTION)
     assert err & 16
     assert commit[0] == -7 and ctx[0] == batch.ctx[0]       # sequence 0 skipped
+
+
+# ------------------------------------------------ point-mass drafts, supplied bonus
+@pytest.mark.parametrize("wi,seed", [(0, 3), (3, 4), (4, 5)])
+def test_rejection_point_mass_drafts(wi, seed):
+    """No draft logits: each draft is a point mass (accept iff u < p(x),
+    residual p without x).  Greedy-style drafts: the planted row maximum
+    passes almost surely, the others almost never."""
+    w = wl.WORKLOADS[wi]
+    batch = wl.make_batch(w, seed, DEV)
+    g = wl.make_accept(w, batch, seed + 1, 'greedy', DEV)
+    r = wl.make_accept(w, batch, seed + 2, 'rejection', DEV)
+    a = {'target_logits': g['target_logits'], 'draft_tokens': g['draft_tokens'],
+         'u_accept': r['u_accept'], 'u_final': r['u_final']}
+    say('point-mass drafts', w.name)
+    acc = _check(batch, a, bd.SV_ACCEPT_REJECTION)
+    say('  mean accepted', acc.mean())
+
+
+@pytest.mark.parametrize("mode", [bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION])
+@pytest.mark.parametrize("wi", [0, 3])
+def test_supplied_bonus_tokens(mode, wi):
+    w = wl.WORKLOADS[wi]
+    batch = wl.make_batch(w, 6, DEV)
+    a = wl.make_accept(w, batch, 7, 'greedy' if mode == 0 else 'rejection', DEV)
+    bonus = torch.randint(0, w.V, (batch.B,), generator=torch.Generator().manual_seed(8),
+                          dtype=torch.int32).to(DEV)
+    acc = _check(batch, a, mode, bonus)
+    if batch.B >= 32:
+        assert (acc == batch.max_T - 1).any()      # some rows take the bonus
+
+
+def test_bad_bonus_is_flagged_and_skipped():
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 9, DEV)
+    a = wl.make_accept(w, batch, 10, 'greedy', DEV)
+    # both sequences accept every draft: plant the drafts on the argmax
+    g = a['target_logits'].float().argmax(dim=1).to(torch.int32)
+    cu = npi(batch.cu_seqlens)
+    d = torch.cat([g[cu[b]:cu[b + 1] - 1] for b in range(batch.B)])
+    a = dict(a, draft_tokens=d.contiguous())
+    bonus = torch.tensor([3, w.V + 5], dtype=torch.int32, device=DEV)
+    acc, out, commit, ctx, err = _run(batch, a, bd.SV_ACCEPT_GREEDY, bonus=bonus)
+    assert err & 16
+    assert acc[0] == batch.max_T - 1 and out[0, batch.max_T - 1] == 3
+    assert acc[1] == -7 and commit[1] == -7                  # skipped, untouched
