@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, 'libspecverify.so')
 
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_ECAPACITY, SV_EWORKSPACE, SV_EHIP = range(6)
-SV_F32, SV_BF16 = 0, 1
+SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 SV_GDN_VERIFY_COMMIT, SV_GDN_VERIFY_ONLY, SV_GDN_COMMIT_ONLY = 0, 1, 2
 SV_ACCEPT_GREEDY, SV_ACCEPT_REJECTION = 0, 1
 SV_SCHEDULE_TWO_PHASE, SV_SCHEDULE_DEFERRED = 0, 1
@@ -61,7 +61,7 @@ class SvAttnConfig(ctypes.Structure):
 class SvGdnConfig(ctypes.Structure):
     _fields_ = [('H', _c_i32), ('dk', _c_i32), ('dv', _c_i32),
                 ('num_slots', _c_i32), ('state_slot', _vp),
-                ('io_dtype', ctypes.c_int)]
+                ('io_dtype', ctypes.c_int), ('state_dtype', ctypes.c_int)]
 
 
 class SvAcceptArgs(ctypes.Structure):
@@ -86,8 +86,8 @@ _SIGS = {
          _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int,
          ctypes.c_float, _c_i32, _vp, _sz, _vp, _vp], ctypes.c_int),
     'gdn_verify_commit': (
-        [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, _c_i32, _vp, _vp,
-         _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+        [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, ctypes.c_int, _vp, _c_i32, _vp,
+         _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
          ctypes.POINTER(SvGdnPending), _vp, _vp], ctypes.c_int),
     'short_conv_verify_commit': (
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, _c_i32, _vp, _vp, _vp,
@@ -215,15 +215,14 @@ def gdn_verify_commit(batch, mode, state, q, k, v, alpha, beta, commit_len,
                       stream=None):
     """GDN verify / commit (``gdn_verify_commit``).
 
-    state fp32 [num_slots, H, dv, dk]; q/k [total_T, H, dk]; v/out
+    state fp32 or fp16 [num_slots, H, dv, dk]; q/k [total_T, H, dk]; v/out
     [total_T, H, dv]; alpha/beta fp32 [total_T, H]; commit_len int32 [B].
     ``pending``: an ``SvGdnPending`` or None.
     """
     num_slots, H, dv, dk = state.shape
-    if state.dtype != torch.float32:
-        raise ValueError('state must be float32')
     _check(lib().gdn_verify_commit(
-        ctypes.byref(batch), int(mode), _ptr(state), _i32(state_slot, 'state_slot'),
+        ctypes.byref(batch), int(mode), _ptr(state), state_dtype(state),
+        _i32(state_slot, 'state_slot'),
         num_slots, _ptr(q), _ptr(k), _ptr(v), _dtype(k), _ptr(alpha), _ptr(beta),
         _i32(commit_len, 'commit_len'), _ptr(out), H, dk, dv,
         ctypes.byref(pending) if pending is not None else None,
@@ -315,8 +314,18 @@ def attn_config(Hq, Hkv, D, page_size, num_pages, block_table, dtype, scale=0.0)
                         _i32(block_table, 'block_table'), dtype, float(scale))
 
 
-def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None):
-    return SvGdnConfig(H, dk, dv, num_slots, _i32(state_slot, 'state_slot'), io_dtype)
+def state_dtype(state):
+    """The ``sv_dtype`` of a recurrent-state tensor (fp32 or fp16)."""
+    if state.dtype == torch.float32:
+        return SV_F32
+    if state.dtype == torch.float16:
+        return SV_F16
+    raise ValueError(f'state must be float32 or float16, not {state.dtype}')
+
+
+def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None, state_dtype=SV_F32):
+    return SvGdnConfig(H, dk, dv, num_slots, _i32(state_slot, 'state_slot'), io_dtype,
+                       state_dtype)
 
 
 def attn_layer(q, k_new, v_new, k_cache, v_cache, out):

@@ -118,11 +118,14 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
   return a;
 }
 
-sv_status check_gdn_common(const sv_batch* batch, float* state, int32_t num_slots,
-                           sv_dtype io_dtype, int32_t H, int32_t dk, int32_t dv, const char* who) {
+sv_status check_gdn_common(const sv_batch* batch, void* state, sv_dtype state_dtype,
+                           int32_t num_slots, sv_dtype io_dtype, int32_t H, int32_t dk,
+                           int32_t dv, const char* who) {
   sv_status st = check_batch(batch, who);
   if (st != SV_OK) return st;
   if (!state) return fail(SV_EINVAL, "%s: state is null", who);
+  if (state_dtype != SV_F32 && state_dtype != SV_F16)
+    return fail(SV_EDTYPE, "%s: unsupported state dtype %d", who, static_cast<int>(state_dtype));
   if (num_slots < 1) return fail(SV_EINVAL, "%s: num_slots must be >= 1", who);
   if (io_dtype != SV_F32 && io_dtype != SV_BF16)
     return fail(SV_EDTYPE, "%s: unsupported io dtype %d", who, static_cast<int>(io_dtype));
@@ -218,14 +221,16 @@ sv_status spec_verify_attention(const sv_batch* batch, const void* q, const void
   return hip_status(sv::launch_attention(a, dtype, stream), "spec_verify_attention");
 }
 
-sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, float* state,
-                            const int32_t* state_slot, int32_t num_slots, const void* q,
+sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state,
+                            sv_dtype state_dtype, const int32_t* state_slot, int32_t num_slots,
+                            const void* q,
                             const void* k, const void* v, sv_dtype io_dtype, const float* alpha,
                             const float* beta, const int32_t* commit_len, void* out, int32_t H,
                             int32_t dk, int32_t dv, const sv_gdn_pending* pending, int32_t* err,
                             hipStream_t stream) {
   const char* who = "gdn_verify_commit";
-  sv_status st = check_gdn_common(batch, state, num_slots, io_dtype, H, dk, dv, who);
+  sv_status st =
+      check_gdn_common(batch, state, state_dtype, num_slots, io_dtype, H, dk, dv, who);
   if (st != SV_OK) return st;
   if (mode != SV_GDN_VERIFY_COMMIT && mode != SV_GDN_VERIFY_ONLY && mode != SV_GDN_COMMIT_ONLY)
     return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
@@ -275,7 +280,7 @@ sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, float* stat
     p.palpha = pending->alpha;
     p.pbeta = pending->beta;
   }
-  return hip_status(sv::launch_gdn(s, p, io_dtype, stream), who);
+  return hip_status(sv::launch_gdn(s, p, io_dtype, state_dtype, stream), who);
 }
 
 sv_status short_conv_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state,
@@ -443,7 +448,8 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
         pp = &pg;
       }
       ++ig;
-      st = gdn_verify_commit(batch, SV_GDN_VERIFY_ONLY, G.state, gcfg->state_slot,
+      st = gdn_verify_commit(batch, SV_GDN_VERIFY_ONLY, G.state, gcfg->state_dtype,
+                             gcfg->state_slot,
                              gcfg->num_slots, G.q, G.k, G.v, gcfg->io_dtype, G.alpha, G.beta,
                              nullptr, G.out, gcfg->H, gcfg->dk, gcfg->dv, pp, err, stream);
     }
@@ -455,8 +461,8 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
   if (st != SV_OK) return st;
   // 3. two-phase: commit the first a+1 tokens of every GDN layer
   if (schedule == SV_SCHEDULE_TWO_PHASE && n_gdn > 0) {
-    sv_status cs = check_gdn_common(batch, gdn[0].state, gcfg->num_slots, gcfg->io_dtype, gcfg->H,
-                                    gcfg->dk, gcfg->dv, who);
+    sv_status cs = check_gdn_common(batch, gdn[0].state, gcfg->state_dtype, gcfg->num_slots,
+                                    gcfg->io_dtype, gcfg->H, gcfg->dk, gcfg->dv, who);
     if (cs != SV_OK) return cs;
     sv::GdnScalars s{};
     s.B = batch->B;
@@ -480,7 +486,8 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
           return fail(SV_EINVAL, "%s: GDN layer %d lacks state/k/v/alpha/beta", who, l0 + i);
         t.l[i] = sv::GdnCommitPtrs{G.state, G.k, G.v, G.alpha, G.beta};
       }
-      st = hip_status(sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, stream), who);
+      st = hip_status(
+          sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, gcfg->state_dtype, stream), who);
       if (st != SV_OK) return st;
     }
   }

@@ -47,6 +47,59 @@ constexpr int kMaxTok = 2 * kMaxT;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// The state is stored as fp32, or as fp16 (rounded to nearest even once per
+// store; all arithmetic stays in fp32).
+typedef _Float16 h16x4_t __attribute__((ext_vector_type(4)));
+
+template <typename ST>
+__device__ __forceinline__ float4 load_state4(const ST* p);
+template <>
+__device__ __forceinline__ float4 load_state4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load_state4<_Float16>(const _Float16* p) {
+  const h16x4_t v = *reinterpret_cast<const h16x4_t*>(p);
+  return make_float4(static_cast<float>(v.x), static_cast<float>(v.y),
+                     static_cast<float>(v.z), static_cast<float>(v.w));
+}
+
+// streaming store: this launch does not read the state again
+template <typename ST>
+__device__ __forceinline__ void store_state4(ST* p, float x, float y, float z, float w);
+template <>
+__device__ __forceinline__ void store_state4<float>(float* p, float x, float y, float z,
+                                                    float w) {
+  const f32x4_t t = {x, y, z, w};
+  __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+// fp32 -> fp16 of a value already rounded to fp32.  The empty asm pins x in
+// a register: otherwise a product feeding the conversion may be contracted
+// into one mixed-precision multiply-add that rounds only once (to fp16), and
+// the replayed and the stored state would then differ in the last bit.
+__device__ __forceinline__ _Float16 to_f16(float x) {
+  asm volatile("" : "+v"(x));
+  return static_cast<_Float16>(x);
+}
+template <>
+__device__ __forceinline__ void store_state4<_Float16>(_Float16* p, float x, float y, float z,
+                                                       float w) {
+  const h16x4_t t = {to_f16(x), to_f16(y), to_f16(z), to_f16(w)};
+  __builtin_nontemporal_store(t, reinterpret_cast<h16x4_t*>(p));
+}
+
+// the value a store and a fresh load would give back
+template <typename ST>
+__device__ __forceinline__ float as_stored(float x);
+template <>
+__device__ __forceinline__ float as_stored<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ float as_stored<_Float16>(float x) {
+  return static_cast<float>(to_f16(x));
+}
+
 // acc + a . b as a chain of fused multiply-adds
 __device__ __forceinline__ float fma4(const float4& a, const float4& b, float acc) {
   acc = fmaf(a.x, b.x, acc);
@@ -78,9 +131,9 @@ struct GdnSmem {
 // COMMIT_ONLY_NP: compile-time COMMIT_ONLY without pending tokens (the
 // batched commit of the two-phase step); q, out and the pending pointers are
 // then never touched.
-template <typename IO, int DK, bool COMMIT_ONLY_NP>
+template <typename IO, typename ST, int DK, bool COMMIT_ONLY_NP>
 __device__ __forceinline__ void gdn_tile(
-    GdnSmem<DK>& sm, const GdnScalars& s, float* __restrict__ state, const void* q,
+    GdnSmem<DK>& sm, const GdnScalars& s, void* __restrict__ state, const void* q,
     const void* k, const void* v, const float* __restrict__ alpha,
     const float* __restrict__ beta, void* out, const void* pk, const void* pv,
     const float* __restrict__ palpha, const float* __restrict__ pbeta, int b,
@@ -143,16 +196,15 @@ __device__ __forceinline__ void gdn_tile(
   const int cl = tid & (kLanesPerRow - 1);
   const int rg = tid / kLanesPerRow;
   constexpr int kRowStride = kThreads / kLanesPerRow;  // rows rg + kRowStride r
-  float* tile = state + (static_cast<size_t>(slot) * H + h) * DV * DK;
+  ST* tile = static_cast<ST*>(state) + (static_cast<size_t>(slot) * H + h) * DV * DK;
 
   // ---- issue the state loads first: they are the long-latency traffic
   float4 sr[kRowsPerThread][NV4];
 #pragma unroll
   for (int r = 0; r < kRowsPerThread; ++r) {
-    const float* rowp = tile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
+    const ST* rowp = tile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
 #pragma unroll
-    for (int j = 0; j < NV4; ++j)
-      sr[r][j] = *reinterpret_cast<const float4*>(rowp + 32 * j + 4 * cl);
+    for (int j = 0; j < NV4; ++j) sr[r][j] = load_state4<ST>(rowp + 32 * j + 4 * cl);
   }
 
   // ---- stage token inputs as fp32
@@ -266,28 +318,28 @@ __device__ __forceinline__ void gdn_tile(
       }
     }
     g = g_new;
-    if (i == pc - 1) {  // end of the replayed tokens: fold the scale
+    if (i == pc - 1) {  // end of the replayed tokens: fold the scale (and the
+                        // storage rounding, so the current tokens run from
+                        // exactly the committed state)
 #pragma unroll
       for (int r = 0; r < kRowsPerThread; ++r)
 #pragma unroll
         for (int j = 0; j < NV4; ++j) {
-          sr[r][j].x *= g;
-          sr[r][j].y *= g;
-          sr[r][j].z *= g;
-          sr[r][j].w *= g;
+          sr[r][j].x = as_stored<ST>(sr[r][j].x * g);
+          sr[r][j].y = as_stored<ST>(sr[r][j].y * g);
+          sr[r][j].z = as_stored<ST>(sr[r][j].z * g);
+          sr[r][j].w = as_stored<ST>(sr[r][j].w * g);
         }
       g = 1.f;
     }
     if (i == store_at) {
 #pragma unroll
       for (int r = 0; r < kRowsPerThread; ++r) {
-        float* rowp = tile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
+        ST* rowp = tile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
 #pragma unroll
-        for (int j = 0; j < NV4; ++j) {
-          // streaming store: this launch does not read the state again
-          const f32x4_t t = {g * sr[r][j].x, g * sr[r][j].y, g * sr[r][j].z, g * sr[r][j].w};
-          __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(rowp + 32 * j + 4 * cl));
-        }
+        for (int j = 0; j < NV4; ++j)
+          store_state4<ST>(rowp + 32 * j + 4 * cl, g * sr[r][j].x, g * sr[r][j].y,
+                           g * sr[r][j].z, g * sr[r][j].w);
       }
     }
   }
@@ -301,15 +353,15 @@ __device__ __forceinline__ void gdn_tile(
   }
 }
 
-template <typename IO, int DK>
+template <typename IO, typename ST, int DK>
 __global__ __launch_bounds__(kThreads) void gdn_kernel(GdnScalars s, GdnFullPtrs p) {
   __shared__ GdnSmem<DK> sm;
   const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  gdn_tile<IO, DK, false>(sm, s, p.state, p.q, p.k, p.v, p.alpha, p.beta, p.out, p.pk,
+  gdn_tile<IO, ST, DK, false>(sm, s, p.state, p.q, p.k, p.v, p.alpha, p.beta, p.out, p.pk,
                    p.pv, p.palpha, p.pbeta, b, h, rb, rb == 0 && h == 0);
 }
 
-template <typename IO, int DK>
+template <typename IO, typename ST, int DK>
 __global__ __launch_bounds__(kThreads) void gdn_commit_multi_kernel(GdnScalars s,
                                                                     GdnCommitTable t) {
   const int rb = blockIdx.x, h = blockIdx.y;
@@ -317,37 +369,57 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_multi_kernel(GdnScalars s
   const int layer = blockIdx.z / s.B;
   const GdnCommitPtrs& p = t.l[layer];
   __shared__ GdnSmem<DK> sm;
-  gdn_tile<IO, DK, true>(sm, s, p.state, p.k, p.k, p.v, p.alpha, p.beta, p.state,
+  gdn_tile<IO, ST, DK, true>(sm, s, p.state, p.k, p.k, p.v, p.alpha, p.beta, p.state,
                          p.k, p.v, p.alpha, p.beta, b, h, rb,
                    rb == 0 && h == 0 && layer == 0);
+}
+
+template <typename IO, typename ST>
+void launch_gdn_t(const GdnScalars& s, const GdnFullPtrs& p, hipStream_t stream) {
+  const dim3 grid(s.dv / kRowsPerBlock, s.H, s.B);
+  if (s.dk == 128)
+    hipLaunchKernelGGL((gdn_kernel<IO, ST, 128>), grid, dim3(kThreads), 0, stream, s, p);
+  else
+    hipLaunchKernelGGL((gdn_kernel<IO, ST, 64>), grid, dim3(kThreads), 0, stream, s, p);
+}
+
+template <typename IO, typename ST>
+void launch_commit_t(const GdnScalars& s, const GdnCommitTable& t, int n_layers,
+                     hipStream_t stream) {
+  const dim3 grid(s.dv / kRowsPerBlock, s.H, s.B * n_layers);
+  if (s.dk == 128)
+    hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128>), grid, dim3(kThreads), 0, stream,
+                       s, t);
+  else
+    hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 64>), grid, dim3(kThreads), 0, stream,
+                       s, t);
 }
 
 }  // namespace
 
 hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io_dt,
-                      hipStream_t stream) {
-  dim3 grid(s.dv / kRowsPerBlock, s.H, s.B);
-  dim3 block(kThreads);
+                      sv_dtype state_dt, hipStream_t stream) {
+  const bool h = state_dt == SV_F16;
   if (io_dt == SV_BF16) {
-    if (s.dk == 128) hipLaunchKernelGGL((gdn_kernel<bf16_t, 128>), grid, block, 0, stream, s, p);
-    else hipLaunchKernelGGL((gdn_kernel<bf16_t, 64>), grid, block, 0, stream, s, p);
+    if (h) launch_gdn_t<bf16_t, _Float16>(s, p, stream);
+    else launch_gdn_t<bf16_t, float>(s, p, stream);
   } else {
-    if (s.dk == 128) hipLaunchKernelGGL((gdn_kernel<float, 128>), grid, block, 0, stream, s, p);
-    else hipLaunchKernelGGL((gdn_kernel<float, 64>), grid, block, 0, stream, s, p);
+    if (h) launch_gdn_t<float, _Float16>(s, p, stream);
+    else launch_gdn_t<float, float>(s, p, stream);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
-                                   int n_layers, sv_dtype io_dt, hipStream_t stream) {
-  dim3 grid(s.dv / kRowsPerBlock, s.H, s.B * n_layers);
-  dim3 block(kThreads);
+                                   int n_layers, sv_dtype io_dt, sv_dtype state_dt,
+                                   hipStream_t stream) {
+  const bool h = state_dt == SV_F16;
   if (io_dt == SV_BF16) {
-    if (s.dk == 128) hipLaunchKernelGGL((gdn_commit_multi_kernel<bf16_t, 128>), grid, block, 0, stream, s, t);
-    else hipLaunchKernelGGL((gdn_commit_multi_kernel<bf16_t, 64>), grid, block, 0, stream, s, t);
+    if (h) launch_commit_t<bf16_t, _Float16>(s, t, n_layers, stream);
+    else launch_commit_t<bf16_t, float>(s, t, n_layers, stream);
   } else {
-    if (s.dk == 128) hipLaunchKernelGGL((gdn_commit_multi_kernel<float, 128>), grid, block, 0, stream, s, t);
-    else hipLaunchKernelGGL((gdn_commit_multi_kernel<float, 64>), grid, block, 0, stream, s, t);
+    if (h) launch_commit_t<float, _Float16>(s, t, n_layers, stream);
+    else launch_commit_t<float, float>(s, t, n_layers, stream);
   }
   return hipGetLastError();
 }

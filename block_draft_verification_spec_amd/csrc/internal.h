@@ -51,7 +51,7 @@ struct ConvArgs {
 hipError_t launch_conv(const ConvArgs& a, sv_dtype io_dtype, hipStream_t stream);
 
 struct GdnFullPtrs {
-  float* state;
+  void* state;                  // fp32 or fp16 [num_slots][H][dv][dk]
   const void* q; const void* k; const void* v;
   const float* alpha; const float* beta;
   void* out;
@@ -59,7 +59,7 @@ struct GdnFullPtrs {
 };
 
 struct GdnCommitPtrs {
-  float* state;
+  void* state;
   const void* k; const void* v;
   const float* alpha; const float* beta;
 };
@@ -69,10 +69,11 @@ struct GdnCommitTable {
 };
 
 hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io,
-                      hipStream_t stream);
+                      sv_dtype state_dtype, hipStream_t stream);
 // COMMIT_ONLY over n_layers (<= kGdnLayersPerLaunch) layers in one launch.
 hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
-                                   int n_layers, sv_dtype io, hipStream_t stream);
+                                   int n_layers, sv_dtype io, sv_dtype state_dtype,
+                                   hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

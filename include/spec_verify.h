@@ -57,7 +57,7 @@ typedef enum {
   SV_EHIP = 5         /* the HIP runtime refused a launch */
 } sv_status;
 
-typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 /* GDN state only */ } sv_dtype;
 
 /* Device error bits (see `err` above). */
 #define SV_DERR_PAGE      1   /* block_table entry outside [0, num_pages) */
@@ -132,7 +132,11 @@ SV_API sv_status spec_verify_attention(const sv_batch* batch,
  *   mode SV_GDN_VERIFY_COMMIT  o for all T_b tokens; state stored at c_b
  *        SV_GDN_VERIFY_ONLY    o for all T_b tokens; commit_len unused
  *        SV_GDN_COMMIT_ONLY    first c_b tokens applied and stored; q, out unused
- *   state       fp32 [num_slots, H, dv, dk], updated in place
+ *   state       [num_slots, H, dv, dk], updated in place, state_dtype SV_F32
+ *               or SV_F16 (lmdeploy #5019 "Two fixes" item 2: the commit
+ *               kernel takes a half-precision state and computes in float);
+ *               all arithmetic is fp32, an fp16 state is rounded to nearest
+ *               even once per store
  *   state_slot  int32 [B] (slot of sequence b) or NULL (slot b)
  *   q, k        [total_T, H, dk]  io_dtype;   v [total_T, H, dv] io_dtype
  *   alpha, beta fp32 [total_T, H]
@@ -161,7 +165,7 @@ typedef struct {
 } sv_gdn_pending;
 
 SV_API sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode,
-    float* state, const int32_t* state_slot, int32_t num_slots,
+    void* state, sv_dtype state_dtype, const int32_t* state_slot, int32_t num_slots,
     const void* q, const void* k, const void* v, sv_dtype io_dtype,
     const float* alpha, const float* beta, const int32_t* commit_len,
     void* out, int32_t H, int32_t dk, int32_t dv,
@@ -292,7 +296,7 @@ typedef struct {
 } sv_attn_layer;
 
 typedef struct {
-  float* state; const void* q; const void* k; const void* v;
+  void* state; const void* q; const void* k; const void* v;
   const float* alpha; const float* beta; void* out;
 } sv_gdn_layer;
 
@@ -307,6 +311,7 @@ typedef struct {
   int32_t H, dk, dv, num_slots;
   const int32_t* state_slot;   /* [B] or NULL */
   sv_dtype io_dtype;
+  sv_dtype state_dtype;        /* SV_F32 or SV_F16 */
 } sv_gdn_config;
 
 

@@ -14,6 +14,9 @@ DEV = 'cuda'
 # (b, h) tile; GDN outputs 2e-3 (fp32) / 1e-2 + half a bf16 ulp of |o_ref|.
 ATT_TOL = {torch.float32: 2e-3, torch.bfloat16: 1e-2}
 GDN_STATE_TOL = 1e-4
+# an fp16 state adds one rounding to nearest per stored element (unit
+# roundoff 2^-11 relative) on top of the fp32 arithmetic
+GDN_STATE_TOL_F16 = 2.0 ** -11 * (1 + GDN_STATE_TOL) + GDN_STATE_TOL
 GDN_OUT_TOL = {torch.float32: 2e-3, torch.bfloat16: 1e-2}
 
 
@@ -59,8 +62,8 @@ def bf16_half_ulp(x):
     return np.ldexp(1.0, (e - 8).astype(int))
 
 
-def check_gdn_state(S_gpu, S_ref, tiles=None):
-    """Per (slot, h) tile: max|dS| / max|S_ref| <= GDN_STATE_TOL."""
+def check_gdn_state(S_gpu, S_ref, tiles=None, tol=GDN_STATE_TOL):
+    """Per (slot, h) tile: max|dS| / max|S_ref| <= tol."""
     S_gpu = np.asarray(S_gpu, dtype=np.float64)
     worst = 0.0
     ns, H = S_ref.shape[:2]
@@ -69,7 +72,7 @@ def check_gdn_state(S_gpu, S_ref, tiles=None):
             ref = S_ref[s, h]
             den = max(np.abs(ref).max(), 1e-30)
             worst = max(worst, np.abs(S_gpu[s, h] - ref).max() / den)
-    assert worst <= GDN_STATE_TOL, f'GDN state normwise error {worst:.3e}'
+    assert worst <= tol, f'GDN state normwise error {worst:.3e}'
     return worst
 
 

@@ -84,8 +84,8 @@ def test_gdn_validation():
     b = _batch()
 
     def call(mode=0, state=16, dk=128, dv=128, q=16, out=16, commit=16, slots=2,
-             io=bd.SV_BF16):
-        return L.gdn_verify_commit(ctypes.byref(b), mode, state, None, slots, q,
+             io=bd.SV_BF16, sdt=bd.SV_F32):
+        return L.gdn_verify_commit(ctypes.byref(b), mode, state, sdt, None, slots, q,
                                    16, 16, io, 16, 16, commit, out, 4, dk, dv,
                                    None, None, None)
     assert call(dk=96) == bd.SV_EDTYPE
@@ -96,6 +96,9 @@ def test_gdn_validation():
     assert call(mode=5) == bd.SV_EINVAL
     assert call(slots=1) == bd.SV_EINVAL                     # identity map needs B slots
     assert call(io=3) == bd.SV_EDTYPE
+    assert call(io=bd.SV_F16) == bd.SV_EDTYPE                # fp16 is a state type only
+    assert call(sdt=bd.SV_BF16) == bd.SV_EDTYPE
+    assert 'state dtype' in L.sv_last_error().decode()
     assert call(state=20) == bd.SV_EINVAL                    # misaligned state
 
 

@@ -1,6 +1,7 @@
 """GPU parity of gdn_verify_commit against the oracle (through the C ABI).
 
-Tolerances: committed state max|dS| / max|S_ref| <= 1e-4 per (b, h) tile;
+Tolerances: committed state max|dS| / max|S_ref| <= 1e-4 per (b, h) tile
+(fp16 state storage: plus one fp16 rounding, 2^-11 relative);
 outputs max-abs <= 2e-3 (fp32 I/O) or <= 1e-2 + half a bf16 ulp of |o_ref|
 (bf16 I/O).  Self-consistency checks on the GPU are bit-exact.
 """
@@ -12,8 +13,8 @@ import torch
 import oracle
 import workloads as wl
 from block_draft_verification_spec_amd import binding as bd
-from gpu_helpers import (DEV, check_gdn_out, check_gdn_state, err_word, np64, npi,
-                         say, sv_batch)
+from gpu_helpers import (DEV, GDN_STATE_TOL_F16, check_gdn_out, check_gdn_state, err_word,
+                         np64, npi, say, sv_batch)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +177,103 @@ def test_bad_commit_length_is_flagged_and_skipped():
                                np64(g['v'][:4]), np64(g['alpha'][:4]), np64(g['beta'][:4]),
                                np.array([0, 4]), np.array([2]), oracle.GDN_VERIFY_COMMIT)
     check_gdn_state(np64(st[:1]), S_ref)
+
+
+# ---- fp16 state storage: fp32 arithmetic, one rounding per stored element
+
+@pytest.mark.parametrize("mode", MODES)
+def test_f16_state_tiny_all_modes(mode):
+    w = wl.WORKLOADS[0]
+    batch = wl.make_batch(w, 0, DEV)
+    g = wl.make_gdn_layer(w, batch, 1, DEV, state_dtype=torch.float16)
+    commit = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
+    say('tiny fp16-state GDN mode', mode)
+    out, st, err = _run(batch, g, mode, commit)
+    assert err == 0 and st.dtype == torch.float16
+    o_ref, S_ref = _oracle(batch, g, mode, None if mode == bd.SV_GDN_VERIFY_ONLY else commit)
+    check_gdn_state(np64(st), S_ref, tol=GDN_STATE_TOL_F16)
+    if mode != bd.SV_GDN_COMMIT_ONLY:
+        check_gdn_out(np64(out), o_ref, torch.float32)
+    if mode == bd.SV_GDN_VERIFY_ONLY:
+        assert torch.equal(st, g['state'])
+
+
+def test_f16_state_full_size_bf16():
+    """The hybrid step's GDN layer (B = 64, H = 32, dk = dv = 128) with an fp16
+    state bank: the state within one fp16 rounding of the oracle, the outputs
+    bit-identical to those of an fp32 state holding the same values (they read
+    the working state, never a rounded one), and the stored state exactly the
+    fp16 rounding of what the fp32 path stores."""
+    w = wl.WORKLOADS[2]
+    batch = wl.make_batch(w, 40, DEV)
+    g = wl.make_gdn_layer(w, batch, 41, DEV, state_dtype=torch.float16)
+    commit = wl.make_commit_len(batch, 42, device=DEV)
+    say('GDN full-size fp16 state')
+    out, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert err == 0
+    o_ref, S_ref = _oracle(batch, g, oracle.GDN_VERIFY_COMMIT, commit)
+    e_s = check_gdn_state(np64(st), S_ref, tol=GDN_STATE_TOL_F16)
+    e_o = check_gdn_out(np64(out), o_ref, torch.bfloat16)
+    say(f'  state err {e_s:.2e}  out err {e_o:.2e}')
+    # the same inputs with the state widened to fp32 first
+    g32 = dict(g, state=g['state'].float())
+    out32, st32, _ = _run(batch, g32, bd.SV_GDN_VERIFY_COMMIT, commit)
+    assert torch.equal(out32, out)
+    assert torch.equal(st, st32.half())
+    # modes agree bit for bit
+    _, st2, _ = _run(batch, g, bd.SV_GDN_COMMIT_ONLY, commit)
+    assert torch.equal(st2, st)
+    out3, st3, _ = _run(batch, g, bd.SV_GDN_VERIFY_ONLY, None)
+    assert torch.equal(st3, g['state']) and torch.equal(out3, out)
+
+
+def test_f16_state_ragged_slots_dk64():
+    w = wl.Workload('gdn_ragged', B=9, k=7, ragged_k=True, ctx=(0, 0), H=3,
+                    dk=64, dv=192, gdn_dtype=torch.bfloat16)
+    batch = wl.make_batch(w, 50, DEV)
+    g = wl.make_gdn_layer(w, batch, 51, DEV, num_slots=13, state_dtype=torch.float16)
+    slots = wl.make_state_slots(batch, 13, 52, DEV)
+    T = torch.tensor(batch.T)
+    commit = (torch.arange(batch.B) % (T + 1)).to(torch.int32).to(DEV)
+    out, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit, slots=slots)
+    assert err == 0
+    o_ref, S_ref = _oracle(batch, g, oracle.GDN_VERIFY_COMMIT, commit, slots)
+    check_gdn_state(np64(st), S_ref, tol=GDN_STATE_TOL_F16)
+    check_gdn_out(np64(out), o_ref, torch.bfloat16)
+    used = set(npi(slots).tolist())
+    for s in range(13):
+        if s not in used:
+            assert torch.equal(st[s], g['state'][s])
+
+
+def test_f16_state_deferred_equals_two_phase():
+    """The pending replay folds the storage rounding into its working state, so
+    the current tokens run from exactly the fp16 state the two-phase schedule
+    stores: outputs and states agree bit for bit."""
+    w = wl.WORKLOADS[2]
+    w = wl.Workload(**{**w.__dict__, 'B': 12, 'H': 4})
+    prev = wl.make_batch(w, 60, DEV)
+    gp = wl.make_gdn_layer(w, prev, 61, DEV, state_dtype=torch.float16)
+    pcommit = wl.make_commit_len(prev, 62, device=DEV)
+    cur = wl.make_batch(wl.Workload(**{**w.__dict__, 'k': 5, 'ragged_k': True}), 63, DEV)
+    gc = wl.make_gdn_layer(w, cur, 64, DEV, state_dtype=torch.float16)
+    gc['state'] = gp['state']
+    ccommit = wl.make_commit_len(cur, 65, device=DEV)
+    # two-phase: commit the previous step, then verify + commit the current one
+    _, s_mid, _ = _run(prev, gp, bd.SV_GDN_COMMIT_ONLY, pcommit)
+    o_two, s_two, _ = _run(cur, gc, bd.SV_GDN_VERIFY_COMMIT, ccommit, state=s_mid)
+    # deferred: replay the previous step's accepted tokens inside the verify
+    pend = bd.make_gdn_pending(sv_batch(prev), gp['k'], gp['v'], gp['alpha'],
+                               gp['beta'], pcommit)
+    o_def, s_def_mid, err = _run(cur, gc, bd.SV_GDN_VERIFY_ONLY, None, pending=pend)
+    assert err == 0
+    assert torch.equal(o_def, o_two)
+    assert torch.equal(s_def_mid, s_mid)
+    _, s_def, _ = _run(cur, gc, bd.SV_GDN_COMMIT_ONLY, ccommit, state=s_def_mid)
+    assert torch.equal(s_def, s_two)
+    # against the oracle, from the stored (rounded) intermediate state
+    o_ref, S_ref = oracle.gdn_step(np64(s_mid), None, np64(gc['q']), np64(gc['k']),
+                                   np64(gc['v']), np64(gc['alpha']), np64(gc['beta']),
+                                   npi(cur.cu_seqlens), npi(ccommit), oracle.GDN_VERIFY_COMMIT)
+    check_gdn_out(np64(o_def), o_ref, torch.bfloat16)
+    check_gdn_state(np64(s_def), S_ref, tol=GDN_STATE_TOL_F16)

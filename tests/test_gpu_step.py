@@ -12,20 +12,20 @@ import torch
 import oracle
 import workloads as wl
 from block_draft_verification_spec_amd import binding as bd
-from gpu_helpers import (DEV, bits, check_attn_out, check_gdn_out, check_gdn_state,
-                         err_word, np64, npi, say, sv_batch)
+from gpu_helpers import (DEV, GDN_STATE_TOL, GDN_STATE_TOL_F16, bits, check_attn_out,
+                         check_gdn_out, check_gdn_state, err_word, np64, npi, say, sv_batch)
 
 pytestmark = pytest.mark.gpu
 
 
-def make_step(w, batch, seed, mode):
+def make_step(w, batch, seed, mode, state_dtype=torch.float32):
     layers = []
     for i, kind in enumerate(w.layers):
         if kind == 'attn':
             lay = wl.make_attn_layer(w, batch, seed + 10 * i, DEV)
             lay['out'] = torch.full_like(lay['q'], float('nan'))
         else:
-            lay = wl.make_gdn_layer(w, batch, seed + 10 * i, DEV)
+            lay = wl.make_gdn_layer(w, batch, seed + 10 * i, DEV, state_dtype=state_dtype)
             lay['out'] = torch.full_like(lay['v'], float('nan'))
         lay['kind'] = kind
         layers.append(lay)
@@ -41,10 +41,12 @@ def run_step(w, batch, layers, acc, mode, schedule=bd.SV_SCHEDULE_TWO_PHASE, pen
                               l['out']) for l in layers if l['kind'] == 'attn']
     g_layers = [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'],
                              l['out']) for l in layers if l['kind'] == 'gdn']
+    dt_s = next((bd.state_dtype(l['state']) for l in layers if l['kind'] == 'gdn'), bd.SV_F32)
     args = bd.StepArgs([1 if l['kind'] == 'attn' else 0 for l in layers],
                        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages,
                                       batch.block_table, dt_a),
-                       a_layers, bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt_g), g_layers,
+                       a_layers, bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt_g,
+                                               state_dtype=dt_s), g_layers,
                        bd.accept_args(mode, acc['target_logits'], acc['draft_tokens'],
                                       acc.get('draft_logits'), acc.get('u_accept'),
                                       acc.get('u_final')))
@@ -143,12 +145,14 @@ def test_hybrid_group_step(mode):
     compare(w, layers, res, ref, before)
 
 
-def test_deferred_schedule_equals_two_phase():
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.float16])
+def test_deferred_schedule_equals_two_phase(state_dtype):
     w = wl.WORKLOADS[3]
     w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1)})
     batch = wl.make_batch(w, 7, DEV, reserve=8)
-    l1, a1 = make_step(w, batch, 8, 'rejection')
-    l2, a2 = make_step(w, batch, 9, 'rejection')
+    l1, a1 = make_step(w, batch, 8, 'rejection', state_dtype)
+    l2, a2 = make_step(w, batch, 9, 'rejection', state_dtype)
+    tol = GDN_STATE_TOL if state_dtype == torch.float32 else 2 * GDN_STATE_TOL_F16
     init = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in l.items()}
             for l in l1]
 
@@ -208,4 +212,4 @@ def test_deferred_schedule_equals_two_phase():
             _, S2 = oracle.gdn_step(s_mid, None, None, np64(l['k']), np64(l['v']),
                                     np64(l['alpha']), np64(l['beta']), npi(batch.cu_seqlens),
                                     npi(t2['commit']), oracle.GDN_COMMIT_ONLY)
-            check_gdn_state(np64(l['state']), S2)
+            check_gdn_state(np64(l['state']), S2, tol=tol)

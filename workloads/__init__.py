@@ -196,9 +196,10 @@ def make_attn_layer(w: Workload, batch: Batch, seed: int, device='cpu'):
 
 
 def make_gdn_layer(w: Workload, batch: Batch, seed: int, device='cpu',
-                   num_slots=None):
-    """State bank ~N(0, 0.1) fp32, q/k/v ~N(0, 1) (L2-normalised as the
-    workload says, before rounding), gates alpha / beta in fp32."""
+                   num_slots=None, state_dtype=torch.float32):
+    """State bank ~N(0, 0.1) (drawn in fp32, stored as ``state_dtype``),
+    q/k/v ~N(0, 1) (L2-normalised as the workload says, before rounding),
+    gates alpha / beta in fp32."""
     g = generator(seed, device)
     Tt = batch.total_T
     ns = batch.B if num_slots is None else num_slots
@@ -220,7 +221,7 @@ def make_gdn_layer(w: Workload, batch: Batch, seed: int, device='cpu',
         beta = torch.sigmoid(torch.randn((Tt, w.H), generator=g,
                                          device=device))
     return {
-        'state': state,
+        'state': state.to(state_dtype),
         'q': q.to(w.gdn_dtype), 'k': k.to(w.gdn_dtype), 'v': v.to(w.gdn_dtype),
         'alpha': alpha.float().contiguous(), 'beta': beta.float().contiguous(),
     }
