@@ -103,6 +103,50 @@ def short_conv_timing(w, batch, sb, commit, stream, dev, reps=20):
             'schedule': 'deferred (pending replay + verify)'}
 
 
+def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=10):
+    """One GDN layer, deferred schedule (replay the previous step's accepted
+    tokens, verify this step's), with the state bank stored as fp32 and as
+    fp16 (fp32 arithmetic either way).  Four independent layers are cycled so
+    the timing is not an L2 replay."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    res = {}
+    for name, sdt in (('fp32_state', torch.float32), ('fp16_state', torch.float16)):
+        layers = [wl.make_gdn_layer(w, batch, 4000 + i, dev, state_dtype=sdt) for i in range(4)]
+        for l in layers:
+            l['out'] = torch.empty_like(l['v'])
+            l['pend'] = bd.make_gdn_pending(sb, l['k'], l['v'], l['alpha'], l['beta'], commit)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+
+        def run(l):
+            bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_ONLY, l['state'], l['q'], l['k'], l['v'],
+                                 l['alpha'], l['beta'], None, l['out'], pending=l['pend'],
+                                 stream=stream)
+        for l in layers:
+            run(l)
+        e0.record(stream)
+        for _ in range(reps):
+            for l in layers:
+                run(l)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * len(layers))
+        es = torch.finfo(sdt).bits // 8
+        T = batch.total_T
+        pend_rows = int(commit.sum().item())
+        # state read + write, current q/k/v/gates/out, replayed k/v/gates
+        nbytes = (2 * batch.B * w.H * w.dv * w.dk * es + T * w.H * (2 * w.dk + 2 * w.dv) * 2
+                  + T * w.H * 8 + pend_rows * w.H * ((w.dk + w.dv) * 2 + 8))
+        res[name] = {'layer_ms': round(ms, 4), 'bytes': nbytes,
+                     'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        del layers
+    res['schedule'] = 'deferred (pending replay + verify)'
+    return res
+
+
 def measured_traffic():
     """HBM bytes per attention launch (stream kernel + combine kernel) from the
     committed FETCH_SIZE / WRITE_SIZE counter runs, already scaled by the copy
@@ -368,6 +412,7 @@ def main():
     gdn_ms = g0.elapsed_time(g1) / max(1, len(gdn_l))
 
     conv = short_conv_timing(w, batch, sb, commits[0], stream, dev)
+    gdn_sd = gdn_state_dtype_timing(w, batch, sb, commits[0], stream, dev)
 
     T = batch.total_T
     n_att, n_gdn = len(att_layers), len(gdn_l)
@@ -403,7 +448,7 @@ def main():
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4)},
-        'next_rows': {'short_conv': conv},
+        'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd},
         'mean_accept_len': round(accepted, 3),
         'dtype_detail': 'bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance',
     }
