@@ -47,6 +47,8 @@ from .attention import append_kv, gather_context, verify_attention
 from .gdn import GDN_COMMIT_ONLY, GDN_VERIFY_COMMIT, GDN_VERIFY_ONLY, gdn_step
 from .accept import greedy_accept, icdf, rejection_accept, softmax64
 from .short_conv import CONV_COMMIT_ONLY, CONV_VERIFY_COMMIT, CONV_VERIFY_ONLY, conv_step
+from .kv_int8 import (append_kv_int8, dequantize_pool, dequantize_rows, quantize_int8,
+                      verify_attention_int8)
 from .step import verify_step
 
 __all__ = [
@@ -54,5 +56,7 @@ __all__ = [
     "GDN_VERIFY_COMMIT", "GDN_VERIFY_ONLY", "GDN_COMMIT_ONLY", "gdn_step",
     "greedy_accept", "rejection_accept", "softmax64", "icdf",
     "CONV_VERIFY_COMMIT", "CONV_VERIFY_ONLY", "CONV_COMMIT_ONLY", "conv_step",
+    "quantize_int8", "dequantize_rows", "dequantize_pool", "append_kv_int8",
+    "verify_attention_int8",
     "verify_step",
 ]
