@@ -19,6 +19,7 @@ SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 SV_GDN_VERIFY_COMMIT, SV_GDN_VERIFY_ONLY, SV_GDN_COMMIT_ONLY = 0, 1, 2
 SV_ACCEPT_GREEDY, SV_ACCEPT_REJECTION = 0, 1
 SV_SCHEDULE_TWO_PHASE, SV_SCHEDULE_DEFERRED = 0, 1
+SV_KV_PLAIN, SV_KV_INT8 = 0, 1
 SV_DERR = {1: 'PAGE', 2: 'CAPACITY', 4: 'SEQLEN', 8: 'COMMIT', 16: 'TOKEN',
            32: 'SLOT'}
 
@@ -43,7 +44,7 @@ class SvConvPending(ctypes.Structure):
 
 class SvAttnLayer(ctypes.Structure):
     _fields_ = [('q', _vp), ('k_new', _vp), ('v_new', _vp), ('k_cache', _vp),
-                ('v_cache', _vp), ('out', _vp)]
+                ('v_cache', _vp), ('out', _vp), ('k_scale', _vp), ('v_scale', _vp)]
 
 
 class SvGdnLayer(ctypes.Structure):
@@ -55,7 +56,8 @@ class SvAttnConfig(ctypes.Structure):
     _fields_ = [('Hq', _c_i32), ('Hkv', _c_i32), ('D', _c_i32),
                 ('page_size', _c_i32), ('num_pages', _c_i32),
                 ('max_pages_per_seq', _c_i32), ('block_table', _vp),
-                ('dtype', ctypes.c_int), ('scale', ctypes.c_float)]
+                ('dtype', ctypes.c_int), ('scale', ctypes.c_float),
+                ('kv_format', ctypes.c_int)]
 
 
 class SvGdnConfig(ctypes.Structure):
@@ -85,6 +87,10 @@ _SIGS = {
         [ctypes.POINTER(SvBatch), _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
          _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int,
          ctypes.c_float, _c_i32, _vp, _sz, _vp, _vp], ctypes.c_int),
+    'spec_verify_attention_kv8': (
+        [ctypes.POINTER(SvBatch), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+         _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_float, _vp, _sz, _vp, _vp],
+        ctypes.c_int),
     'gdn_verify_commit': (
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, ctypes.c_int, _vp, _c_i32, _vp,
          _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
@@ -210,6 +216,29 @@ def spec_verify_attention(batch, q, k_new, v_new, k_cache, v_cache,
         _i32(err, 'err'), _stream(stream)))
 
 
+def spec_verify_attention_kv8(batch, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                              block_table, ctx_lens, out, scale=0.0, workspace=None, err=None,
+                              stream=None):
+    """Verification attention over INT8 pages (``spec_verify_attention_kv8``).
+
+    q/k_new/v_new/out bf16 as for ``spec_verify_attention``; caches int8
+    [num_pages, Hkv, P, D]; k_scale / v_scale fp32 [Hkv, D].
+    """
+    if k_cache.dtype != torch.int8 or v_cache.dtype != torch.int8:
+        raise ValueError('INT8 pages must be torch.int8')
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise ValueError('scales must be float32')
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k_new.shape[1]
+    num_pages, P = k_cache.shape[0], k_cache.shape[2]
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().spec_verify_attention_kv8(
+        ctypes.byref(batch), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _i32(block_table, 'block_table'), block_table.shape[1],
+        num_pages, P, _i32(ctx_lens, 'ctx_lens'), _ptr(out), Hq, Hkv, D, float(scale),
+        _ptr(workspace), ws_n, _i32(err, 'err'), _stream(stream)))
+
+
 def gdn_verify_commit(batch, mode, state, q, k, v, alpha, beta, commit_len,
                       out, state_slot=None, pending=None, err=None,
                       stream=None):
@@ -309,9 +338,10 @@ class StepArgs:
         self.acc = accept_args
 
 
-def attn_config(Hq, Hkv, D, page_size, num_pages, block_table, dtype, scale=0.0):
+def attn_config(Hq, Hkv, D, page_size, num_pages, block_table, dtype, scale=0.0,
+                kv_format=SV_KV_PLAIN):
     return SvAttnConfig(Hq, Hkv, D, page_size, num_pages, block_table.shape[1],
-                        _i32(block_table, 'block_table'), dtype, float(scale))
+                        _i32(block_table, 'block_table'), dtype, float(scale), kv_format)
 
 
 def state_dtype(state):
@@ -328,9 +358,9 @@ def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None, state_dtype=SV_F
                        state_dtype)
 
 
-def attn_layer(q, k_new, v_new, k_cache, v_cache, out):
+def attn_layer(q, k_new, v_new, k_cache, v_cache, out, k_scale=None, v_scale=None):
     return SvAttnLayer(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-                       _ptr(v_cache), _ptr(out))
+                       _ptr(v_cache), _ptr(out), _ptr(k_scale), _ptr(v_scale))
 
 
 def gdn_layer(state, q, k, v, alpha, beta, out):

@@ -51,8 +51,8 @@ sv_status check_batch(const sv_batch* b, const char* who) {
 sv_status check_attn(const sv_batch* batch, const void* q, const void* k_new, const void* v_new,
                      void* k_cache, void* v_cache, const int32_t* block_table,
                      int32_t max_pages, int32_t num_pages, int32_t P, const int32_t* ctx_lens,
-                     void* out, int32_t Hq, int32_t Hkv, int32_t D, sv_dtype dtype) {
-  const char* who = "spec_verify_attention";
+                     void* out, int32_t Hq, int32_t Hkv, int32_t D, sv_dtype dtype,
+                     const char* who = "spec_verify_attention") {
   sv_status st = check_batch(batch, who);
   if (st != SV_OK) return st;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !ctx_lens || !out)
@@ -88,7 +88,8 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
                             const int32_t* block_table, int32_t max_pages, int32_t num_pages,
                             int32_t P, const int32_t* ctx_lens, void* out, int32_t Hq,
                             int32_t Hkv, int32_t D, sv_dtype dtype, float scale, int32_t write_kv,
-                            void* ws, int32_t* err) {
+                            void* ws, int32_t* err, const float* k_scale = nullptr,
+                            const float* v_scale = nullptr) {
   sv::AttnArgs a{};
   a.B = batch->B;
   a.total_T = batch->total_T;
@@ -111,8 +112,11 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
   a.scale = scale == 0.f ? 1.f / std::sqrt(static_cast<float>(D)) : scale;
   a.write_kv = write_kv ? 1 : 0;
   a.err = err;
+  a.kv8 = k_scale != nullptr;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   if (dtype == SV_BF16) {
-    a.n_wg = sv::attn_stream_grid(D, Hq / Hkv, a.max_T);
+    a.n_wg = sv::attn_stream_grid(D, Hq / Hkv, a.max_T, a.kv8 != 0);
     sv::attn_workspace_carve(ws, a.B, Hkv, D, a.n_wg, &a.seg_meta, &a.part_o, &a.part_ml);
   }
   return a;
@@ -219,6 +223,33 @@ sv_status spec_verify_attention(const sv_batch* batch, const void* q, const void
                                   max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv,
                                   D, dtype, scale, write_kv, workspace, err);
   return hip_status(sv::launch_attention(a, dtype, stream), "spec_verify_attention");
+}
+
+sv_status spec_verify_attention_kv8(const sv_batch* batch, const void* q, const void* k_new,
+                                    const void* v_new, int8_t* k_cache, int8_t* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    int32_t num_pages, int32_t page_size,
+                                    const int32_t* ctx_lens, void* out, int32_t Hq, int32_t Hkv,
+                                    int32_t D, float scale, void* workspace,
+                                    size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+  const char* who = "spec_verify_attention_kv8";
+  sv_status st = check_attn(batch, q, k_new, v_new, k_cache, v_cache, block_table,
+                            max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv, D,
+                            SV_BF16, who);
+  if (st != SV_OK) return st;
+  if (!k_scale || !v_scale) return fail(SV_EINVAL, "%s: k_scale and v_scale are required", who);
+  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 15)
+    return fail(SV_EINVAL, "%s: scales must be 16-byte aligned", who);
+  const size_t need = sv::attn_workspace_bytes(batch->B, batch->total_T, Hq, Hkv, D,
+                                               max_pages_per_seq, page_size, SV_BF16);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
+                workspace ? workspace_bytes : size_t(0));
+  sv::AttnArgs a = make_attn_args(batch, q, k_new, v_new, k_cache, v_cache, block_table,
+                                  max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv,
+                                  D, SV_BF16, scale, 1, workspace, err, k_scale, v_scale);
+  return hip_status(sv::launch_attention(a, SV_BF16, stream), who);
 }
 
 sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state,
@@ -414,6 +445,10 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
   }
   if (n_attn && (!acfg || !attn)) return fail(SV_EINVAL, "%s: attention config/layers missing", who);
   if (n_gdn && (!gcfg || !gdn)) return fail(SV_EINVAL, "%s: GDN config/layers missing", who);
+  if (n_attn && acfg->kv_format != SV_KV_PLAIN && acfg->kv_format != SV_KV_INT8)
+    return fail(SV_EINVAL, "%s: unknown kv_format %d", who, static_cast<int>(acfg->kv_format));
+  if (n_attn && acfg->kv_format == SV_KV_INT8 && acfg->dtype != SV_BF16)
+    return fail(SV_EDTYPE, "%s: INT8 KV pages take bf16 activations", who);
   if (pending && schedule != SV_SCHEDULE_DEFERRED)
     return fail(SV_EINVAL, "%s: pending tokens are only used by the deferred schedule", who);
   if (pending && (!pending->layers || !pending->commit_len))
@@ -428,11 +463,19 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
   for (int l = 0; l < n_layers; ++l) {
     if (layer_kind[l] == 1) {
       const sv_attn_layer& L = attn[ia++];
-      st = spec_verify_attention(batch, L.q, L.k_new, L.v_new, L.k_cache, L.v_cache,
-                                 acfg->block_table, acfg->max_pages_per_seq, acfg->num_pages,
-                                 acfg->page_size, ctx_lens, L.out, acfg->Hq, acfg->Hkv, acfg->D,
-                                 acfg->dtype, acfg->scale, 1, workspace, workspace_bytes, err,
-                                 stream);
+      if (acfg->kv_format == SV_KV_INT8) {
+        st = spec_verify_attention_kv8(
+            batch, L.q, L.k_new, L.v_new, static_cast<int8_t*>(L.k_cache),
+            static_cast<int8_t*>(L.v_cache), L.k_scale, L.v_scale, acfg->block_table,
+            acfg->max_pages_per_seq, acfg->num_pages, acfg->page_size, ctx_lens, L.out, acfg->Hq,
+            acfg->Hkv, acfg->D, acfg->scale, workspace, workspace_bytes, err, stream);
+      } else {
+        st = spec_verify_attention(batch, L.q, L.k_new, L.v_new, L.k_cache, L.v_cache,
+                                   acfg->block_table, acfg->max_pages_per_seq, acfg->num_pages,
+                                   acfg->page_size, ctx_lens, L.out, acfg->Hq, acfg->Hkv, acfg->D,
+                                   acfg->dtype, acfg->scale, 1, workspace, workspace_bytes, err,
+                                   stream);
+      }
     } else {
       const sv_gdn_layer& G = gdn[ig];
       sv_gdn_pending pg{};

@@ -28,12 +28,22 @@
 //     so the online-softmax state of a query row and its output columns sit
 //     in the same lane and the rescale needs no shuffle;
 //   * the 4 waves merge their (max, sum, O) in LDS in a fixed order.
+// INT8 pages (bf16 activations; the main model's kv_cache_quant_type =
+// int8_per_channel in the onnxruntime-genai pull request 2457 commit message on
+// the MTP head): code = clamp(rint(x / s), -127, 127) with a static fp32 scale
+// s per (KV head, channel) for K and for V.  A small kernel first writes the
+// in-flight rows' codes into their slots; the stream kernel then reads every
+// position from the pages (8 KiB per 64-key tile at D = 128, half the bf16
+// bytes), widens the codes to fp16 exactly on the way into LDS and runs the
+// same tiles with fp16 MFMAs: the K scale is folded into Q (q_d s_d rounded to
+// fp16), the V scale applied to the accumulated output channel.
 // fp32 path: one wave per (query token, head), plain VALU online softmax.
 
 #include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -46,6 +56,9 @@ constexpr int kKT = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(4))) float float4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -65,6 +78,26 @@ __device__ __forceinline__ uint32_t half16(const uint4& u, int e) {
 __device__ __forceinline__ uint32_t half16(u32x4_t u, int e) {
   const uint32_t w = u[e >> 1];
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Four int8 codes (one 32-bit word) -> four fp16 values, exactly: the byte
+// with its sign bit flipped is u = c + 128 in 0..255; placed under the fp16
+// exponent of 1024 it reads 1024 + u, and subtracting 1152 leaves c.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const f16x2_t bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
+  const f16x2_t l = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias;
+  const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;
+  lo = __builtin_bit_cast(uint32_t, l);
+  hi = __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
 __device__ __forceinline__ int seq_tiles(int L, int T) { return (L + T + kKT - 1) / kKT; }
@@ -128,14 +161,13 @@ __host__ __device__ inline int piece_wg(int t, int W, int N) {
 
 // PF: tiles in flight per workgroup (a ring of register buffers; registers
 // are the largest staging store of a CU).
-// WPE: waves per SIMD the register allocation is held to (workgroups per
-// CU; the LDS of three fits in one CU).
-template <int D, int NQT, int PF, int WPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void attn_stream_bf16(AttnArgs a) {
-  constexpr int CPK = D / 8;        // 16-byte chunks per key row
-  constexpr int KPT = CPK / 4;      // keys per thread per tile (4 or 2)
-  constexpr int KS = D + 8;         // K row stride in LDS (bf16 elements)
+// KV8: INT8 pages (fp16 tiles in LDS and fp16 MFMAs) instead of bf16 pages.
+template <int D, int NQT, int PF, bool KV8>
+__device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
+  constexpr int DPC = KV8 ? 16 : 8;  // dims per 16-byte chunk
+  constexpr int CPK = D / DPC;      // 16-byte chunks per key row
+  constexpr int KPT = CPK / 4;      // keys per thread per tile (4, 2 or 1)
+  constexpr int KS = D + 8;         // K row stride in LDS (16-bit elements)
   constexpr int VS = kKT + 4;       // V^T row stride in LDS
   constexpr int NDT = D / 16;       // 16-dim output tiles
   constexpr int NKS = D / 32;       // k-steps of the QK^T product
@@ -194,14 +226,17 @@ void attn_stream_bf16(AttnArgs a) {
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
   const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
   const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
-  const int dc = tid % CPK, kb = tid / CPK;  // thread's slice: keys KPT*kb.., dims 8*dc..
+  const int8_t* kc8 = static_cast<const int8_t*>(a.k_cache);
+  const int8_t* vc8 = static_cast<const int8_t*>(a.v_cache);
+  const int dc = tid % CPK, kb = tid / CPK;  // thread's slice: keys KPT*kb.., dims DPC*dc..
   const float sl2 = a.scale * kLog2e;
   bool bad_page = false;
 
   // State of the current piece and chunk (function scope, read by the
   // always-inlined helpers below).
   int b = 0, g = 0, x0 = 0, T = 1, L = 0, M = 1, pos_end = 1, first_page = 0;
-  bf16x8_t qf[NQT][NKS];
+  using QF = std::conditional_t<KV8, f16x8_t, bf16x8_t>;
+  QF qf[NQT][NKS];
   float4_t oacc[NQT][NDT];
   float m_run[NQT], l_run[NQT];
 
@@ -219,6 +254,15 @@ void attn_stream_bf16(AttnArgs a) {
       const int p = tile * kKT + KPT * kb + i;
       const int pc = min(p, pos_end - 1);
       const int pid = s_ids[pc / P - first_page];
+      if constexpr (KV8) {
+        // every position, in-flight ones included, is read from the pages
+        // (a bad page reads page 0: the sequence is flagged)
+        const size_t off =
+            ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pc % P)) * D + 16 * dc;
+        r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc8 + off));
+        r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc8 + off));
+        continue;
+      }
       const bool in_ctx = p < L && p < pos_end && pid >= 0;
       const size_t off_c =
           ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pc % P)) * D + 8 * dc;
@@ -234,6 +278,39 @@ void attn_stream_bf16(AttnArgs a) {
   };
   // K rows: 16-byte stores; V transposed: KPT keys of one dim per store.
   auto write_lds = [&](const TileRegs<KPT>& r) __attribute__((always_inline)) {
+    if constexpr (KV8) {
+      // 16 codes per register quad -> 16 fp16 values (two quads)
+      u32x4_t kh[KPT][2], vh[KPT][2];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t lo, hi;
+          i8x4_to_f16(r.k[i][c], lo, hi);
+          kh[i][c >> 1][2 * (c & 1)] = lo;
+          kh[i][c >> 1][2 * (c & 1) + 1] = hi;
+          i8x4_to_f16(r.v[i][c], lo, hi);
+          vh[i][c >> 1][2 * (c & 1)] = lo;
+          vh[i][c >> 1][2 * (c & 1) + 1] = hi;
+        }
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(Ks + (KPT * kb + i) * KS + 16 * dc);
+        dst[0] = kh[i][0];
+        dst[1] = kh[i][1];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        uint16_t* dst = Vt + (16 * dc + e) * VS + KPT * kb;
+        if constexpr (KPT == 2) {
+          *reinterpret_cast<uint32_t*>(dst) =
+              half16(vh[0][e >> 3], e & 7) | (half16(vh[1][e >> 3], e & 7) << 16);
+        } else {
+          *dst = static_cast<uint16_t>(half16(vh[0][e >> 3], e & 7));
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       *reinterpret_cast<u32x4_t*>(Ks + (KPT * kb + i) * KS + 8 * dc) = r.k[i];
@@ -261,9 +338,14 @@ void attn_stream_bf16(AttnArgs a) {
       float4_t sacc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        U16x8 af;
-        af.u = *reinterpret_cast<const uint4*>(Ks + (16 * w + lr) * KS + 32 * ks + 8 * lg);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, qf[nt][ks], sacc, 0, 0, 0);
+        const u32x4_t araw =
+            *reinterpret_cast<const u32x4_t*>(Ks + (16 * w + lr) * KS + 32 * ks + 8 * lg);
+        if constexpr (KV8)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, araw),
+                                                        qf[nt][ks], sacc, 0, 0, 0);
+        else
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, araw),
+                                                         qf[nt][ks], sacc, 0, 0, 0);
       }
       // lane holds S^T[key 4 lg + r][row lr]
       const int m = 16 * nt + lr;
@@ -287,9 +369,11 @@ void attn_stream_bf16(AttnArgs a) {
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint16_t hb = f32_to_bf16(exp2f(sv[r] - m_new));
+          // the rounded weight enters both the PV product and the normaliser
+          const float e = exp2f(sv[r] - m_new);
+          const uint16_t hb = KV8 ? f32_to_f16_bits(e) : f32_to_bf16(e);
           pf[r] = static_cast<short>(hb);
-          psum += bf16_to_f32(hb);
+          psum += KV8 ? f16_bits_to_f32(hb) : bf16_to_f32(hb);
         }
         l_run[nt] = l_run[nt] * alpha + psum;
 #pragma unroll
@@ -300,7 +384,13 @@ void attn_stream_bf16(AttnArgs a) {
       for (int dt = 0; dt < NDT; ++dt) {
         const short4_t vf =
             *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS + 16 * w + 4 * lg);
-        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, oacc[nt][dt], 0, 0, 0);
+        if constexpr (KV8)
+          oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(f16x4_t, vf), __builtin_bit_cast(f16x4_t, pf), oacc[nt][dt], 0, 0,
+              0);
+        else
+          oacc[nt][dt] =
+              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, oacc[nt][dt], 0, 0, 0);
       }
     }
   };
@@ -358,7 +448,19 @@ void attn_stream_bf16(AttnArgs a) {
         } else {
           tq.u = make_uint4(0, 0, 0, 0);
         }
-        qf[nt][ks] = tq.v;
+        if constexpr (KV8) {
+          // fold the K channel scales into q: q_d s_d, rounded to fp16
+          const float* ksc = a.k_scale + static_cast<size_t>(g) * D + 32 * ks + 8 * lg;
+          const float4 s0 = *reinterpret_cast<const float4*>(ksc);
+          const float4 s1 = *reinterpret_cast<const float4*>(ksc + 4);
+          const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          f16x8_t qh;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qh[e] = static_cast<_Float16>(bf16_to_f32(tq.h[e]) * sc[e]);
+          qf[nt][ks] = qh;
+        } else {
+          qf[nt][ks] = tq.v;
+        }
       }
     }
 #pragma unroll
@@ -387,7 +489,7 @@ void attn_stream_bf16(AttnArgs a) {
 
       // write-through of the in-flight K/V rows that fall in this chunk (reads
       // of those positions come from k_new / v_new)
-      if (a.write_kv) {
+      if (!KV8 && a.write_kv) {
         for (int idx = tid; idx < T * CPK; idx += kThreads) {
           const int j = idx / CPK, c = idx - j * CPK;
           const int p = L + j;
@@ -474,7 +576,11 @@ void attn_stream_bf16(AttnArgs a) {
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww)
         if (wm[ww][m] != -INFINITY) ls += wl[ww][m] * exp2f(wm[ww][m] - mm);
-      const float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
+      float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
+      if constexpr (KV8) {  // the V channel scales
+        const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + static_cast<size_t>(g) * D + d4);
+        o = make_float4(o.x * vs.x, o.y * vs.y, o.z * vs.z, o.w * vs.w);
+      }
       if (whole) {
         const int j = m / G, hh = m - j * G;
         const size_t row = static_cast<size_t>(x0 + j) * a.Hq + g * G + hh;
@@ -494,6 +600,60 @@ void attn_stream_bf16(AttnArgs a) {
     }
   }
   if (bad_page) flag_error(a.err, SV_DERR_PAGE);
+}
+
+// WPE: waves per SIMD the register allocation is held to (workgroups per
+// CU; the LDS of three fits in one CU).
+template <int D, int NQT, int PF, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_stream_bf16(AttnArgs a) {
+  attn_stream_body<D, NQT, PF, false>(a);
+}
+
+template <int D, int NQT, int PF, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_stream_kv8(AttnArgs a) {
+  attn_stream_body<D, NQT, PF, true>(a);
+}
+
+// --------------------------------------------------------------------------
+// INT8 pages: the in-flight rows' codes, written before the stream kernel
+// reads them.  One workgroup per (verify token, sequence); four channels per
+// thread: code = clamp(rint(x / s), -127, 127) with the fp32 quotient.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t quant4(uint2 x, float4 s) {
+  const float xs[4] = {bf16_to_f32(x.x & 0xffffu), bf16_to_f32(x.x >> 16),
+                       bf16_to_f32(x.y & 0xffffu), bf16_to_f32(x.y >> 16)};
+  const float ss[4] = {s.x, s.y, s.z, s.w};
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float c = fminf(fmaxf(rintf(xs[e] / ss[e]), -127.f), 127.f);
+    w |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xffu) << (8 * e);
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(256) void attn_append_kv8(AttnArgs a) {
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int x0, T, L;
+  if (!attn_seq_ok(a, b, &x0, &T, &L, false)) return;  // the stream kernel flags it
+  if (j >= T) return;
+  const int p = L + j;
+  const int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + p / a.P];
+  if (pid < 0 || pid >= a.num_pages) return;          // flagged by the stream kernel
+  const int HD = a.Hkv * a.D;
+  const size_t src = static_cast<size_t>(x0 + j) * HD;
+  for (int c4 = tid; c4 < HD / 4; c4 += 256) {
+    const int idx = 4 * c4, g = idx / a.D, d = idx - g * a.D;
+    const size_t dst = ((static_cast<size_t>(pid) * a.Hkv + g) * a.P + (p % a.P)) * a.D + d;
+    const uint2 kx = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.k_new) + src + idx);
+    const uint2 vx = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v_new) + src + idx);
+    *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(a.k_cache) + dst) =
+        quant4(kx, *reinterpret_cast<const float4*>(a.k_scale + idx));
+    *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(a.v_cache) + dst) =
+        quant4(vx, *reinterpret_cast<const float4*>(a.v_scale + idx));
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -637,10 +797,14 @@ constexpr int waves_per_simd() {
   return NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
 }
 
-template <int D, int NQT>
+template <int D, int NQT, bool KV8>
 const void* stream_kernel() {
-  return reinterpret_cast<const void*>(
-      &attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>);
+  if constexpr (KV8)
+    return reinterpret_cast<const void*>(
+        &attn_stream_kv8<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>);
+  else
+    return reinterpret_cast<const void*>(
+        &attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>);
 }
 
 int nqt_for(int G, int max_T) {
@@ -648,48 +812,57 @@ int nqt_for(int G, int max_T) {
   return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
 }
 
+template <bool KV8>
 const void* stream_kernel_for(int D, int nqt) {
   if (D == 128) {
-    if (nqt == 1) return stream_kernel<128, 1>();
-    if (nqt == 2) return stream_kernel<128, 2>();
-    return stream_kernel<128, 4>();
+    if (nqt == 1) return stream_kernel<128, 1, KV8>();
+    if (nqt == 2) return stream_kernel<128, 2, KV8>();
+    return stream_kernel<128, 4, KV8>();
   }
-  if (nqt == 1) return stream_kernel<64, 1>();
-  if (nqt == 2) return stream_kernel<64, 2>();
-  return stream_kernel<64, 4>();
+  if (nqt == 1) return stream_kernel<64, 1, KV8>();
+  if (nqt == 2) return stream_kernel<64, 2, KV8>();
+  return stream_kernel<64, 4, KV8>();
 }
 
 // Resident workgroups of one stream-kernel instance on the current device:
 // the grid that keeps every CU busy without a second wave of workgroups.
-int stream_grid(int D, int nqt) {
+int stream_grid(int D, int nqt, bool kv8) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int>, int> cache;
+  static std::map<std::tuple<int, int, int, bool>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_tuple(dev, D, nqt);
+  const auto key = std::make_tuple(dev, D, nqt, kv8);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel_for(D, nqt), kThreads, 0) !=
-          hipSuccess || per_cu < 1)
+  const void* fn = kv8 ? stream_kernel_for<true>(D, nqt) : stream_kernel_for<false>(D, nqt);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
+      per_cu < 1)
     per_cu = 1;
   const int n = cus * per_cu;
   cache[key] = n;
   return n;
 }
 
+// The workspace holds the pieces of the largest grid of either page format.
 int stream_grid_max(int D) {
-  return std::max(stream_grid(D, 1), std::max(stream_grid(D, 2), stream_grid(D, 4)));
+  int n = 0;
+  for (int kv8 = 0; kv8 < 2; ++kv8)
+    for (int nqt : {1, 2, 4}) n = std::max(n, stream_grid(D, nqt, kv8 != 0));
+  return n;
 }
 
 template <int D, int NQT>
-void launch_bf16(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>),
-                     dim3(a.n_wg), dim3(kThreads),
-                     0, stream, a);
+void launch_stream(const AttnArgs& a, hipStream_t stream) {
+  if (a.kv8)
+    hipLaunchKernelGGL((attn_stream_kv8<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>),
+                       dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>),
+                       dim3(a.n_wg), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
@@ -719,22 +892,29 @@ void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_m
   *part_ml = reinterpret_cast<float*>(base + meta + o_bytes);
 }
 
-int attn_stream_grid(int D, int G, int max_T) { return stream_grid(D, nqt_for(G, max_T)); }
+int attn_stream_grid(int D, int G, int max_T, bool kv8) {
+  return stream_grid(D, nqt_for(G, max_T), kv8);
+}
 
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype, hipStream_t stream) {
   if (dtype == SV_F32) {
     hipLaunchKernelGGL(attn_f32, dim3(a.Hq, a.max_T, a.B), dim3(64), 0, stream, a);
     return hipGetLastError();
   }
+  if (a.kv8) {
+    hipLaunchKernelGGL(attn_append_kv8, dim3(a.max_T, a.B), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nqt = nqt_for(a.Hq / a.Hkv, a.max_T);
   if (a.D == 128) {
-    if (nqt == 1) launch_bf16<128, 1>(a, stream);
-    else if (nqt == 2) launch_bf16<128, 2>(a, stream);
-    else launch_bf16<128, 4>(a, stream);
+    if (nqt == 1) launch_stream<128, 1>(a, stream);
+    else if (nqt == 2) launch_stream<128, 2>(a, stream);
+    else launch_stream<128, 4>(a, stream);
   } else {
-    if (nqt == 1) launch_bf16<64, 1>(a, stream);
-    else if (nqt == 2) launch_bf16<64, 2>(a, stream);
-    else launch_bf16<64, 4>(a, stream);
+    if (nqt == 1) launch_stream<64, 1>(a, stream);
+    else if (nqt == 2) launch_stream<64, 2>(a, stream);
+    else launch_stream<64, 4>(a, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -88,6 +88,10 @@ struct AttnArgs {
   int Hq, Hkv, D;
   float scale;                  // already resolved (never 0)
   int write_kv;
+  // INT8 pages: k_cache / v_cache hold int8 codes, scales fp32 [Hkv][D]
+  int kv8;
+  const float* k_scale;
+  const float* v_scale;
   int32_t* err;
   // stream-kernel grid and the pieces of segments cut by range boundaries
   int n_wg;                     // workgroups (grid.x)
@@ -102,7 +106,7 @@ size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D,
 void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_meta,
                           float** part_o, float** part_ml);
 // Grid of the stream kernel for these shapes on the current device.
-int attn_stream_grid(int D, int G, int max_T);
+int attn_stream_grid(int D, int G, int max_T, bool kv8);
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype,
                             hipStream_t stream);
 

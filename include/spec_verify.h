@@ -117,6 +117,35 @@ SV_API sv_status spec_verify_attention(const sv_batch* batch,
     int32_t* err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The same verification attention over INT8 pages.
+ *
+ * onnxruntime-genai #2457, commit message on the MTP head and INT8 KV: the
+ * main model's cache uses kv_cache_quant_type = int8_per_channel with scales
+ * calibrated per attention layer.  Symmetric per-channel codes with a static
+ * fp32 scale for every (KV head, channel), one set for K and one for V:
+ *   code = clamp(round_half_even(x / s), -127, 127),   x ~ s * code
+ * where x / s is the correctly rounded fp32 quotient of the row value (bf16,
+ * widened exactly) and the scale.  The result is the attention of
+ * spec_verify_attention over the dequantized cache; the in-flight rows are
+ * ALWAYS written (their codes at L_b .. L_b + T_b - 1) and read back like
+ * every other position, so they enter as their codes too.
+ *
+ *   q, k_new, v_new, out  bf16, shapes as above
+ *   k_cache, v_cache      int8 [num_pages, Hkv, page_size, D], updated in place
+ *   k_scale, v_scale      fp32 [Hkv, D], positive and finite (a zero or
+ *                         non-finite scale gives saturated codes, no error)
+ * Limits as for the bf16 path; every tensor 16-byte aligned.  Workspace:
+ * spec_verify_attention_workspace_bytes(..., SV_BF16).
+ * ------------------------------------------------------------------------ */
+SV_API sv_status spec_verify_attention_kv8(const sv_batch* batch,
+    const void* q, const void* k_new, const void* v_new,
+    int8_t* k_cache, int8_t* v_cache, const float* k_scale, const float* v_scale,
+    const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_pages,
+    int32_t page_size, const int32_t* ctx_lens, void* out,
+    int32_t Hq, int32_t Hkv, int32_t D, float scale,
+    void* workspace, size_t workspace_bytes, int32_t* err, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Gated delta-net recurrent state: verify and commit.
  *
  * Gated delta rule (Yang, Kautz & Hatamizadeh, ICLR 2025), per (b, h), state
@@ -275,7 +304,8 @@ SV_API sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode,
  * target pass, then the speculative round whose recurrent-state commit runs
  * after acceptance):
  *   1. every layer in model order: attention layers run
- *      spec_verify_attention (write_kv = 1); GDN layers run their verify pass
+ *      spec_verify_attention (write_kv = 1), or spec_verify_attention_kv8
+ *      when acfg->kv_format is SV_KV_INT8; GDN layers run their verify pass
  *      (deferred schedule: applying the pending tokens first and storing);
  *   2. spec_accept -> result, commit_len = accept_len + 1;
  *   3. two-phase schedule: one launch applies the first commit_len tokens of
@@ -290,9 +320,12 @@ SV_API sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode,
  * ------------------------------------------------------------------------ */
 typedef enum { SV_SCHEDULE_TWO_PHASE = 0, SV_SCHEDULE_DEFERRED = 1 } sv_schedule;
 
+typedef enum { SV_KV_PLAIN = 0, SV_KV_INT8 = 1 } sv_kv_format;
+
 typedef struct {
   const void* q; const void* k_new; const void* v_new;
   void* k_cache; void* v_cache; void* out;
+  const float* k_scale; const float* v_scale;  /* SV_KV_INT8 only */
 } sv_attn_layer;
 
 typedef struct {
@@ -305,6 +338,7 @@ typedef struct {
   const int32_t* block_table;  /* [B, max_pages_per_seq] */
   sv_dtype dtype;
   float scale;                 /* 0 => 1/sqrt(D) */
+  sv_kv_format kv_format;      /* SV_KV_INT8: int8 pools, dtype SV_BF16 */
 } sv_attn_config;
 
 typedef struct {

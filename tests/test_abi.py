@@ -79,6 +79,44 @@ def test_attention_validation():
     assert 'workspace' in L.sv_last_error().decode()
 
 
+def test_attention_kv8_validation():
+    L = bd.lib()
+    b = _batch()
+    args = dict(q=16, kc=16, ks=16, vs=16, P=64, D=128, Hq=32, Hkv=8, ws=16, wsn=1 << 30)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.spec_verify_attention_kv8(
+            ctypes.byref(b), a['q'], 16, 16, a['kc'], 16, a['ks'], a['vs'], 16, 4, 8, a['P'],
+            16, 16, a['Hq'], a['Hkv'], a['D'], 0.0, a['ws'], a['wsn'], None, None)
+    assert call(ks=None) == bd.SV_EINVAL
+    assert 'scale' in L.sv_last_error().decode()
+    assert call(vs=None) == bd.SV_EINVAL
+    assert call(ks=20) == bd.SV_EINVAL                       # misaligned scales
+    assert call(kc=24) == bd.SV_EINVAL                       # misaligned pool
+    assert call(D=96) == bd.SV_EDTYPE
+    assert call(P=48) == bd.SV_EINVAL
+    assert call(Hq=30) == bd.SV_EINVAL
+    assert call(ws=None) == bd.SV_EWORKSPACE
+    assert 'spec_verify_attention_kv8' in L.sv_last_error().decode()
+
+
+def test_step_rejects_int8_pages_with_fp32_activations():
+    L = bd.lib()
+    b = _batch()
+    kinds = (ctypes.c_uint8 * 1)(1)
+    cfg = bd.SvAttnConfig(32, 8, 128, 64, 8, 4, 16, bd.SV_F32, 0.0, bd.SV_KV_INT8)
+    lay = (bd.SvAttnLayer * 1)(bd.SvAttnLayer(16, 16, 16, 16, 16, 16, 16, 16))
+    acc = bd.SvAcceptArgs(0, bd.SV_BF16, 100, 16, None, 16, None, None)
+    st = L.spec_verify_step(ctypes.byref(b), 1, kinds, ctypes.byref(cfg), lay, None, None,
+                            ctypes.byref(acc), 16, 16, 16, 0, None, 16, 1 << 30, None, None)
+    assert st == bd.SV_EDTYPE and 'INT8' in L.sv_last_error().decode()
+    cfg.kv_format = 5
+    st = L.spec_verify_step(ctypes.byref(b), 1, kinds, ctypes.byref(cfg), lay, None, None,
+                            ctypes.byref(acc), 16, 16, 16, 0, None, 16, 1 << 30, None, None)
+    assert st == bd.SV_EINVAL and 'kv_format' in L.sv_last_error().decode()
+
+
 def test_gdn_validation():
     L = bd.lib()
     b = _batch()

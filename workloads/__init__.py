@@ -195,6 +195,30 @@ def make_attn_layer(w: Workload, batch: Batch, seed: int, device='cpu'):
     }
 
 
+def make_attn_layer_kv8(w: Workload, batch: Batch, seed: int, device='cpu'):
+    """INT8 pages: bf16 q / k_new / v_new rows ~N(0, 1); page codes drawn as
+    round(N(0, 32^2)) clipped to +-127 (a bell-shaped histogram over the code
+    range, as calibrated scales give); per-(KV head, channel) fp32 scales
+    ~U(0.5, 1.5) * 4 / 127, so rows of the same N(0, 1) data span the range."""
+    g = generator(seed, device)
+    Tt = batch.total_T
+    shape_pool = (batch.num_pages, w.Hkv, batch.P, w.D)
+
+    def codes():
+        c = torch.randn(shape_pool, generator=g, device=device).mul_(32.0).round_()
+        return c.clamp_(-127, 127).to(torch.int8)
+
+    return {
+        'q': _randn((Tt, w.Hq, w.D), g, device, torch.bfloat16),
+        'k_new': _randn((Tt, w.Hkv, w.D), g, device, torch.bfloat16),
+        'v_new': _randn((Tt, w.Hkv, w.D), g, device, torch.bfloat16),
+        'k_cache': codes(),
+        'v_cache': codes(),
+        'k_scale': (torch.rand((w.Hkv, w.D), generator=g, device=device) + 0.5).mul_(4.0 / 127),
+        'v_scale': (torch.rand((w.Hkv, w.D), generator=g, device=device) + 0.5).mul_(4.0 / 127),
+    }
+
+
 def make_gdn_layer(w: Workload, batch: Batch, seed: int, device='cpu',
                    num_slots=None, state_dtype=torch.float32):
     """State bank ~N(0, 0.1) (drawn in fp32, stored as ``state_dtype``),
