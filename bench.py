@@ -147,6 +147,53 @@ def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=10):
     return res
 
 
+def attn_kv8_bytes(w, batch):
+    """Algorithmic HBM bytes of one attention layer over INT8 pages: the
+    cached codes, the in-flight bf16 rows and their codes, Q, O, the scales
+    and the block table."""
+    ctx = sum(batch.ctx)
+    T = batch.total_T
+    per_tok = w.Hq * w.D * 2 + 2 * w.Hkv * w.D * 2 + 2 * w.Hkv * w.D + w.Hq * w.D * 2
+    return (ctx * w.Hkv * w.D * 2 + T * per_tok + 2 * w.Hkv * w.D * 4
+            + batch.B * batch.block_table.shape[1] * 4)
+
+
+def attn_kv8_timing(w, batch, sb, ctx, ws, stream, dev, n_layers=16, reps=3):
+    """Attention layers over INT8 pages at the step's shape and contexts, back
+    to back between two events on the launch stream (the append, stream and
+    combine launches of each call)."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    layers = [wl.make_attn_layer_kv8(w, batch, 5000 + i, dev) for i in range(n_layers)]
+    for l in layers:
+        l['out'] = torch.empty_like(l['q'])
+
+    def run(l):
+        bd.spec_verify_attention_kv8(sb, l['q'], l['k_new'], l['v_new'], l['k_cache'],
+                                     l['v_cache'], l['k_scale'], l['v_scale'],
+                                     batch.block_table, ctx, l['out'], workspace=ws,
+                                     stream=stream)
+    for l in layers:
+        run(l)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for l in layers:
+            run(l)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_layers)
+    nbytes = attn_kv8_bytes(w, wl.Batch(**{**batch.__dict__, 'ctx': ctx.tolist()}))
+    del layers
+    return {'layer_ms': round(ms, 4), 'bytes': nbytes,
+            'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1),
+            'frac_of_peak': round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            'launches': reps * n_layers}
+
+
 def measured_traffic():
     """HBM bytes per attention launch (stream kernel + combine kernel) from the
     committed FETCH_SIZE / WRITE_SIZE counter runs, already scaled by the copy
@@ -413,6 +460,7 @@ def main():
 
     conv = short_conv_timing(w, batch, sb, commits[0], stream, dev)
     gdn_sd = gdn_state_dtype_timing(w, batch, sb, commits[0], stream, dev)
+    kv8 = attn_kv8_timing(w, batch, sb, ctx_fixed, ws, stream, dev)
 
     T = batch.total_T
     n_att, n_gdn = len(att_layers), len(gdn_l)
@@ -448,7 +496,7 @@ def main():
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4)},
-        'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd},
+        'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd, 'attention_int8_kv': kv8},
         'mean_accept_len': round(accepted, 3),
         'dtype_detail': 'bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance',
     }

@@ -63,8 +63,8 @@ sv_status check_attn(const sv_batch* batch, const void* q, const void* k_new, co
     return fail(SV_EINVAL, "%s: page_size, max_pages_per_seq, num_pages must be >= 1", who);
   if (dtype == SV_BF16) {
     if (D != 64 && D != 128) return fail(SV_EDTYPE, "%s: bf16 path needs D in {64,128} (got %d)", who, D);
-    if (P < 16 || !(P % 64 == 0 || 64 % P == 0))
-      return fail(SV_EINVAL, "%s: page_size %d must be 16, 32 or a multiple of 64", who, P);
+    if (P < 16 || (P & (P - 1)) != 0)
+      return fail(SV_EINVAL, "%s: page_size %d must be a power of two >= 16", who, P);
     if (batch->B > 2048)
       return fail(SV_ECAPACITY, "%s: the bf16 path takes at most 2048 sequences (got %d)", who,
                   batch->B);

@@ -181,6 +181,10 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   __shared__ int s_scan[kThreads];
   uint16_t* Ks = lds;
   uint16_t* Vt = lds + kKT * KS;
+  // V^T column swizzle: key k of row r sits at column k ^ vswz(r), a multiple
+  // of 4 (8 for INT8) that depends on r / 16 only, so the transposed stores
+  // of a wave spread over the banks and a read of 4 keys stays contiguous
+  auto vswz = [](int r) __attribute__((always_inline)) { return (KV8 ? 8 : 4) * (r >> 4); };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -235,44 +239,60 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   // State of the current piece and chunk (function scope, read by the
   // always-inlined helpers below).
   int b = 0, g = 0, x0 = 0, T = 1, L = 0, M = 1, pos_end = 1, first_page = 0;
+  int last_tile = 0, last_pg = 0;   // of the current chunk
+  const int ps = __builtin_ctz(P);  // the page size is a power of two
+  const int toff = KPT * kb;        // the thread's first key in a tile
   using QF = std::conditional_t<KV8, f16x8_t, bf16x8_t>;
   QF qf[NQT][NKS];
   float4_t oacc[NQT][NDT];
   float m_run[NQT], l_run[NQT];
 
-  // Branch-free tile load: every thread issues the same 2 * KPT loads for
-  // every tile, so the compiler's wait counts stay exact.  A key at or past
-  // pos_end (or in a bad page) reads a valid in-flight row of the sequence
-  // instead: its score is masked, so it gets probability exactly 0, and the
-  // finite values it brings add exactly 0.  Nothing is done to the loaded
-  // values before they are stored to LDS, so no instruction waits on a load
-  // earlier than the tile's own turn in the ring.
+  // Tile load: every thread issues the same 2 * KPT loads for every tile,
+  // so the compiler's wait counts stay exact; the page lookup and address are
+  // computed once per tile (a thread's keys share one page).  A key at or
+  // past pos_end is masked in the scores, so it gets probability exactly 0;
+  // what it reads must only be finite: an in-flight row (bf16) or any code
+  // (INT8).  Nothing is done to the loaded values before they are stored to
+  // LDS, so no instruction waits on a load earlier than the tile's own turn.
   auto load_tile = [&](int tile) __attribute__((always_inline)) {
     TileRegs<KPT> r;
+    // tiles past the chunk (prefetch) re-read its last tile; the thread's
+    // KPT keys share one page (P >= 16 >= KPT and pos is a multiple of KPT)
+    const int tc = min(tile, last_tile);
+    const int pos = tc * kKT + toff;
+    const int pid = s_ids[min((pos >> ps) - first_page, last_pg)];
+    // a bad page reads page 0: the sequence is flagged
+    const size_t base =
+        ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pos & (P - 1))) * D + DPC * dc;
+    if constexpr (KV8) {
+      // every position, in-flight ones included, is read from the pages
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc8 + base + i * D));
+        r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc8 + base + i * D));
+      }
+      return r;
+    }
+    if (tc * kKT + kKT <= L) {  // context keys only (block-uniform)
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc + base + i * D));
+        r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc + base + i * D));
+      }
+      return r;
+    }
+    // in-flight keys come from k_new / v_new (past the end: a valid row,
+    // masked in the scores)
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int p = tile * kKT + KPT * kb + i;
-      const int pc = min(p, pos_end - 1);
-      const int pid = s_ids[pc / P - first_page];
-      if constexpr (KV8) {
-        // every position, in-flight ones included, is read from the pages
-        // (a bad page reads page 0: the sequence is flagged)
-        const size_t off =
-            ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pc % P)) * D + 16 * dc;
-        r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc8 + off));
-        r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc8 + off));
-        continue;
-      }
-      const bool in_ctx = p < L && p < pos_end && pid >= 0;
-      const size_t off_c =
-          ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pc % P)) * D + 8 * dc;
+      const int p = pos + i;
+      const bool in_ctx = p < L && pid >= 0;
       const size_t off_n =
-          (static_cast<size_t>(x0 + min(max(p - L, 0), T - 1)) * Hkv + g) * D + 8 * dc;
-      // streaming loads: every context byte is read once per launch
+          (static_cast<size_t>(x0 + min(max(p - L, 0), T - 1)) * Hkv + g) * D + DPC * dc;
       r.k[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(in_ctx ? kc + off_c : kn + off_n));
+          reinterpret_cast<const u32x4_t*>(in_ctx ? kc + base + i * D : kn + off_n));
       r.v[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(in_ctx ? vc + off_c : vn + off_n));
+          reinterpret_cast<const u32x4_t*>(in_ctx ? vc + base + i * D : vn + off_n));
     }
     return r;
   };
@@ -301,7 +321,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        uint16_t* dst = Vt + (16 * dc + e) * VS + KPT * kb;
+        uint16_t* dst = Vt + (16 * dc + e) * VS + ((KPT * kb) ^ vswz(16 * dc + e));
         if constexpr (KPT == 2) {
           *reinterpret_cast<uint32_t*>(dst) =
               half16(vh[0][e >> 3], e & 7) | (half16(vh[1][e >> 3], e & 7) << 16);
@@ -319,7 +339,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       uint32_t hv[KPT];
 #pragma unroll
       for (int i = 0; i < KPT; ++i) hv[i] = half16(r.v[i], e);
-      uint16_t* dst = Vt + (8 * dc + e) * VS + KPT * kb;
+      uint16_t* dst = Vt + (8 * dc + e) * VS + ((KPT * kb) ^ vswz(8 * dc + e));
       if constexpr (KPT == 4) {
         uint2 pk;
         pk.x = hv[0] | (hv[1] << 16);
@@ -376,14 +396,17 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
           psum += KV8 ? f16_bits_to_f32(hb) : bf16_to_f32(hb);
         }
         l_run[nt] = l_run[nt] * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // skip when no row's max moved
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] *= alpha;
+          for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] *= alpha;
+        }
         m_run[nt] = m_new;
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const short4_t vf =
-            *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS + 16 * w + 4 * lg);
+            *reinterpret_cast<const short4_t*>(Vt + (16 * dt + lr) * VS +
+                                               ((16 * w + 4 * lg) ^ vswz(16 * dt)));
         if constexpr (KV8)
           oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
               __builtin_bit_cast(f16x4_t, vf), __builtin_bit_cast(f16x4_t, pf), oacc[nt][dt], 0, 0,
@@ -476,6 +499,8 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       pos_end = min(c1 * kKT, L + T);  // keys at or past it are masked
       first_page = (c0 * kKT) / P;
       const int n_pages = (pos_end - 1) / P - first_page + 1;
+      last_tile = (pos_end - 1) / kKT;
+      last_pg = n_pages - 1;
       __syncthreads();  // the previous chunk is done with s_ids and the tile LDS
       for (int i = tid; i < n_pages; i += kThreads) {
         int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + first_page + i];

@@ -98,8 +98,8 @@ typedef struct {
  *                last page are never read
  *   ctx_lens     int32 [B]
  *   out          [total_T, Hq, D]           dtype
- * dtype SV_BF16 (fp32 accumulation; D = 64 or 128; page_size 16, 32 or a
- * multiple of 64; Hq/Hkv * max_T <= 64) or SV_F32 (D <= 128).  scale = 0 means
+ * dtype SV_BF16 (fp32 accumulation; D = 64 or 128; page_size a power of two
+ * >= 16; Hq/Hkv * max_T <= 64) or SV_F32 (D <= 128).  scale = 0 means
  * 1/sqrt(D).  Workspace: spec_verify_attention_workspace_bytes(); it holds
  * the split-KV partials (fp32) and is scratch between calls.
  * ------------------------------------------------------------------------ */

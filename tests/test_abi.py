@@ -71,6 +71,7 @@ def test_attention_validation():
     assert call(Hq=30) == bd.SV_EINVAL                       # Hq % Hkv
     assert call(D=96) == bd.SV_EDTYPE                        # bf16 head size
     assert call(P=48) == bd.SV_EINVAL                        # page size
+    assert call(P=192) == bd.SV_EINVAL                       # not a power of two
     assert call(q=None) == bd.SV_EINVAL
     assert call(dt=7) == bd.SV_EDTYPE
     assert call(Hq=64, Hkv=2) == bd.SV_ECAPACITY             # 32 heads x 4 > 64 rows
