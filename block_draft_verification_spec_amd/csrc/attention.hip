@@ -256,10 +256,19 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   // LDS, so no instruction waits on a load earlier than the tile's own turn.
   auto load_tile = [&](int tile) __attribute__((always_inline)) {
     TileRegs<KPT> r;
-    // tiles past the chunk (prefetch) re-read its last tile; the thread's
-    // KPT keys share one page (P >= 16 >= KPT and pos is a multiple of KPT)
-    const int tc = min(tile, last_tile);
-    const int pos = tc * kKT + toff;
+    if (tile > last_tile) {  // prefetch past the chunk, never computed: read
+                             // the sequence's first in-flight row (small, hot)
+      const size_t off_n = (static_cast<size_t>(x0) * Hkv + g) * D + 8 * dc;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kn + off_n));
+        r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vn + off_n));
+      }
+      return r;
+    }
+    // the thread's KPT keys share one page (P >= 16 >= KPT and pos is a
+    // multiple of KPT)
+    const int pos = tile * kKT + toff;
     const int pid = s_ids[min((pos >> ps) - first_page, last_pg)];
     // a bad page reads page 0: the sequence is flagged
     const size_t base =
@@ -273,7 +282,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       }
       return r;
     }
-    if (tc * kKT + kKT <= L) {  // context keys only (block-uniform)
+    if (tile * kKT + kKT <= L) {  // context keys only (block-uniform)
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc + base + i * D));
