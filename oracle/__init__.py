@@ -50,6 +50,8 @@ from .short_conv import CONV_COMMIT_ONLY, CONV_VERIFY_COMMIT, CONV_VERIFY_ONLY, 
 from .kv_int8 import (append_kv_int8, dequantize_pool, dequantize_rows, quantize_int8,
                       verify_attention_int8)
 from .step import verify_step
+from .checkpoint import (conv_checkpoints, conv_commit_prefix, gdn_checkpoints,
+                         gdn_commit_prefix)
 
 __all__ = [
     "append_kv", "gather_context", "verify_attention",
@@ -59,4 +61,5 @@ __all__ = [
     "quantize_int8", "dequantize_rows", "dequantize_pool", "append_kv_int8",
     "verify_attention_int8",
     "verify_step",
+    "gdn_checkpoints", "gdn_commit_prefix", "conv_checkpoints", "conv_commit_prefix",
 ]
