@@ -99,6 +99,18 @@ _SIGS = {
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, _c_i32, _vp, _vp, _vp,
          ctypes.c_int, _c_i32, _vp, _vp, _c_i32, _c_i32, ctypes.POINTER(SvConvPending),
          _vp, _vp], ctypes.c_int),
+    'gdn_verify_checkpoint': (
+        [ctypes.POINTER(SvBatch), _vp, ctypes.c_int, _vp, _c_i32, _vp, _vp, _vp, ctypes.c_int,
+         _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp], ctypes.c_int),
+    'gdn_commit_prefix': (
+        [ctypes.POINTER(SvBatch), _vp, ctypes.c_int, _vp, _c_i32, _vp, _c_i32, _vp, _c_i32,
+         _c_i32, _c_i32, _vp, _vp], ctypes.c_int),
+    'short_conv_verify_checkpoint': (
+        [ctypes.POINTER(SvBatch), _vp, _vp, _c_i32, _vp, _vp, _vp, ctypes.c_int, _c_i32, _vp,
+         _vp, _c_i32, _c_i32, _c_i32, _vp, _vp], ctypes.c_int),
+    'short_conv_commit_prefix': (
+        [ctypes.POINTER(SvBatch), _vp, _vp, _c_i32, _vp, _c_i32, _vp, ctypes.c_int, _c_i32,
+         _c_i32, _vp, _vp], ctypes.c_int),
     'spec_accept_workspace_bytes': ([_c_i32, _c_i32, _c_i32, ctypes.c_int], _sz),
     'spec_accept_args': (
         [ctypes.POINTER(SvBatch), ctypes.POINTER(SvAcceptArgs), _vp, _vp, _vp, _vp, _sz, _vp,
@@ -289,6 +301,56 @@ def short_conv_verify_commit(batch, mode, state, x, weight, bias, commit_len, ou
 
 def make_conv_pending(batch, x, commit_len):
     return SvConvPending(batch, _ptr(x), _i32(commit_len, 'commit_len'))
+
+
+def gdn_verify_checkpoint(batch, state, q, k, v, alpha, beta, out, checkpoints,
+                          state_slot=None, err=None, stream=None):
+    """Verify writing the checkpoint series (``gdn_verify_checkpoint``).
+
+    checkpoints [B, window, H, dv, dk] in the state's dtype; the state bank is
+    read only.
+    """
+    num_slots, H, dv, dk = state.shape
+    if checkpoints.dtype != state.dtype:
+        raise ValueError('checkpoints must have the state dtype')
+    _check(lib().gdn_verify_checkpoint(
+        ctypes.byref(batch), _ptr(state), state_dtype(state), _i32(state_slot, 'state_slot'),
+        num_slots, _ptr(q), _ptr(k), _ptr(v), _dtype(k), _ptr(alpha), _ptr(beta), _ptr(out),
+        _ptr(checkpoints), checkpoints.shape[1], H, dk, dv, _i32(err, 'err'), _stream(stream)))
+
+
+def gdn_commit_prefix(batch, state, checkpoints, commit_len, state_slot=None, err=None,
+                      stream=None):
+    """CommitPrefix over a GatedDeltaNet checkpoint series (``gdn_commit_prefix``)."""
+    num_slots, H, dv, dk = state.shape
+    if checkpoints.dtype != state.dtype:
+        raise ValueError('checkpoints must have the state dtype')
+    _check(lib().gdn_commit_prefix(
+        ctypes.byref(batch), _ptr(state), state_dtype(state), _i32(state_slot, 'state_slot'),
+        num_slots, _ptr(checkpoints), checkpoints.shape[1], _i32(commit_len, 'commit_len'), H,
+        dk, dv, _i32(err, 'err'), _stream(stream)))
+
+
+def short_conv_verify_checkpoint(batch, state, x, weight, bias, out, prefix_states,
+                                 state_slot=None, activation=SV_ACT_NONE, err=None,
+                                 stream=None):
+    """Short-conv verify writing the prefix-state series
+    (``short_conv_verify_checkpoint``); prefix_states [B, window, K-1, C]."""
+    num_slots, Km1, C = state.shape
+    _check(lib().short_conv_verify_checkpoint(
+        ctypes.byref(batch), _ptr(state), _i32(state_slot, 'state_slot'), num_slots, _ptr(x),
+        _ptr(weight), _ptr(bias), _dtype(x), int(activation), _ptr(out), _ptr(prefix_states),
+        prefix_states.shape[1], C, Km1 + 1, _i32(err, 'err'), _stream(stream)))
+
+
+def short_conv_commit_prefix(batch, state, prefix_states, commit_len, state_slot=None,
+                             err=None, stream=None):
+    """CommitPrefix over the conv's prefix-state series (``short_conv_commit_prefix``)."""
+    num_slots, Km1, C = state.shape
+    _check(lib().short_conv_commit_prefix(
+        ctypes.byref(batch), _ptr(state), _i32(state_slot, 'state_slot'), num_slots,
+        _ptr(prefix_states), prefix_states.shape[1], _i32(commit_len, 'commit_len'),
+        _dtype(state), C, Km1 + 1, _i32(err, 'err'), _stream(stream)))
 
 
 def spec_accept_workspace_bytes(B, total_T, V, mode):

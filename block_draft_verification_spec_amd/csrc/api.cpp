@@ -375,6 +375,174 @@ sv_status short_conv_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void
   return hip_status(sv::launch_conv(a, io_dtype, stream), who);
 }
 
+namespace {
+
+constexpr int32_t kMaxWindow = 64;  // checkpoint slots per sequence
+
+sv_status check_window(const sv_batch* batch, int32_t window, const char* who) {
+  if (window < batch->max_T || window > kMaxWindow)
+    return fail(SV_EINVAL, "%s: window must be in max_T..%d (got %d, max_T %d)", who, kMaxWindow,
+                window, batch->max_T);
+  return SV_OK;
+}
+
+sv::GdnScalars gdn_scalars(const sv_batch* batch, int mode, const int32_t* state_slot,
+                           int32_t num_slots, const int32_t* commit_len, int32_t H, int32_t dk,
+                           int32_t dv, int32_t window, int32_t* err) {
+  sv::GdnScalars s{};
+  s.B = batch->B;
+  s.total_T = batch->total_T;
+  s.max_T = batch->max_T;
+  s.cu = batch->cu_seqlens;
+  s.mode = mode;
+  s.state_slot = state_slot;
+  s.num_slots = num_slots;
+  s.commit_len = commit_len;
+  s.H = H;
+  s.dk = dk;
+  s.dv = dv;
+  s.window = window;
+  s.err = err;
+  return s;
+}
+
+sv_status check_conv_common(const sv_batch* batch, const void* state, const int32_t* state_slot,
+                            int32_t num_slots, sv_dtype io_dtype, int32_t C, int32_t K,
+                            const char* who) {
+  sv_status st = check_batch(batch, who);
+  if (st != SV_OK) return st;
+  if (io_dtype != SV_F32 && io_dtype != SV_BF16)
+    return fail(SV_EDTYPE, "%s: unsupported io dtype %d", who, static_cast<int>(io_dtype));
+  if (K < 2 || K > 8) return fail(SV_EINVAL, "%s: K must be in 2..8 (got %d)", who, K);
+  if (C < 1) return fail(SV_EINVAL, "%s: C must be >= 1", who);
+  if (!state) return fail(SV_EINVAL, "%s: state is required", who);
+  if (num_slots < 1) return fail(SV_EINVAL, "%s: num_slots must be >= 1", who);
+  if (!state_slot && num_slots < batch->B)
+    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  return SV_OK;
+}
+
+}  // namespace
+
+sv_status gdn_verify_checkpoint(const sv_batch* batch, const void* state, sv_dtype state_dtype,
+                                const int32_t* state_slot, int32_t num_slots, const void* q,
+                                const void* k, const void* v, sv_dtype io_dtype,
+                                const float* alpha, const float* beta, void* out,
+                                void* checkpoints, int32_t window, int32_t H, int32_t dk,
+                                int32_t dv, int32_t* err, hipStream_t stream) {
+  const char* who = "gdn_verify_checkpoint";
+  sv_status st = check_gdn_common(batch, const_cast<void*>(state), state_dtype, num_slots,
+                                  io_dtype, H, dk, dv, who);
+  if (st != SV_OK) return st;
+  st = check_window(batch, window, who);
+  if (st != SV_OK) return st;
+  if (!q || !k || !v || !alpha || !beta || !out || !checkpoints)
+    return fail(SV_EINVAL, "%s: q, k, v, alpha, beta, out and checkpoints are required", who);
+  if (reinterpret_cast<uintptr_t>(checkpoints) & 15)
+    return fail(SV_EINVAL, "%s: checkpoints must be 16-byte aligned", who);
+  if (!state_slot && num_slots < batch->B)
+    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  const sv::GdnScalars s = gdn_scalars(batch, SV_GDN_VERIFY_ONLY, state_slot, num_slots, nullptr,
+                                       H, dk, dv, window, err);
+  sv::GdnFullPtrs p{};
+  p.state = const_cast<void*>(state);  // read only: VERIFY_ONLY without pending tokens
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.out = out;
+  p.ckpt = checkpoints;
+  return hip_status(sv::launch_gdn(s, p, io_dtype, state_dtype, stream), who);
+}
+
+sv_status gdn_commit_prefix(const sv_batch* batch, void* state, sv_dtype state_dtype,
+                            const int32_t* state_slot, int32_t num_slots, const void* checkpoints,
+                            int32_t window, const int32_t* commit_len, int32_t H, int32_t dk,
+                            int32_t dv, int32_t* err, hipStream_t stream) {
+  const char* who = "gdn_commit_prefix";
+  sv_status st =
+      check_gdn_common(batch, state, state_dtype, num_slots, SV_F32, H, dk, dv, who);
+  if (st != SV_OK) return st;
+  st = check_window(batch, window, who);
+  if (st != SV_OK) return st;
+  if (!checkpoints || !commit_len)
+    return fail(SV_EINVAL, "%s: checkpoints and commit_len are required", who);
+  if (reinterpret_cast<uintptr_t>(checkpoints) & 15)
+    return fail(SV_EINVAL, "%s: checkpoints must be 16-byte aligned", who);
+  if (!state_slot && num_slots < batch->B)
+    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  const sv::GdnScalars s = gdn_scalars(batch, SV_GDN_COMMIT_ONLY, state_slot, num_slots,
+                                       commit_len, H, dk, dv, window, err);
+  return hip_status(sv::launch_gdn_commit_prefix(s, checkpoints, state, state_dtype, stream), who);
+}
+
+sv_status short_conv_verify_checkpoint(const sv_batch* batch, const void* state,
+                                       const int32_t* state_slot, int32_t num_slots,
+                                       const void* x, const float* weight, const float* bias,
+                                       sv_dtype io_dtype, int32_t activation, void* out,
+                                       void* prefix_states, int32_t window, int32_t C, int32_t K,
+                                       int32_t* err, hipStream_t stream) {
+  const char* who = "short_conv_verify_checkpoint";
+  sv_status st = check_conv_common(batch, state, state_slot, num_slots, io_dtype, C, K, who);
+  if (st != SV_OK) return st;
+  st = check_window(batch, window, who);
+  if (st != SV_OK) return st;
+  if (activation != SV_ACT_NONE && activation != SV_ACT_SILU)
+    return fail(SV_EINVAL, "%s: unknown activation %d", who, activation);
+  if (!x || !weight || !out || !prefix_states)
+    return fail(SV_EINVAL, "%s: x, weight, out and prefix_states are required", who);
+  sv::ConvArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.mode = SV_GDN_VERIFY_ONLY;
+  a.state_slot = state_slot;
+  a.num_slots = num_slots;
+  a.C = C;
+  a.K = K;
+  a.activation = activation;
+  a.state = const_cast<void*>(state);  // read only: VERIFY_ONLY without pending tokens
+  a.x = x;
+  a.weight = weight;
+  a.bias = bias;
+  a.out = out;
+  a.series = prefix_states;
+  a.window = window;
+  a.err = err;
+  return hip_status(sv::launch_conv(a, io_dtype, stream), who);
+}
+
+sv_status short_conv_commit_prefix(const sv_batch* batch, void* state, const int32_t* state_slot,
+                                   int32_t num_slots, const void* prefix_states, int32_t window,
+                                   const int32_t* commit_len, sv_dtype io_dtype, int32_t C,
+                                   int32_t K, int32_t* err, hipStream_t stream) {
+  const char* who = "short_conv_commit_prefix";
+  sv_status st = check_conv_common(batch, state, state_slot, num_slots, io_dtype, C, K, who);
+  if (st != SV_OK) return st;
+  st = check_window(batch, window, who);
+  if (st != SV_OK) return st;
+  if (!prefix_states || !commit_len)
+    return fail(SV_EINVAL, "%s: prefix_states and commit_len are required", who);
+  sv::ConvArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.mode = SV_GDN_COMMIT_ONLY;
+  a.state_slot = state_slot;
+  a.num_slots = num_slots;
+  a.commit_len = commit_len;
+  a.C = C;
+  a.K = K;
+  a.state = state;
+  a.series = const_cast<void*>(prefix_states);
+  a.window = window;
+  a.err = err;
+  return hip_status(sv::launch_conv_commit_prefix(a, io_dtype, stream), who);
+}
+
 size_t spec_accept_workspace_bytes(int32_t B, int32_t total_T, int32_t V, sv_accept_mode mode) {
   if (B < 1 || total_T < 1 || V < 1) return 0;
   return sv::accept_workspace_bytes(B, total_T, V, mode);

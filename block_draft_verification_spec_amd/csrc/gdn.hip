@@ -131,13 +131,16 @@ struct GdnSmem {
 // COMMIT_ONLY_NP: compile-time COMMIT_ONLY without pending tokens (the
 // batched commit of the two-phase step); q, out and the pending pointers are
 // then never touched.
-template <typename IO, typename ST, int DK, bool COMMIT_ONLY_NP>
+// CKPT: verify (mode VERIFY_ONLY, no pending) that also writes the state after
+// every token into the checkpoint series, end-aligned: token i of a T-token
+// sequence goes to slot window - T + i of ckpt [B][window][H][dv][dk].
+template <typename IO, typename ST, int DK, bool COMMIT_ONLY_NP, bool CKPT = false>
 __device__ __forceinline__ void gdn_tile(
     GdnSmem<DK>& sm, const GdnScalars& s, void* __restrict__ state, const void* q,
     const void* k, const void* v, const float* __restrict__ alpha,
     const float* __restrict__ beta, void* out, const void* pk, const void* pv,
     const float* __restrict__ palpha, const float* __restrict__ pbeta, int b,
-    int h, int rb, bool report) {
+    int h, int rb, bool report, void* __restrict__ ckpt = nullptr) {
   using L = io<IO>;
   constexpr int NV4 = DK / 32;  // float4 per row per thread
   auto& k_s = sm.k_s;
@@ -342,6 +345,18 @@ __device__ __forceinline__ void gdn_tile(
                            g * sr[r][j].z, g * sr[r][j].w);
       }
     }
+    if constexpr (CKPT) {
+      ST* ctile = static_cast<ST*>(ckpt) +
+                  ((static_cast<size_t>(b) * s.window + (s.window - T + i)) * H + h) * DV * DK;
+#pragma unroll
+      for (int r = 0; r < kRowsPerThread; ++r) {
+        ST* rowp = ctile + static_cast<size_t>(row0 + rg + kRowStride * r) * DK;
+#pragma unroll
+        for (int j = 0; j < NV4; ++j)
+          store_state4<ST>(rowp + 32 * j + 4 * cl, g * sr[r][j].x, g * sr[r][j].y,
+                           g * sr[r][j].z, g * sr[r][j].w);
+      }
+    }
   }
 
   if (verify) {
@@ -353,12 +368,45 @@ __device__ __forceinline__ void gdn_tile(
   }
 }
 
-template <typename IO, typename ST, int DK>
+template <typename IO, typename ST, int DK, bool CKPT>
 __global__ __launch_bounds__(kThreads) void gdn_kernel(GdnScalars s, GdnFullPtrs p) {
   __shared__ GdnSmem<DK> sm;
   const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  gdn_tile<IO, ST, DK, false>(sm, s, p.state, p.q, p.k, p.v, p.alpha, p.beta, p.out, p.pk,
-                   p.pv, p.palpha, p.pbeta, b, h, rb, rb == 0 && h == 0);
+  gdn_tile<IO, ST, DK, false, CKPT>(sm, s, p.state, p.q, p.k, p.v, p.alpha, p.beta, p.out,
+                                    p.pk, p.pv, p.palpha, p.pbeta, b, h, rb,
+                                    rb == 0 && h == 0, p.ckpt);
+}
+
+// CommitPrefix over the checkpoint series: the slot of the accepted prefix
+// becomes the state (c_b = 0 keeps it).  One workgroup per (head, sequence),
+// a plain 16-byte copy of the dv x dk tile.
+template <typename ST>
+__global__ __launch_bounds__(256) void gdn_commit_prefix_kernel(GdnScalars s, const void* ckpt,
+                                                                void* state) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const bool report = h == 0 && tid == 0;
+  const int x0 = s.cu[b];
+  const int T = s.cu[b + 1] - x0;
+  if (T < 1 || T > s.max_T || x0 < 0 || x0 + T > s.total_T) {
+    if (report) flag_error(s.err, SV_DERR_SEQLEN);
+    return;
+  }
+  const int slot = s.state_slot ? s.state_slot[b] : b;
+  if (slot < 0 || slot >= s.num_slots) {
+    if (report) flag_error(s.err, SV_DERR_SLOT);
+    return;
+  }
+  const int c = s.commit_len[b];
+  if (c < 0 || c > T) {
+    if (report) flag_error(s.err, SV_DERR_COMMIT);
+    return;
+  }
+  if (c == 0) return;
+  const size_t n16 = static_cast<size_t>(s.dv) * s.dk * sizeof(ST) / 16;
+  const uint4* src = static_cast<const uint4*>(ckpt) +
+                     ((static_cast<size_t>(b) * s.window + (s.window - T + c - 1)) * s.H + h) * n16;
+  uint4* dst = static_cast<uint4*>(state) + (static_cast<size_t>(slot) * s.H + h) * n16;
+  for (size_t i = tid; i < n16; i += 256) dst[i] = src[i];
 }
 
 template <typename IO, typename ST, int DK>
@@ -377,10 +425,17 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_multi_kernel(GdnScalars s
 template <typename IO, typename ST>
 void launch_gdn_t(const GdnScalars& s, const GdnFullPtrs& p, hipStream_t stream) {
   const dim3 grid(s.dv / kRowsPerBlock, s.H, s.B);
-  if (s.dk == 128)
-    hipLaunchKernelGGL((gdn_kernel<IO, ST, 128>), grid, dim3(kThreads), 0, stream, s, p);
-  else
-    hipLaunchKernelGGL((gdn_kernel<IO, ST, 64>), grid, dim3(kThreads), 0, stream, s, p);
+  if (p.ckpt) {
+    if (s.dk == 128)
+      hipLaunchKernelGGL((gdn_kernel<IO, ST, 128, true>), grid, dim3(kThreads), 0, stream, s, p);
+    else
+      hipLaunchKernelGGL((gdn_kernel<IO, ST, 64, true>), grid, dim3(kThreads), 0, stream, s, p);
+  } else {
+    if (s.dk == 128)
+      hipLaunchKernelGGL((gdn_kernel<IO, ST, 128, false>), grid, dim3(kThreads), 0, stream, s, p);
+    else
+      hipLaunchKernelGGL((gdn_kernel<IO, ST, 64, false>), grid, dim3(kThreads), 0, stream, s, p);
+  }
 }
 
 template <typename IO, typename ST>
@@ -421,6 +476,18 @@ hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
     if (h) launch_commit_t<float, _Float16>(s, t, n_layers, stream);
     else launch_commit_t<float, float>(s, t, n_layers, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_commit_prefix(const GdnScalars& s, const void* ckpt, void* state,
+                                    sv_dtype state_dt, hipStream_t stream) {
+  const dim3 grid(s.H, s.B);
+  if (state_dt == SV_F16)
+    hipLaunchKernelGGL(gdn_commit_prefix_kernel<_Float16>, grid, dim3(256), 0, stream, s, ckpt,
+                       state);
+  else
+    hipLaunchKernelGGL(gdn_commit_prefix_kernel<float>, grid, dim3(256), 0, stream, s, ckpt,
+                       state);
   return hipGetLastError();
 }
 

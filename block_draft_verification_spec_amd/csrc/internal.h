@@ -25,6 +25,7 @@ struct GdnScalars {
   int p_total_T, p_max_T;
   const int32_t* p_cu;          // [B+1]
   const int32_t* p_commit;      // [B]
+  int window;                   // checkpoint series slots (checkpoint calls)
   int32_t* err;
 };
 
@@ -46,9 +47,13 @@ struct ConvArgs {
   const int32_t* p_cu;          // [B+1]
   const int32_t* p_commit;      // [B]
   const void* px;               // [p_total_T][C]
+  void* series;                 // [B][window][K-1][C] prefix states, or null
+  int window;
   int32_t* err;
 };
 hipError_t launch_conv(const ConvArgs& a, sv_dtype io_dtype, hipStream_t stream);
+// CommitPrefix of the conv: state[slot_b] = series[b][c_b - 1] where c_b >= 1.
+hipError_t launch_conv_commit_prefix(const ConvArgs& a, sv_dtype io_dtype, hipStream_t stream);
 
 struct GdnFullPtrs {
   void* state;                  // fp32 or fp16 [num_slots][H][dv][dk]
@@ -56,6 +61,7 @@ struct GdnFullPtrs {
   const float* alpha; const float* beta;
   void* out;
   const void* pk; const void* pv; const float* palpha; const float* pbeta;
+  void* ckpt;                   // checkpoint series [B][window][H][dv][dk], or null
 };
 
 struct GdnCommitPtrs {
@@ -70,6 +76,9 @@ struct GdnCommitTable {
 
 hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io,
                       sv_dtype state_dtype, hipStream_t stream);
+// CommitPrefix: state[slot_b] = ckpt[b][window - T_b + c_b - 1] where c_b >= 1.
+hipError_t launch_gdn_commit_prefix(const GdnScalars& s, const void* ckpt, void* state,
+                                    sv_dtype state_dtype, hipStream_t stream);
 // COMMIT_ONLY over n_layers (<= kGdnLayersPerLaunch) layers in one launch.
 hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
                                    int n_layers, sv_dtype io, sv_dtype state_dtype,

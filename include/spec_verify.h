@@ -300,6 +300,50 @@ SV_API sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode,
     int32_t* err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Checkpoint-series commit (the pages' other rollback, for comparison with
+ * the replay commit above).
+ *
+ * onnxruntime-genai #2457, commit messages on the per-token state series and
+ * CommitPrefix: during the step the operators publish the state after every
+ * token into a window of `window` slots (window >= max_T) per sequence;
+ * GatedDeltaNet writes slot window - 1 after the last token (token j of a
+ * T_b-token sequence -> slot window - T_b + j), the short convolution writes
+ * slot j after local token j.  After acceptance, CommitPrefix copies the
+ * slot of the accepted prefix (c_b tokens kept; c_b = 0 keeps the state)
+ * into the sequence's state slot.  Slots no token maps to are not written.
+ * The verify calls leave the state bank untouched and take no pending
+ * tokens; outputs are those of VERIFY_ONLY.
+ *
+ *   checkpoints    [B, window, H, dv, dk] in state_dtype
+ *   prefix_states  [B, window, K-1, C] in io_dtype
+ * Other arguments as for gdn_verify_commit / short_conv_verify_commit.
+ * Device errors: SEQLEN, SLOT and (CommitPrefix) COMMIT bits; the sequence
+ * is skipped.
+ * ------------------------------------------------------------------------ */
+SV_API sv_status gdn_verify_checkpoint(const sv_batch* batch,
+    const void* state, sv_dtype state_dtype, const int32_t* state_slot, int32_t num_slots,
+    const void* q, const void* k, const void* v, sv_dtype io_dtype,
+    const float* alpha, const float* beta, void* out,
+    void* checkpoints, int32_t window, int32_t H, int32_t dk, int32_t dv,
+    int32_t* err, hipStream_t stream);
+
+SV_API sv_status gdn_commit_prefix(const sv_batch* batch,
+    void* state, sv_dtype state_dtype, const int32_t* state_slot, int32_t num_slots,
+    const void* checkpoints, int32_t window, const int32_t* commit_len,
+    int32_t H, int32_t dk, int32_t dv, int32_t* err, hipStream_t stream);
+
+SV_API sv_status short_conv_verify_checkpoint(const sv_batch* batch,
+    const void* state, const int32_t* state_slot, int32_t num_slots,
+    const void* x, const float* weight, const float* bias, sv_dtype io_dtype,
+    int32_t activation, void* out, void* prefix_states, int32_t window,
+    int32_t C, int32_t K, int32_t* err, hipStream_t stream);
+
+SV_API sv_status short_conv_commit_prefix(const sv_batch* batch,
+    void* state, const int32_t* state_slot, int32_t num_slots,
+    const void* prefix_states, int32_t window, const int32_t* commit_len,
+    sv_dtype io_dtype, int32_t C, int32_t K, int32_t* err, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * The whole step over a hybrid stack, in dependency order (lmdeploy #5019:
  * target pass, then the speculative round whose recurrent-state commit runs
  * after acceptance):

@@ -162,6 +162,37 @@ def test_short_conv_validation():
     assert call(mode=7) == bd.SV_EINVAL
 
 
+def test_checkpoint_validation():
+    L = bd.lib()
+    b = _batch()                                             # max_T = 4
+
+    def gv(window=4, ck=16, sdt=bd.SV_F32, out=16):
+        return L.gdn_verify_checkpoint(ctypes.byref(b), 16, sdt, None, 2, 16, 16, 16, bd.SV_BF16,
+                                       16, 16, out, ck, window, 4, 128, 128, None, None)
+    assert gv(window=3) == bd.SV_EINVAL                      # window < max_T
+    assert 'window' in L.sv_last_error().decode()
+    assert gv(window=65) == bd.SV_EINVAL
+    assert gv(ck=None) == bd.SV_EINVAL
+    assert gv(ck=20) == bd.SV_EINVAL                         # misaligned series
+    assert gv(out=None) == bd.SV_EINVAL
+    assert gv(sdt=bd.SV_BF16) == bd.SV_EDTYPE
+
+    def gc(window=4, commit=16):
+        return L.gdn_commit_prefix(ctypes.byref(b), 16, bd.SV_F32, None, 2, 16, window, commit,
+                                   4, 128, 128, None, None)
+    assert gc(commit=None) == bd.SV_EINVAL
+    assert gc(window=2) == bd.SV_EINVAL
+
+    def cv(window=4, ps=16, K=4):
+        return L.short_conv_verify_checkpoint(ctypes.byref(b), 16, None, 2, 16, 16, None,
+                                              bd.SV_BF16, 0, 16, ps, window, 64, K, None, None)
+    assert cv(ps=None) == bd.SV_EINVAL
+    assert cv(window=1) == bd.SV_EINVAL
+    assert cv(K=9) == bd.SV_EINVAL
+    assert L.short_conv_commit_prefix(ctypes.byref(b), 16, None, 2, 16, 4, None, bd.SV_BF16, 64,
+                                      4, None, None) == bd.SV_EINVAL
+
+
 def test_accept_validation():
     L = bd.lib()
     b = _batch()
