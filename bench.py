@@ -147,6 +147,69 @@ def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=10):
     return res
 
 
+def checkpoint_timing(w, batch, sb, commit, stream, dev, reps=10):
+    """The checkpoint-series commit of the pages against the replay commit:
+    per GDN layer (fp32 state) and per short-conv layer, the verify that
+    writes the per-token series plus CommitPrefix of the accepted slot.  Four
+    independent layers are cycled."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    W = batch.max_T
+    T = batch.total_T
+    kept = int((commit > 0).sum().item())
+    res = {'window': W}
+
+    def timed(layers, run):
+        for l in layers:
+            run(l)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for l in layers:
+                run(l)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(layers))
+
+    gl = [wl.make_gdn_layer(w, batch, 6000 + i, dev) for i in range(4)]
+    for l in gl:
+        l['out'] = torch.empty_like(l['v'])
+        l['ck'] = torch.empty((batch.B, W, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+
+    def run_g(l):
+        bd.gdn_verify_checkpoint(sb, l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'],
+                                 l['out'], l['ck'], stream=stream)
+        bd.gdn_commit_prefix(sb, l['state'], l['ck'], commit, stream=stream)
+    ms = timed(gl, run_g)
+    tile = w.H * w.dv * w.dk * 4
+    nbytes = (batch.B * tile + T * tile + 2 * kept * tile + T * w.H * (2 * w.dk + 2 * w.dv) * 2
+              + T * w.H * 8)
+    res['gdn_layer'] = {'layer_ms': round(ms, 4), 'bytes': nbytes,
+                        'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del gl
+    cl = [wl.make_conv_layer(w, batch, 7000 + i, dev) for i in range(4)]
+    for c in cl:
+        c['out'] = torch.empty_like(c['x'])
+        c['ps'] = torch.empty((batch.B, W) + tuple(c['state'].shape[1:]), dtype=c['state'].dtype,
+                              device=dev)
+
+    def run_c(c):
+        bd.short_conv_verify_checkpoint(sb, c['state'], c['x'], c['weight'], c['bias'], c['out'],
+                                        c['ps'], activation=bd.SV_ACT_SILU, stream=stream)
+        bd.short_conv_commit_prefix(sb, c['state'], c['ps'], commit, stream=stream)
+    ms = timed(cl, run_c)
+    row = (w.conv_K - 1) * w.conv_C * 2
+    nbytes = (batch.B * row + T * row + 2 * kept * row + 2 * T * w.conv_C * 2
+              + w.conv_C * (w.conv_K + 1) * 4)
+    res['conv_layer'] = {'layer_ms': round(ms, 4), 'bytes': nbytes,
+                         'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del cl
+    return res
+
+
 def attn_kv8_bytes(w, batch):
     """Algorithmic HBM bytes of one attention layer over INT8 pages: the
     cached codes, the in-flight bf16 rows and their codes, Q, O, the scales
@@ -461,6 +524,7 @@ def main():
     conv = short_conv_timing(w, batch, sb, commits[0], stream, dev)
     gdn_sd = gdn_state_dtype_timing(w, batch, sb, commits[0], stream, dev)
     kv8 = attn_kv8_timing(w, batch, sb, ctx_fixed, ws, stream, dev)
+    ckpt = checkpoint_timing(w, batch, sb, commits[0], stream, dev)
 
     T = batch.total_T
     n_att, n_gdn = len(att_layers), len(gdn_l)
@@ -496,7 +560,8 @@ def main():
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4)},
-        'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd, 'attention_int8_kv': kv8},
+        'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd, 'attention_int8_kv': kv8,
+                      'checkpoint_commit': ckpt},
         'mean_accept_len': round(accepted, 3),
         'dtype_detail': 'bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance',
     }
