@@ -213,3 +213,80 @@ def test_deferred_schedule_equals_two_phase(state_dtype):
                                     np64(l['alpha']), np64(l['beta']), npi(batch.cu_seqlens),
                                     npi(t2['commit']), oracle.GDN_COMMIT_ONLY)
             check_gdn_state(np64(l['state']), S2, tol=tol)
+
+
+def test_step_with_int8_kv_pages():
+    """The step's attention layers over INT8 pages (kv_format = SV_KV_INT8):
+    acceptance, commit lengths and ctx_lens bit-exact, attention outputs and
+    written codes against the INT8 oracle, GDN outputs and committed states
+    against the GDN oracle (two-phase schedule)."""
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1)})
+    batch = wl.make_batch(w, 17, DEV)
+    layers = []
+    for i, kind in enumerate(w.layers):
+        if kind == 'attn':
+            lay = wl.make_attn_layer_kv8(w, batch, 1700 + 10 * i, DEV)
+            lay['out'] = torch.full_like(lay['q'], float('nan'))
+        else:
+            lay = wl.make_gdn_layer(w, batch, 1700 + 10 * i, DEV)
+            lay['out'] = torch.full_like(lay['v'], float('nan'))
+        lay['kind'] = kind
+        layers.append(lay)
+    acc = wl.make_accept(w, batch, 1799, 'rejection', DEV)
+    before = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in l.items()}
+              for l in layers]
+    args = bd.StepArgs(
+        [1 if l['kind'] == 'attn' else 0 for l in layers],
+        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table,
+                       bd.SV_BF16, kv_format=bd.SV_KV_INT8),
+        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'],
+                       l['k_scale'], l['v_scale']) for l in layers if l['kind'] == 'attn'],
+        bd.gdn_config(w.H, w.dk, w.dv, batch.B, bd.SV_BF16),
+        [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'], l['out'])
+         for l in layers if l['kind'] == 'gdn'],
+        bd.accept_args(bd.SV_ACCEPT_REJECTION, acc['target_logits'], acc['draft_tokens'],
+                       acc['draft_logits'], acc['u_accept'], acc['u_final']))
+    sb = sv_batch(batch)
+    ws = torch.zeros(bd.spec_verify_step_workspace_bytes(sb, args), dtype=torch.uint8, device=DEV)
+    result = torch.full((batch.B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
+    commit = torch.full((batch.B,), -7, dtype=torch.int32, device=DEV)
+    ctx = batch.ctx_lens.clone()
+    err = err_word()
+    say('step with INT8 KV pages')
+    bd.spec_verify_step(sb, args, ctx, result, commit, workspace=ws, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    a_ref, o_ref = oracle.rejection_accept(np64(acc['target_logits']), np64(acc['draft_logits']),
+                                           npi(acc['draft_tokens']), np64(acc['u_accept']),
+                                           np64(acc['u_final']), npi(batch.cu_seqlens),
+                                           batch.max_T)
+    r = npi(result)
+    np.testing.assert_array_equal(r[:batch.B], a_ref)
+    np.testing.assert_array_equal(r[batch.B:].reshape(batch.B, -1), o_ref)
+    np.testing.assert_array_equal(npi(commit), a_ref + 1)
+    np.testing.assert_array_equal(npi(ctx), npi(batch.ctx_lens) + a_ref + 1)
+    cu, table, ctx0 = npi(batch.cu_seqlens), npi(batch.block_table), npi(batch.ctx_lens)
+    for l, b0 in zip(layers, before):
+        if l['kind'] == 'attn':
+            ks, vs = b0['k_scale'].cpu().numpy(), b0['v_scale'].cpu().numpy()
+            ref = oracle.verify_attention_int8(
+                np64(b0['q']), b0['k_new'].float().cpu().numpy(),
+                b0['v_new'].float().cpu().numpy(), b0['k_cache'].cpu().numpy(),
+                b0['v_cache'].cpu().numpy(), ks, vs, table, ctx0, cu, batch.P)
+            check_attn_out(np64(l['out']), ref, torch.bfloat16)
+            k_exp, v_exp = oracle.append_kv_int8(
+                b0['k_cache'].cpu().numpy(), b0['v_cache'].cpu().numpy(),
+                b0['k_new'].float().cpu().numpy(), b0['v_new'].float().cpu().numpy(), ks, vs,
+                table, ctx0, cu, batch.P)
+            assert np.array_equal(l['k_cache'].cpu().numpy(), k_exp)
+            assert np.array_equal(l['v_cache'].cpu().numpy(), v_exp)
+        else:
+            o, _ = oracle.gdn_step(np64(b0['state']), None, np64(b0['q']), np64(b0['k']),
+                                   np64(b0['v']), np64(b0['alpha']), np64(b0['beta']), cu, None,
+                                   oracle.GDN_VERIFY_ONLY)
+            check_gdn_out(np64(l['out']), o, torch.bfloat16)
+            _, S = oracle.gdn_step(np64(b0['state']), None, None, np64(b0['k']), np64(b0['v']),
+                                   np64(b0['alpha']), np64(b0['beta']), cu, a_ref + 1,
+                                   oracle.GDN_COMMIT_ONLY)
+            check_gdn_state(np64(l['state']), S)
