@@ -103,18 +103,19 @@ def short_conv_timing(w, batch, sb, commit, stream, dev, reps=20):
             'schedule': 'deferred (pending replay + verify)'}
 
 
-def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=10):
+def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=4):
     """One GDN layer, deferred schedule (replay the previous step's accepted
     tokens, verify this step's), with the state bank stored as fp32 and as
-    fp16 (fp32 arithmetic either way).  Four independent layers are cycled so
-    the timing is not an L2 replay."""
+    fp16 (fp32 arithmetic either way).  Sixteen independent layers are
+    cycled: their 2.1 GB of fp32 state is far beyond the last-level cache,
+    as in the step."""
     import torch
 
     import workloads as wl
     from block_draft_verification_spec_amd import binding as bd
     res = {}
     for name, sdt in (('fp32_state', torch.float32), ('fp16_state', torch.float16)):
-        layers = [wl.make_gdn_layer(w, batch, 4000 + i, dev, state_dtype=sdt) for i in range(4)]
+        layers = [wl.make_gdn_layer(w, batch, 4000 + i, dev, state_dtype=sdt) for i in range(16)]
         for l in layers:
             l['out'] = torch.empty_like(l['v'])
             l['pend'] = bd.make_gdn_pending(sb, l['k'], l['v'], l['alpha'], l['beta'], commit)
