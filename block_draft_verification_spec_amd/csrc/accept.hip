@@ -36,6 +36,35 @@ constexpr int kPerThread = kChunk / kThreads;
 
 __host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
+// exp(x) for x <= 0 in fp64 for the per-entry work, by the table-driven
+// method of P. T. P. Tang (ACM TOMS 15(2), 1989): with k the integer nearest
+// to x * 256 / ln 2 and r = x - k ln2 / 256 (|r| <= ln2 / 512, taken in two
+// fma steps with ln 2 split into a double and its remainder),
+//   exp(x) = 2^(k >> 8) * 2^((k & 255) / 256) * (1 + p(r)),
+// p the degree-5 Taylor polynomial of exp(r) - 1 (remainder below 1e-20
+// relative).  The 256 table entries are filled per block with exp2.
+constexpr int kExpTab = 256;
+
+__device__ __forceinline__ void exp_table_init(double* tab) {
+  for (int j = threadIdx.x; j < kExpTab; j += blockDim.x)
+    tab[j] = exp2(static_cast<double>(j) / kExpTab);
+}
+
+__device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
+  if (!(x > -745.0)) return 0.0;                    // below the smallest subnormal; -inf
+  constexpr double kInvStep = 256.0 / 0.693147180559945309417232121458176568;
+  constexpr double kStepHi = 0x1.62e42fefa39efp-1 / 256.0;   // ln 2 rounded to double, / 256
+  constexpr double kStepLo = 2.319046813846299558e-17 / 256.0;  // ln 2 minus that double, / 256
+  const double k = rint(x * kInvStep);
+  double r = fma(-k, kStepHi, x);
+  r = fma(-k, kStepLo, r);
+  const int ki = static_cast<int>(k);
+  const double pr =
+      r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0 + r * (1.0 / 120.0)))));
+  const double t = tab[ki & (kExpTab - 1)];
+  return ldexp(fma(t, pr, t), ki >> 8);
+}
+
 // Workspace layout (byte offsets are 256-aligned).
 struct AcceptWs {
   size_t keys, stats, dec, fin, csum, total;
@@ -203,6 +232,8 @@ __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
   }
   __shared__ float redm[kThreads / 64];
   __shared__ double reds[kThreads / 64];
+  __shared__ double tab[kExpTab];
+  exp_table_init(tab);
   m = wave_max_f32(m);
   if ((tid & 63) == 0) redm[tid >> 6] = m;
   __syncthreads();
@@ -212,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
   if (m > -INFINITY) {
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e)
-      if (vals[e] > -INFINITY) s += exp(static_cast<double>(vals[e]) - static_cast<double>(m));
+      if (vals[e] > -INFINITY) s += exp_nonpos(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
   }
   s = wave_sum_f64(s);
   if ((tid & 63) == 0) reds[tid >> 6] = s;
@@ -304,14 +335,20 @@ __global__ __launch_bounds__(64) void decide_reject(AcceptArgs a) {
   }
 }
 
-// Weight of vocabulary entry y for the final draw of a sequence.
+// Weight of vocabulary entry y for the final draw of a sequence; rz holds the
+// reciprocals of the two normalisers (f.y, f.w).
 template <typename T>
 __device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int rt, int rd,
-                                              const double4& f, int y) {
-  const double p = exp(static_cast<double>(ld<T>(a.target, static_cast<size_t>(rt) * a.V + y)) - f.x) / f.y;
+                                              const double4& f, const double2& rz, int y,
+                                              const double* tab) {
+  const double p =
+      exp_nonpos(static_cast<double>(ld<T>(a.target, static_cast<size_t>(rt) * a.V + y)) - f.x,
+                 tab) * rz.x;
   if (kind == 0) return p;
   if (kind == 2) return y == rd ? 0.0 : p;  // point-mass draft at rd
-  const double q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(rd) * a.V + y)) - f.z) / f.w;
+  const double q =
+      exp_nonpos(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(rd) * a.V + y)) - f.z,
+                 tab) * rz.y;
   return fmax(p - q, 0.0);
 }
 
@@ -322,11 +359,15 @@ __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
   const int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
   if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
+  const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
+  __shared__ double tab[kExpTab];
+  exp_table_init(tab);
+  __syncthreads();
   double s = 0.0;
 #pragma unroll 4
   for (int e = 0; e < kPerThread; ++e) {
     const int y = chunk * kChunk + e * kThreads + tid;
-    if (y < a.V) s += draw_weight<T>(a, d.y, d.z, d.w, f, y);
+    if (y < a.V) s += draw_weight<T>(a, d.y, d.z, d.w, f, rz, y, tab);
   }
   s = wave_sum_f64(s);
   __shared__ double red[kThreads / 64];
@@ -345,7 +386,8 @@ __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
 // each thread owns kPerThread consecutive entries.
 template <typename T>
 __device__ int chunk_search(const AcceptArgs& a, int kind, int rt, int rd, const double4& f,
-                            int chunk, double base, double t, int* last_pos) {
+                            const double2& rz, const double* tab, int chunk, double base,
+                            double t, int* last_pos) {
   const int tid = threadIdx.x;
   __shared__ double pre[kThreads];
   __shared__ int found;
@@ -356,7 +398,7 @@ __device__ int chunk_search(const AcceptArgs& a, int kind, int rt, int rd, const
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int y = y0 + e;
-    w[e] = y < a.V ? draw_weight<T>(a, kind, rt, rd, f, y) : 0.0;
+    w[e] = y < a.V ? draw_weight<T>(a, kind, rt, rd, f, rz, y, tab) : 0.0;
     s += w[e];
   }
   pre[tid] = s;
@@ -396,6 +438,9 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
   if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
+  const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
+  __shared__ double tab[kExpTab];
+  exp_table_init(tab);
   const int nc = n_chunks(a.V);
   double* csum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum) + static_cast<size_t>(b) * nc;
   __shared__ double total_s;
@@ -414,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
       double s = 0.0;
       for (int e = 0; e < kPerThread; ++e) {
         const int y = c * kChunk + e * kThreads + tid;
-        if (y < a.V) s += draw_weight<T>(a, 0, d.z, d.w, f, y);
+        if (y < a.V) s += draw_weight<T>(a, 0, d.z, d.w, f, rz, y, tab);
       }
       s = wave_sum_f64(s);
       __shared__ double red[kThreads / 64];
@@ -462,12 +507,12 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
     for (int c = nc - 1; c >= 0 && y < 0; --c) {
       if (!(csum[c] > 0.0)) continue;
       int lastp;
-      chunk_search<T>(a, d.y, d.z, d.w, f, c, 0.0, INFINITY, &lastp);
+      chunk_search<T>(a, d.y, d.z, d.w, f, rz, tab, c, 0.0, INFINITY, &lastp);
       y = lastp;
     }
   } else {
     int lastp;
-    y = chunk_search<T>(a, d.y, d.z, d.w, f, chunk, base_s, t, &lastp);
+    y = chunk_search<T>(a, d.y, d.z, d.w, f, rz, tab, chunk, base_s, t, &lastp);
     if (y < 0) y = lastp;
   }
   if (tid == 0) {
