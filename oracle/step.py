@@ -87,7 +87,10 @@ def verify_step(layers, cu_seqlens, ctx_lens, block_table, page_size, max_T,
                             lay['v'], lay['alpha'], lay['beta'], cu_seqlens,
                             commit_len, GDN_COMMIT_ONLY)
             states[idx] = S
-    new_ctx = (np.asarray(ctx_lens, dtype=np.int64) + commit_len).astype(np.int32)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    if ctx.shape != commit_len.shape:
+        raise ValueError(f'ctx_lens has {ctx.shape[0]} entries for {commit_len.shape[0]} sequences')
+    new_ctx = (ctx + commit_len).astype(np.int32)
     return {
         'outputs': outputs, 'k_cache': kcs, 'v_cache': vcs, 'state': states,
         'accept_len': accept_len, 'out_tokens': out_tokens,
