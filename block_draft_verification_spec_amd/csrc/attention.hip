@@ -709,21 +709,47 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
   if (wf >= wl_) return;  // one piece: written by the stream kernel
   const int m = j * G + (h - g * G);
-  float mm = -INFINITY;
-  for (int wg = wf; wg <= wl_; ++wg)
-    mm = fmaxf(mm, a.part_ml[2 * (static_cast<size_t>(s + wg) * kMaxRows + m)]);
   float acc[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
   float ls = 0.f;
-  for (int wg = wf; wg <= wl_; ++wg) {
-    const size_t pi = static_cast<size_t>(s + wg) * kMaxRows + m;
-    const float ms = a.part_ml[2 * pi];
-    if (ms == -INFINITY) continue;
-    const float f = exp2f(ms - mm);
-    ls += f * a.part_ml[2 * pi + 1];
+  constexpr int kFew = 4;  // pieces fetched at once (one round trip)
+  if (wl_ - wf < kFew) {
+    float pm[kFew], pl[kFew], po[kFew][D / 64];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] += f * a.part_o[pi * D + lane + 64 * e];
+    for (int i = 0; i < kFew; ++i) {
+      pm[i] = -INFINITY;
+      if (wf + i > wl_) continue;
+      const size_t pi = static_cast<size_t>(s + wf + i) * kMaxRows + m;
+      pm[i] = a.part_ml[2 * pi];
+      pl[i] = a.part_ml[2 * pi + 1];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) po[i][e] = a.part_o[pi * D + lane + 64 * e];
+    }
+    float mm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) mm = fmaxf(mm, pm[i]);
+#pragma unroll
+    for (int i = 0; i < kFew; ++i) {
+      if (pm[i] == -INFINITY) continue;
+      const float f = exp2f(pm[i] - mm);
+      ls += f * pl[i];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) acc[e] += f * po[i][e];
+    }
+  } else {
+    float mm = -INFINITY;
+    for (int wg = wf; wg <= wl_; ++wg)
+      mm = fmaxf(mm, a.part_ml[2 * (static_cast<size_t>(s + wg) * kMaxRows + m)]);
+    for (int wg = wf; wg <= wl_; ++wg) {
+      const size_t pi = static_cast<size_t>(s + wg) * kMaxRows + m;
+      const float ms = a.part_ml[2 * pi];
+      if (ms == -INFINITY) continue;
+      const float f = exp2f(ms - mm);
+      ls += f * a.part_ml[2 * pi + 1];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) acc[e] += f * a.part_o[pi * D + lane + 64 * e];
+    }
   }
   const size_t row = static_cast<size_t>(x0 + j) * a.Hq + h;
   const float inv = 1.f / ls;
