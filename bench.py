@@ -522,6 +522,19 @@ def main():
     torch.cuda.synchronize()
     gdn_ms = g0.elapsed_time(g1) / max(1, len(gdn_l))
 
+    # acceptance alone (same logits, uniforms and workspace), back to back
+    acc_reps = 20
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(acc_reps):
+        bd.spec_accept(sb, amode, acc['target_logits'], acc['draft_tokens'], result,
+                       draft_logits=acc.get('draft_logits'), u_accept=acc.get('u_accept'),
+                       u_final=acc.get('u_final'), workspace=ws, err=err)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    acc_ms = a0.elapsed_time(a1) / acc_reps
+
     conv = short_conv_timing(w, batch, sb, commits[0], stream, dev)
     gdn_sd = gdn_state_dtype_timing(w, batch, sb, commits[0], stream, dev)
     kv8 = attn_kv8_timing(w, batch, sb, ctx_fixed, ws, stream, dev)
@@ -560,7 +573,8 @@ def main():
                      'bytes_per_launch': b_att,
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
-                     'gdn_layer_verify_commit': round(gdn_ms, 4)},
+                     'gdn_layer_verify_commit': round(gdn_ms, 4),
+                     'acceptance': round(acc_ms, 4)},
         'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd, 'attention_int8_kv': kv8,
                       'checkpoint_commit': ckpt},
         'mean_accept_len': round(accepted, 3),

@@ -43,7 +43,15 @@ __host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChun
 //   exp(x) = 2^(k >> 8) * 2^((k & 255) / 256) * (1 + p(r)),
 // p the degree-5 Taylor polynomial of exp(r) - 1 (remainder below 1e-20
 // relative).  The 256 table entries are filled per block with exp2.
+// Every step is a full-rate fp64 or integer operation: adding 1.5 * 2^52 to
+// x * 256 / ln 2 (in one fma) rounds it to the nearest integer, ties to even,
+// and leaves that integer in the low word of the sum; the power 2^(k >> 8) is
+// added to the exponent field of the table product, which lies in [1 - 2^-9,
+// 2) and so stays a normal number for x >= -700.  Below -700 the result is 0
+// (e^-700 < 2^-1009, far under the last bit of any sum that holds the row
+// maximum's weight, which is 1), as it is for -inf and NaN.
 constexpr int kExpTab = 256;
+constexpr int kChunksPerWg = 1;  // chunks of one row a workgroup covers
 
 __device__ __forceinline__ void exp_table_init(double* tab) {
   for (int j = threadIdx.x; j < kExpTab; j += blockDim.x)
@@ -51,18 +59,23 @@ __device__ __forceinline__ void exp_table_init(double* tab) {
 }
 
 __device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
-  if (!(x > -745.0)) return 0.0;                    // below the smallest subnormal; -inf
+  constexpr double kMin = -700.0;
+  constexpr double kShift = 0x1.8p52;
   constexpr double kInvStep = 256.0 / 0.693147180559945309417232121458176568;
   constexpr double kStepHi = 0x1.62e42fefa39efp-1 / 256.0;   // ln 2 rounded to double, / 256
   constexpr double kStepLo = 2.319046813846299558e-17 / 256.0;  // ln 2 minus that double, / 256
-  const double k = rint(x * kInvStep);
-  double r = fma(-k, kStepHi, x);
+  const double xc = fmax(x, kMin);
+  const double ks = fma(xc, kInvStep, kShift);
+  const int ki = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(ks)));
+  const double k = ks - kShift;
+  double r = fma(-k, kStepHi, xc);
   r = fma(-k, kStepLo, r);
-  const int ki = static_cast<int>(k);
   const double pr =
       r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0 + r * (1.0 / 120.0)))));
   const double t = tab[ki & (kExpTab - 1)];
-  return ldexp(fma(t, pr, t), ki >> 8);
+  const long long e = __double_as_longlong(fma(t, pr, t)) +
+                      (static_cast<long long>(ki >> 8) << 52);
+  return x >= kMin ? __longlong_as_double(e) : 0.0;
 }
 
 // Workspace layout (byte offsets are 256-aligned).
@@ -156,13 +169,15 @@ __global__ __launch_bounds__(kThreads) void row_argmax_partial(AcceptArgs a) {
   const int nc = gridDim.x;
   const size_t base = static_cast<size_t>(row) * a.V;
   unsigned long long best = 0;
+  float vals[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
+    vals[e] = ld<T>(a.target, base + min(chunk * kChunk + e * kThreads + tid, a.V - 1));
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const int idx = chunk * kChunk + e * kThreads + tid;
-    if (idx < a.V) {
-      const unsigned long long key = argmax_key(ld<T>(a.target, base + idx), idx);
-      best = key > best ? key : best;
-    }
+    const unsigned long long key = idx < a.V ? argmax_key(vals[e], idx) : 0ull;
+    best = key > best ? key : best;
   }
   best = wave_max_u64(best);
   __shared__ unsigned long long red[kThreads / 64];
@@ -217,43 +232,49 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
 // Row r < total_T: target row r; otherwise draft row r - total_T.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
-  const int chunk = blockIdx.x, r = blockIdx.y;
+  const int r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int nc = gridDim.x;
+  const int nc = n_chunks(a.V);
   const void* src = r < a.total_T ? a.target : a.draft;
   const size_t base = static_cast<size_t>(r < a.total_T ? r : r - a.total_T) * a.V;
-  float vals[kPerThread];
-  float m = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int idx = chunk * kChunk + e * kThreads + tid;
-    vals[e] = idx < a.V ? ld<T>(src, base + idx) : -INFINITY;
-    m = fmaxf(m, vals[e]);
-  }
   __shared__ float redm[kThreads / 64];
   __shared__ double reds[kThreads / 64];
   __shared__ double tab[kExpTab];
-  exp_table_init(tab);
-  m = wave_max_f32(m);
-  if ((tid & 63) == 0) redm[tid >> 6] = m;
-  __syncthreads();
-  m = redm[0];
-  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, redm[w]);
-  double s = 0.0;
-  if (m > -INFINITY) {
+  exp_table_init(tab);  // read after the first barrier below
+  const int c_end = min(nc, (static_cast<int>(blockIdx.x) + 1) * kChunksPerWg);
+  for (int chunk = blockIdx.x * kChunksPerWg; chunk < c_end; ++chunk) {
+    float vals[kPerThread];
+    float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      if (vals[e] > -INFINITY) s += exp_nonpos(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
-  }
-  s = wave_sum_f64(s);
-  if ((tid & 63) == 0) reds[tid >> 6] = s;
-  __syncthreads();
-  if (tid == 0) {
-    s = reds[0];
-    for (int w = 1; w < kThreads / 64; ++w) s += reds[w];
-    const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
-    reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats)
-        [static_cast<size_t>(r) * nc + chunk] = make_double2(static_cast<double>(m), s);
+    for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
+      vals[e] = ld<T>(src, base + min(chunk * kChunk + e * kThreads + tid, a.V - 1));
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (chunk * kChunk + e * kThreads + tid >= a.V) vals[e] = -INFINITY;
+      m = fmaxf(m, vals[e]);
+    }
+    m = wave_max_f32(m);
+    if ((tid & 63) == 0) redm[tid >> 6] = m;
+    __syncthreads();
+    m = redm[0];
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, redm[w]);
+    double s = 0.0;
+    if (m > -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        s += exp_nonpos(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
+    }
+    s = wave_sum_f64(s);
+    if ((tid & 63) == 0) reds[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) {
+      s = reds[0];
+      for (int w = 1; w < kThreads / 64; ++w) s += reds[w];
+      const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+      reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats)
+          [static_cast<size_t>(r) * nc + chunk] = make_double2(static_cast<double>(m), s);
+    }
+    __syncthreads();  // redm and reds are rewritten by the next chunk
   }
 }
 
@@ -335,49 +356,75 @@ __global__ __launch_bounds__(64) void decide_reject(AcceptArgs a) {
   }
 }
 
-// Weight of vocabulary entry y for the final draw of a sequence; rz holds the
-// reciprocals of the two normalisers (f.y, f.w).
+// Logits of vocabulary entry y (clamped into the row, so the load is always
+// in bounds and never waits on a branch) for the final draw of a sequence:
+// the target row rt and, with DRAFT (kind 1), the draft row rd.
+template <typename T, bool DRAFT>
+__device__ __forceinline__ float2 draw_logits(const AcceptArgs& a, int rt, int rd, int y) {
+  const int yc = min(y, a.V - 1);
+  const float lt = ld<T>(a.target, static_cast<size_t>(rt) * a.V + yc);
+  const float lq = DRAFT ? ld<T>(a.draft, static_cast<size_t>(rd) * a.V + yc) : 0.f;
+  return make_float2(lt, lq);
+}
+
+// The logits of entries y0 + stride * e, e < kPerThread, every load issued
+// before any is used.
 template <typename T>
-__device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int rt, int rd,
+__device__ __forceinline__ void load_draw_logits(const AcceptArgs& a, int kind, int rt, int rd,
+                                                 int y0, int stride, float2* lg) {
+  if (kind == 1) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) lg[e] = draw_logits<T, true>(a, rt, rd, y0 + stride * e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) lg[e] = draw_logits<T, false>(a, rt, rd, y0 + stride * e);
+  }
+}
+
+// Weight of vocabulary entry y from its logits; rz holds the reciprocals of
+// the two normalisers (f.y, f.w).  Entries past the vocabulary weigh 0.
+__device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int rd,
                                               const double4& f, const double2& rz, int y,
-                                              const double* tab) {
-  const double p =
-      exp_nonpos(static_cast<double>(ld<T>(a.target, static_cast<size_t>(rt) * a.V + y)) - f.x,
-                 tab) * rz.x;
+                                              float2 lg, const double* tab) {
+  if (y >= a.V) return 0.0;
+  const double p = exp_nonpos(static_cast<double>(lg.x) - f.x, tab) * rz.x;
   if (kind == 0) return p;
   if (kind == 2) return y == rd ? 0.0 : p;  // point-mass draft at rd
-  const double q =
-      exp_nonpos(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(rd) * a.V + y)) - f.z,
-                 tab) * rz.y;
+  const double q = exp_nonpos(static_cast<double>(lg.y) - f.z, tab) * rz.y;
   return fmax(p - q, 0.0);
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
-  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int nc = n_chunks(a.V);
   const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
   const int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
   if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
   __shared__ double tab[kExpTab];
+  __shared__ double red[kThreads / 64];
   exp_table_init(tab);
   __syncthreads();
-  double s = 0.0;
-#pragma unroll 4
-  for (int e = 0; e < kPerThread; ++e) {
-    const int y = chunk * kChunk + e * kThreads + tid;
-    if (y < a.V) s += draw_weight<T>(a, d.y, d.z, d.w, f, rz, y, tab);
-  }
-  s = wave_sum_f64(s);
-  __shared__ double red[kThreads / 64];
-  if ((tid & 63) == 0) red[tid >> 6] = s;
-  __syncthreads();
-  if (tid == 0) {
-    s = red[0];
-    for (int w = 1; w < kThreads / 64; ++w) s += red[w];
-    reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum)
-        [static_cast<size_t>(b) * gridDim.x + chunk] = s;
+  const int c_end = min(nc, (static_cast<int>(blockIdx.x) + 1) * kChunksPerWg);
+  for (int chunk = blockIdx.x * kChunksPerWg; chunk < c_end; ++chunk) {
+    float2 lg[kPerThread];
+    load_draw_logits<T>(a, d.y, d.z, d.w, chunk * kChunk + tid, kThreads, lg);
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      s += draw_weight(a, d.y, d.w, f, rz, chunk * kChunk + e * kThreads + tid, lg[e], tab);
+    s = wave_sum_f64(s);
+    if ((tid & 63) == 0) red[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) {
+      s = red[0];
+      for (int w = 1; w < kThreads / 64; ++w) s += red[w];
+      reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum)
+          [static_cast<size_t>(b) * nc + chunk] = s;
+    }
+    __syncthreads();  // red is rewritten by the next chunk
   }
 }
 
@@ -395,10 +442,11 @@ __device__ int chunk_search(const AcceptArgs& a, int kind, int rt, int rd, const
   double w[kPerThread];
   double s = 0.0;
   const int y0 = chunk * kChunk + tid * kPerThread;
+  float2 lg[kPerThread];
+  load_draw_logits<T>(a, kind, rt, rd, y0, 1, lg);
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const int y = y0 + e;
-    w[e] = y < a.V ? draw_weight<T>(a, kind, rt, rd, f, rz, y, tab) : 0.0;
+    w[e] = draw_weight(a, kind, rd, f, rz, y0 + e, lg[e], tab);
     s += w[e];
   }
   pre[tid] = s;
@@ -459,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
       double s = 0.0;
       for (int e = 0; e < kPerThread; ++e) {
         const int y = c * kChunk + e * kThreads + tid;
-        if (y < a.V) s += draw_weight<T>(a, 0, d.z, d.w, f, rz, y, tab);
+        s += draw_weight(a, 0, d.w, f, rz, y, draw_logits<T, false>(a, d.z, d.w, y), tab);
       }
       s = wave_sum_f64(s);
       __shared__ double red[kThreads / 64];
@@ -530,9 +578,10 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
   } else {
     const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
-    hipLaunchKernelGGL((row_stats_partial<T>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
+    const int ncw = (nc + kChunksPerWg - 1) / kChunksPerWg;
+    hipLaunchKernelGGL((row_stats_partial<T>), dim3(ncw, rows), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(64), 0, stream, a);
-    hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((residual_partial<T>), dim3(ncw, a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((final_draw<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
