@@ -122,6 +122,9 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
   return a;
 }
 
+// true for a pointer the 16-byte vector loads cannot take (null passes)
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 sv_status check_gdn_common(const sv_batch* batch, void* state, sv_dtype state_dtype,
                            int32_t num_slots, sv_dtype io_dtype, int32_t H, int32_t dk,
                            int32_t dv, const char* who) {
@@ -272,6 +275,9 @@ sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state
     return fail(SV_EINVAL, "%s: commit_len is required unless VERIFY_ONLY", who);
   if (!state_slot && num_slots < batch->B)
     return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) ||
+      (pending && (misaligned16(pending->k) || misaligned16(pending->v))))
+    return fail(SV_EINVAL, "%s: q, k, v must be 16-byte aligned", who);
   sv::GdnScalars s{};
   s.B = batch->B;
   s.total_T = batch->total_T;
@@ -440,6 +446,8 @@ sv_status gdn_verify_checkpoint(const sv_batch* batch, const void* state, sv_dty
     return fail(SV_EINVAL, "%s: q, k, v, alpha, beta, out and checkpoints are required", who);
   if (reinterpret_cast<uintptr_t>(checkpoints) & 15)
     return fail(SV_EINVAL, "%s: checkpoints must be 16-byte aligned", who);
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v))
+    return fail(SV_EINVAL, "%s: q, k, v must be 16-byte aligned", who);
   if (!state_slot && num_slots < batch->B)
     return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
   const sv::GdnScalars s = gdn_scalars(batch, SV_GDN_VERIFY_ONLY, state_slot, num_slots, nullptr,

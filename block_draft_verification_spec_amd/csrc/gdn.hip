@@ -120,6 +120,24 @@ __device__ __forceinline__ float lane8_sum(float v) {
   return v;
 }
 
+// One 16-byte chunk of token inputs to fp32 in LDS (dst 16-byte aligned):
+// eight bf16 values or four fp32 values.
+template <typename LS>
+__device__ __forceinline__ void chunk_to_f32(const uint4& r, float* dst);
+template <>
+__device__ __forceinline__ void chunk_to_f32<uint16_t>(const uint4& r, float* dst) {
+  float4* d = reinterpret_cast<float4*>(dst);
+  d[0] = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  d[1] = make_float4(__uint_as_float(r.z << 16), __uint_as_float(r.z & 0xffff0000u),
+                     __uint_as_float(r.w << 16), __uint_as_float(r.w & 0xffff0000u));
+}
+template <>
+__device__ __forceinline__ void chunk_to_f32<float>(const uint4& r, float* dst) {
+  *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(r.x), __uint_as_float(r.y),
+                                                __uint_as_float(r.z), __uint_as_float(r.w));
+}
+
 template <int DK>
 struct GdnSmem {
   float k_s[kMaxTok][DK];
@@ -204,7 +222,59 @@ __device__ __forceinline__ void gdn_tile(
   constexpr int kRowStride = kThreads / kLanesPerRow;  // rows rg + kRowStride r
   ST* tile = static_cast<ST*>(state) + (static_cast<size_t>(slot) * H + h) * DV * DK;
 
-  // ---- issue the state loads first: they are the long-latency traffic
+  // ---- token inputs: a fixed set of 16-byte loads per thread (chunks of the
+  // k and q rows and of this block's slice of the v rows), all issued before
+  // any is used, so the block waits one memory round trip for all of them; a
+  // chunk past the last token reads token 0 again and is not stored.  Rows are
+  // 16-byte aligned (the entry points require aligned q, k, v).
+  using LS = typename L::storage;
+  constexpr int EPC = 16 / sizeof(LS);                    // elements per chunk
+  constexpr int KCH = DK / EPC;                           // chunks per k or q row
+  constexpr int VCH = kRowsPerBlock / EPC;                // chunks per v row slice
+  constexpr int KN = (kMaxTok * KCH + kThreads - 1) / kThreads;
+  constexpr int QN = (kMaxT * KCH + kThreads - 1) / kThreads;
+  constexpr int VN = (kMaxTok * VCH + kThreads - 1) / kThreads;
+  const LS* kp = static_cast<const LS*>(k);
+  const LS* pkp = static_cast<const LS*>(pk);
+  const LS* vp = static_cast<const LS*>(v);
+  const LS* pvp = static_cast<const LS*>(pv);
+  // token t of the stream (replayed pending tokens, then this call's)
+  auto tok = [&](int t, const LS* pend, const LS* cur, int width) __attribute__((always_inline)) {
+    return t < pc ? pend + (static_cast<size_t>(px0 + t) * H + h) * width
+                  : cur + (static_cast<size_t>(x0 + t - pc) * H + h) * width;
+  };
+  uint4 kr[KN], qr[QN], vr[VN];
+#pragma unroll
+  for (int i = 0; i < KN; ++i) {
+    const int idx = tid + kThreads * i, t = idx / KCH;
+    kr[i] = *reinterpret_cast<const uint4*>(tok(t < n_tot ? t : 0, pkp, kp, DK) +
+                                            (idx % KCH) * EPC);
+  }
+  if (verify) {
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int idx = tid + kThreads * i, t = idx / KCH;
+      qr[i] = *reinterpret_cast<const uint4*>(
+          static_cast<const LS*>(q) + (static_cast<size_t>(x0 + (t < T ? t : 0)) * H + h) * DK +
+          (idx % KCH) * EPC);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VN; ++i) {
+    const int idx = tid + kThreads * i, t = idx / VCH;
+    vr[i] = *reinterpret_cast<const uint4*>(tok(t < n_tot ? t : 0, pvp, vp, DV) + row0 +
+                                            (idx % VCH) * EPC);
+  }
+  float ar = 0.f, br = 0.f;
+  if (tid < n_tot) {
+    const int t = tid;
+    const size_t gi = t < pc ? static_cast<size_t>(px0 + t) * H + h
+                             : static_cast<size_t>(x0 + t - pc) * H + h;
+    ar = t < pc ? palpha[gi] : alpha[gi];
+    br = t < pc ? pbeta[gi] : beta[gi];
+  }
+
+  // ---- the state loads: the long-latency traffic
   float4 sr[kRowsPerThread][NV4];
 #pragma unroll
   for (int r = 0; r < kRowsPerThread; ++r) {
@@ -213,29 +283,27 @@ __device__ __forceinline__ void gdn_tile(
     for (int j = 0; j < NV4; ++j) sr[r][j] = load_state4<ST>(rowp + 32 * j + 4 * cl);
   }
 
-  // ---- stage token inputs as fp32
-  for (int i = tid; i < n_tot * DK; i += kThreads) {
-    const int t = i / DK, e = i - t * DK;
-    k_s[t][e] = t < pc ? L::load(pk, (static_cast<size_t>(px0 + t) * H + h) * DK + e)
-                       : L::load(k, (static_cast<size_t>(x0 + t - pc) * H + h) * DK + e);
+  // ---- token inputs to LDS as fp32
+#pragma unroll
+  for (int i = 0; i < KN; ++i) {
+    const int idx = tid + kThreads * i, t = idx / KCH;
+    if (t < n_tot) chunk_to_f32<LS>(kr[i], &k_s[t][(idx % KCH) * EPC]);
   }
   if (verify) {
-    for (int i = tid; i < T * DK; i += kThreads) {
-      const int t = i / DK, e = i - t * DK;
-      q_s[t][e] = L::load(q, (static_cast<size_t>(x0 + t) * H + h) * DK + e);
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int idx = tid + kThreads * i, t = idx / KCH;
+      if (t < T) chunk_to_f32<LS>(qr[i], &q_s[t][(idx % KCH) * EPC]);
     }
   }
-  for (int i = tid; i < n_tot * kRowsPerBlock; i += kThreads) {
-    const int t = i / kRowsPerBlock, r = i - t * kRowsPerBlock;
-    v_s[t][r] = t < pc ? L::load(pv, (static_cast<size_t>(px0 + t) * H + h) * DV + row0 + r)
-                       : L::load(v, (static_cast<size_t>(x0 + t - pc) * H + h) * DV + row0 + r);
+#pragma unroll
+  for (int i = 0; i < VN; ++i) {
+    const int idx = tid + kThreads * i, t = idx / VCH;
+    if (t < n_tot) chunk_to_f32<LS>(vr[i], &v_s[t][(idx % VCH) * EPC]);
   }
   if (tid < n_tot) {
-    const int t = tid;
-    const size_t gi = t < pc ? static_cast<size_t>(px0 + t) * H + h
-                             : static_cast<size_t>(x0 + t - pc) * H + h;
-    a_s[t] = t < pc ? palpha[gi] : alpha[gi];
-    b_s[t] = t < pc ? pbeta[gi] : beta[gi];
+    a_s[tid] = ar;
+    b_s[tid] = br;
   }
   __syncthreads();
   // k_t . q_t of every current token, once per block: 16 lanes per token

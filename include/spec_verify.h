@@ -176,7 +176,8 @@ SV_API sv_status spec_verify_attention_kv8(const sv_batch* batch,
  *               tokens of sequence b are applied to the state before this
  *               call's tokens, and the state is then stored even in
  *               VERIFY_ONLY mode.  It must describe the same B sequences.
- * dk = 64 or 128; dv a multiple of 64 up to 256.
+ * dk = 64 or 128; dv a multiple of 64 up to 256.  state, q, k, v (and the
+ * pending k, v) must be 16-byte aligned; SV_EINVAL otherwise.
  * ------------------------------------------------------------------------ */
 typedef enum {
   SV_GDN_VERIFY_COMMIT = 0,

@@ -139,6 +139,8 @@ def test_gdn_validation():
     assert call(sdt=bd.SV_BF16) == bd.SV_EDTYPE
     assert 'state dtype' in L.sv_last_error().decode()
     assert call(state=20) == bd.SV_EINVAL                    # misaligned state
+    assert call(q=24) == bd.SV_EINVAL                        # misaligned q
+    assert 'aligned' in L.sv_last_error().decode()
 
 
 def test_short_conv_validation():
