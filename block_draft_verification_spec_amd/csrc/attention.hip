@@ -102,22 +102,28 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 
 __device__ __forceinline__ int seq_tiles(int L, int T) { return (L + T + kKT - 1) / kKT; }
 
-// Validate a sequence for attention.  Returns false (and maybe flags) if the
-// whole sequence must be skipped.
+// Validate a sequence (first row x0, T verify tokens, L cached tokens) for
+// attention.  Returns false (and maybe flags) if the whole sequence must be
+// skipped.
+__device__ __forceinline__ bool attn_seq_valid(const AttnArgs& a, int x0, int T, int L,
+                                               bool report) {
+  if (T < 1 || T > a.max_T || x0 < 0 || x0 + T > a.total_T || L < 0) {
+    if (report) flag_error(a.err, SV_DERR_SEQLEN);
+    return false;
+  }
+  if (static_cast<long long>(L) + T > static_cast<long long>(a.max_pages) * a.P) {
+    if (report) flag_error(a.err, SV_DERR_CAPACITY);
+    return false;
+  }
+  return true;
+}
+
 __device__ __forceinline__ bool attn_seq_ok(const AttnArgs& a, int b, int* x0, int* T, int* L,
                                             bool report) {
   *x0 = a.cu[b];
   *T = a.cu[b + 1] - *x0;
   *L = a.ctx_lens[b];
-  if (*T < 1 || *T > a.max_T || *x0 < 0 || *x0 + *T > a.total_T || *L < 0) {
-    if (report) flag_error(a.err, SV_DERR_SEQLEN);
-    return false;
-  }
-  if (static_cast<long long>(*L) + *T > static_cast<long long>(a.max_pages) * a.P) {
-    if (report) flag_error(a.err, SV_DERR_CAPACITY);
-    return false;
-  }
-  return true;
+  return attn_seq_valid(a, *x0, *T, *L, report);
 }
 
 // Element offset of (position p, kv head g, dim d0) in the pool, or -1 if the
@@ -178,7 +184,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   __shared__ float wl[4][ROWS];
   __shared__ int s_pre[kMaxB + 1];           // tiles before sequence b (all its heads)
   __shared__ int s_ids[kChunkTiles * 4];     // page ids of the current chunk
-  __shared__ int s_scan[kThreads];
+  __shared__ int s_scan[kThreads / 64];
   uint16_t* Ks = lds;
   uint16_t* Vt = lds + kKT * KS;
   // V^T column swizzle: key k of row r sits at column k ^ vswz(r), a multiple
@@ -190,30 +196,44 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int B = a.B, Hkv = a.Hkv, G = a.Hq / a.Hkv, P = a.P;
 
-  // ---- tiles of every sequence and their prefix over segments
+  // ---- tiles of every sequence and their prefix over segments.  Thread tid
+  // owns sequences tid * kPer .. tid * kPer + kPer - 1; their cu_seqlens and
+  // ctx_lens entries are all loaded (indices clamped) before any is used.
   constexpr int kPer = (kMaxB + kThreads - 1) / kThreads;
+  int cuv[kPer + 1], lv[kPer];
+#pragma unroll
+  for (int i = 0; i <= kPer; ++i) cuv[i] = a.cu[min(tid * kPer + i, B)];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) lv[i] = a.ctx_lens[min(tid * kPer + i, B - 1)];
+  // one wait for all of them here (the uses below sit in branches, into which
+  // the compiler would otherwise move a load and its wait)
+#pragma unroll
+  for (int i = 0; i <= kPer; ++i) asm volatile("" : "+v"(cuv[i]));
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(lv[i]));
   int part[kPer];
   int run = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = tid * kPer + i;
     int v = 0;
-    if (b < B) {
-      int x0, T, L;
-      if (attn_seq_ok(a, b, &x0, &T, &L, blockIdx.x == 0)) v = seq_tiles(L, T) * Hkv;
-    }
+    if (b < B && attn_seq_valid(a, cuv[i], cuv[i + 1] - cuv[i], lv[i], blockIdx.x == 0))
+      v = seq_tiles(lv[i], cuv[i + 1] - cuv[i]) * Hkv;
     run += v;
     part[i] = run;
   }
-  s_scan[tid] = run;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+  // inclusive scan of the per-thread totals: within each wave by shuffles,
+  // then the totals of the waves before it
+  int inc = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
   }
-  const int excl = s_scan[tid] - run;
+  if (lane == 63) s_scan[w] = inc;
+  __syncthreads();
+  int excl = inc - run;
+  for (int ww = 0; ww < w; ++ww) excl += s_scan[ww];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = tid * kPer + i;
@@ -454,16 +474,15 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     const int lt_end = min(t_hi, seg_start + nt_b) - seg_start;
     const int s = b * Hkv + g;
     const bool whole = lt_begin == 0 && lt_end == nt_b;
+    x0 = a.cu[b];
+    T = a.cu[b + 1] - x0;
+    L = a.ctx_lens[b];
+    M = G * T;
     if (lt_begin == 0 && tid == 0) {
       a.seg_meta[2 * s] = wg;
       a.seg_meta[2 * s + 1] = piece_wg(seg_start + nt_b - 1, W, N);
     }
     t = seg_start + lt_end;
-
-    x0 = a.cu[b];
-    T = a.cu[b + 1] - x0;
-    L = a.ctx_lens[b];
-    M = G * T;
 
     // Q fragments (B operand of S^T = K Q^T): row 16 nt + lr, dims 32 s + 8 lg ..
 #pragma unroll
@@ -521,24 +540,6 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       }
       __syncthreads();
 
-      // write-through of the in-flight K/V rows that fall in this chunk (reads
-      // of those positions come from k_new / v_new)
-      if (!KV8 && a.write_kv) {
-        for (int idx = tid; idx < T * CPK; idx += kThreads) {
-          const int j = idx / CPK, c = idx - j * CPK;
-          const int p = L + j;
-          if (p < c0 * kKT || p >= pos_end) continue;
-          const int pid = s_ids[p / P - first_page];
-          if (pid < 0) continue;
-          const size_t off_c = ((static_cast<size_t>(pid) * Hkv + g) * P + (p % P)) * D + 8 * c;
-          const size_t off_n = (static_cast<size_t>(x0 + j) * Hkv + g) * D + 8 * c;
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + off_c) =
-              *reinterpret_cast<const uint4*>(kn + off_n);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + off_c) =
-              *reinterpret_cast<const uint4*>(vn + off_n);
-        }
-      }
-
       r0 = load_tile(c0);
       if constexpr (PF > 1) r1 = load_tile(c0 + 1);
       if constexpr (PF > 2) r2 = load_tile(c0 + 2);
@@ -558,6 +559,24 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
             if (tile + u + 2 >= c1) break;
             consume(tile + u + 2, r2);
           }
+        }
+      }
+      // write-through of the in-flight K/V rows that fall in this chunk (after
+      // its tiles: their reads of those positions come from k_new / v_new, so
+      // no tile load waits behind these copies)
+      if (!KV8 && a.write_kv) {
+        for (int idx = tid; idx < T * CPK; idx += kThreads) {
+          const int j = idx / CPK, c = idx - j * CPK;
+          const int p = L + j;
+          if (p < c0 * kKT || p >= pos_end) continue;
+          const int pid = s_ids[p / P - first_page];
+          if (pid < 0) continue;
+          const size_t off_c = ((static_cast<size_t>(pid) * Hkv + g) * P + (p % P)) * D + 8 * c;
+          const size_t off_n = (static_cast<size_t>(x0 + j) * Hkv + g) * D + 8 * c;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + off_c) =
+              *reinterpret_cast<const uint4*>(kn + off_n);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + off_c) =
+              *reinterpret_cast<const uint4*>(vn + off_n);
         }
       }
     }
