@@ -182,7 +182,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKT * KS + D * VS];
   __shared__ float wm[4][ROWS];
   __shared__ float wl[4][ROWS];
-  __shared__ int s_pre[kMaxB + 1];           // tiles before sequence b (all its heads)
+  __shared__ int s_first[2];                 // the sequence holding tile t_lo, its first tile
   __shared__ int s_ids[kChunkTiles * 4];     // page ids of the current chunk
   __shared__ int s_scan[kThreads / 64];
   uint16_t* Ks = lds;
@@ -234,17 +234,25 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   __syncthreads();
   int excl = inc - run;
   for (int ww = 0; ww < w; ++ww) excl += s_scan[ww];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int b = tid * kPer + i;
-    if (b < B) s_pre[b + 1] = excl + part[i];
-  }
-  if (tid == 0) s_pre[0] = 0;
-  __syncthreads();
-  const int N = s_pre[B];
+  const int N = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
   const int W = gridDim.x, wg = blockIdx.x;
   const int t_lo = static_cast<int>(static_cast<long long>(wg) * N / W);
   const int t_hi = static_cast<int>(static_cast<long long>(wg + 1) * N / W);
+  // the sequence whose tiles hold t_lo: the one thread owning it says so
+  // (sequences without tiles own an empty range and never match)
+  {
+    int pre = excl;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int end = excl + part[i];
+      if (t_lo >= pre && t_lo < end) {
+        s_first[0] = tid * kPer + i;
+        s_first[1] = pre;
+      }
+      pre = end;
+    }
+  }
+  __syncthreads();
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
@@ -458,31 +466,42 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
 
   TileRegs<KPT> r0, r1, r2;
 
+  // Pieces in order: sequence cb (its first tile is cbase) and its Hkv
+  // segments of nt_b tiles; past its last tile the next sequence with tiles.
+  int cb = t_lo < t_hi ? s_first[0] : B, cbase = t_lo < t_hi ? s_first[1] : 0;
+  int nt_b = 0;
+  bool next_seq = true;
   for (int t = t_lo; t < t_hi;) {
-    // ---- the piece: segment (b, g) tiles [lt_begin, lt_end)
-    int lo = 0, hi = B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pre[mid] <= t) lo = mid;
-      else hi = mid;
+    if (next_seq) {
+      for (; cb < B; ++cb) {  // skipped: sequences that failed validation
+        x0 = a.cu[cb];
+        T = a.cu[cb + 1] - x0;
+        L = a.ctx_lens[cb];
+        if (attn_seq_valid(a, x0, T, L, false)) break;
+      }
+      if (cb >= B) break;  // not reached: tiles before N belong to valid sequences
+      nt_b = seq_tiles(L, T);
+      next_seq = false;
     }
-    b = lo;
-    const int nt_b = (s_pre[b + 1] - s_pre[b]) / Hkv;
-    g = (t - s_pre[b]) / nt_b;
-    const int seg_start = s_pre[b] + g * nt_b;
+    // ---- the piece: segment (b, g) tiles [lt_begin, lt_end)
+    b = cb;
+    g = (t - cbase) / nt_b;
+    const int seg_start = cbase + g * nt_b;
     const int lt_begin = t - seg_start;
     const int lt_end = min(t_hi, seg_start + nt_b) - seg_start;
     const int s = b * Hkv + g;
     const bool whole = lt_begin == 0 && lt_end == nt_b;
-    x0 = a.cu[b];
-    T = a.cu[b + 1] - x0;
-    L = a.ctx_lens[b];
     M = G * T;
     if (lt_begin == 0 && tid == 0) {
       a.seg_meta[2 * s] = wg;
       a.seg_meta[2 * s + 1] = piece_wg(seg_start + nt_b - 1, W, N);
     }
     t = seg_start + lt_end;
+    if (t == cbase + Hkv * nt_b) {
+      cbase = t;
+      ++cb;
+      next_seq = true;
+    }
 
     // Q fragments (B operand of S^T = K Q^T): row 16 nt + lr, dims 32 s + 8 lg ..
 #pragma unroll
@@ -864,9 +883,10 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
   if (lane + 64 < D) out[lane + 64] = o[1] * inv;
 }
 
-// One tile in flight per workgroup and as many resident workgroups as the
-// registers allow measured fastest: more workgroups hide latency better than
-// a deeper ring in fewer of them.
+// One tile in flight per workgroup and three resident workgroups per CU
+// measured fastest: more workgroups hide latency better than a deeper ring in
+// fewer of them, but a fourth (128 registers, the LDS of four fitting a CU)
+// was 10 % slower at the 64-sequence hybrid shape.
 template <int D, int NQT>
 constexpr int ring_depth() {
   return 1;
