@@ -34,62 +34,71 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs a) {
   const int b = blockIdx.y;
   const int c = blockIdx.x * kThreads + threadIdx.x;
   const bool report = blockIdx.x == 0 && threadIdx.x == 0;
-  // ---- validate the sequence (uniform over the block)
+  // ---- validate the sequence (uniform over the block).  Every per-sequence
+  // value is loaded before any is checked (the guards depend on kernel
+  // arguments only), so the block waits one round trip for all of them.
+  const bool has_commit = a.mode != SV_GDN_VERIFY_ONLY;
   const int x0 = a.cu[b];
-  const int T = a.cu[b + 1] - x0;
-  if (T < 1 || T > a.max_T || x0 < 0 || x0 + T > a.total_T) {
-    if (report) flag_error(a.err, SV_DERR_SEQLEN);
-    return;
-  }
+  const int x1 = a.cu[b + 1];
   const int slot = a.state_slot ? a.state_slot[b] : b;
-  if (slot < 0 || slot >= a.num_slots) {
-    if (report) flag_error(a.err, SV_DERR_SLOT);
+  const int cm_in = has_commit ? a.commit_len[b] : 0;
+  const int p0 = a.has_pending ? a.p_cu[b] : 0;
+  const int p1 = a.has_pending ? a.p_cu[b + 1] : 1;
+  const int pc_in = a.has_pending ? a.p_commit[b] : 0;
+  const int T = x1 - x0;
+  const int pT = p1 - p0;
+  int bad = 0;
+  if (T < 1 || T > a.max_T || x0 < 0 || x0 + T > a.total_T) bad = SV_DERR_SEQLEN;
+  else if (slot < 0 || slot >= a.num_slots) bad = SV_DERR_SLOT;
+  else if (cm_in < 0 || cm_in > T) bad = SV_DERR_COMMIT;
+  else if (a.has_pending && (pT < 1 || pT > a.p_max_T || p0 < 0 || p0 + pT > a.p_total_T))
+    bad = SV_DERR_SEQLEN;
+  else if (pc_in < 0 || pc_in > pT) bad = SV_DERR_COMMIT;
+  if (bad) {
+    if (report) flag_error(a.err, bad);
     return;
   }
-  int cm = 0;
-  if (a.mode != SV_GDN_VERIFY_ONLY) {
-    cm = a.commit_len[b];
-    if (cm < 0 || cm > T) {
-      if (report) flag_error(a.err, SV_DERR_COMMIT);
-      return;
-    }
-  }
-  int px0 = 0, pc = 0;
-  if (a.has_pending) {
-    px0 = a.p_cu[b];
-    const int pT = a.p_cu[b + 1] - px0;
-    if (pT < 1 || pT > a.p_max_T || px0 < 0 || px0 + pT > a.p_total_T) {
-      if (report) flag_error(a.err, SV_DERR_SEQLEN);
-      return;
-    }
-    pc = a.p_commit[b];
-    if (pc < 0 || pc > pT) {
-      if (report) flag_error(a.err, SV_DERR_COMMIT);
-      return;
-    }
-  }
+  const int cm = cm_in;
+  const int px0 = p0, pc = pc_in;
   if (c >= a.C) return;
   const int C = a.C;
   const size_t srow = static_cast<size_t>(slot) * (K - 1);
 
-  // ---- window: the last K-1 inputs, then the pending ones shifted in
+  // ---- every input this thread reads, loaded before any is used (rows
+  // clamped into the sequence, the surplus masked afterwards): the window,
+  // the pending inputs, this call's inputs
+  const bool verify = a.mode != SV_GDN_COMMIT_ONLY;
+  const int n = verify ? T : cm;  // current tokens read
   float win[K - 1];
 #pragma unroll
   for (int i = 0; i < K - 1; ++i) win[i] = L::load(a.state, (srow + i) * C + c);
-  for (int t = 0; t < pc; ++t) {
+  float pin[kMaxT];
+  if (a.has_pending) {
 #pragma unroll
-    for (int i = 0; i < K - 2; ++i) win[i] = win[i + 1];
-    win[K - 2] = L::load(a.px, static_cast<size_t>(px0 + t) * C + c);
+    for (int t = 0; t < kMaxT; ++t)
+      pin[t] = L::load(a.px, static_cast<size_t>(px0 + min(t, pT - 1)) * C + c);
   }
-
-  const bool verify = a.mode != SV_GDN_COMMIT_ONLY;
-  const int n = verify ? T : cm;  // current tokens read
   float z[K - 1 + kMaxT];
 #pragma unroll
-  for (int i = 0; i < K - 1; ++i) z[i] = win[i];
+  for (int t = 0; t < kMaxT; ++t)
+    z[K - 1 + t] = L::load(a.x, static_cast<size_t>(x0 + min(t, T - 1)) * C + c);
 #pragma unroll
   for (int t = 0; t < kMaxT; ++t)
-    z[K - 1 + t] = t < n ? L::load(a.x, static_cast<size_t>(x0 + t) * C + c) : 0.f;
+    if (t >= n) z[K - 1 + t] = 0.f;
+
+  // ---- the window: the last K-1 inputs, then the pending ones shifted in
+  if (a.has_pending) {
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t < pc) {
+#pragma unroll
+        for (int i = 0; i < K - 2; ++i) win[i] = win[i + 1];
+        win[K - 2] = pin[t];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) z[i] = win[i];
 
   if (verify) {
     float w[K];

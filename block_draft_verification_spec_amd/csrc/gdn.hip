@@ -173,40 +173,33 @@ __device__ __forceinline__ void gdn_tile(
   auto& kq_s = sm.kq_s;
 
   const int tid = threadIdx.x;
-  // ---- validate the sequence (uniform over the block)
+  // ---- validate the sequence (uniform over the block).  Every per-sequence
+  // value is loaded before any is checked (the guards depend on kernel
+  // arguments only), so the block waits one round trip for all of them.
+  const bool has_commit = s.mode != SV_GDN_VERIFY_ONLY;
+  const bool has_pend = !COMMIT_ONLY_NP && s.has_pending;
   const int x0 = s.cu[b];
-  const int T = s.cu[b + 1] - x0;
-  if (T < 1 || T > s.max_T || x0 < 0 || x0 + T > s.total_T) {
-    if (report && tid == 0) flag_error(s.err, SV_DERR_SEQLEN);
-    return;
-  }
+  const int x1 = s.cu[b + 1];
   const int slot = s.state_slot ? s.state_slot[b] : b;
-  if (slot < 0 || slot >= s.num_slots) {
-    if (report && tid == 0) flag_error(s.err, SV_DERR_SLOT);
+  const int c_in = has_commit ? s.commit_len[b] : 0;
+  const int p0 = has_pend ? s.p_cu[b] : 0;
+  const int p1 = has_pend ? s.p_cu[b + 1] : 1;
+  const int pc_in = has_pend ? s.p_commit[b] : 0;
+  const int T = x1 - x0;
+  const int pT = p1 - p0;
+  int bad = 0;
+  if (T < 1 || T > s.max_T || x0 < 0 || x0 + T > s.total_T) bad = SV_DERR_SEQLEN;
+  else if (slot < 0 || slot >= s.num_slots) bad = SV_DERR_SLOT;
+  else if (c_in < 0 || c_in > T) bad = SV_DERR_COMMIT;
+  else if (has_pend && (pT < 1 || pT > s.p_max_T || p0 < 0 || p0 + pT > s.p_total_T))
+    bad = SV_DERR_SEQLEN;
+  else if (pc_in < 0 || pc_in > pT) bad = SV_DERR_COMMIT;
+  if (bad) {
+    if (report && tid == 0) flag_error(s.err, bad);
     return;
   }
-  int c = 0;
-  if (s.mode != SV_GDN_VERIFY_ONLY) {
-    c = s.commit_len[b];
-    if (c < 0 || c > T) {
-      if (report && tid == 0) flag_error(s.err, SV_DERR_COMMIT);
-      return;
-    }
-  }
-  int px0 = 0, pc = 0;
-  if (!COMMIT_ONLY_NP && s.has_pending) {
-    px0 = s.p_cu[b];
-    const int pT = s.p_cu[b + 1] - px0;
-    if (pT < 1 || pT > s.p_max_T || px0 < 0 || px0 + pT > s.p_total_T) {
-      if (report && tid == 0) flag_error(s.err, SV_DERR_SEQLEN);
-      return;
-    }
-    pc = s.p_commit[b];
-    if (pc < 0 || pc > pT) {
-      if (report && tid == 0) flag_error(s.err, SV_DERR_COMMIT);
-      return;
-    }
-  }
+  const int c = c_in;
+  const int px0 = p0, pc = pc_in;
   const bool verify = !COMMIT_ONLY_NP && s.mode != SV_GDN_COMMIT_ONLY;
   const int n_cur = verify ? T : c;
   const int n_tot = pc + n_cur;
