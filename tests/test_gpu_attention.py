@@ -35,6 +35,20 @@ def _run(w, batch, lay, table=None, kc=None, vc=None, write_kv=True):
     return out, kc, vc, int(err.item())
 
 
+def _seq_ref(lay, batch, b):
+    """Oracle output of sequence b alone (only its pages gathered)."""
+    cu, table, ctx = npi(batch.cu_seqlens), npi(batch.block_table), npi(batch.ctx_lens)
+    pages = table[b][table[b] >= 0]
+    sub_t = np.full_like(table[b:b + 1], -1)
+    sub_t[0, :len(pages)] = np.arange(len(pages))
+    rows = slice(cu[b], cu[b + 1])
+    return oracle.verify_attention(
+        np64(lay['q'][rows]), np64(lay['k_new'][rows]), np64(lay['v_new'][rows]),
+        np64(lay['k_cache'][torch.from_numpy(pages).to(DEV)]),
+        np64(lay['v_cache'][torch.from_numpy(pages).to(DEV)]), sub_t, ctx[b:b + 1],
+        np.array([0, cu[b + 1] - cu[b]]), batch.P), rows
+
+
 def _check(w, batch, lay, seqs=None):
     out, kc, vc, err = _run(w, batch, lay)
     assert err == 0, err
@@ -49,15 +63,7 @@ def _check(w, batch, lay, seqs=None):
     else:
         e = 0.0
         for b in seqs:    # one sequence at a time: gather only its pages
-            pages = table[b][table[b] >= 0]
-            sub_t = np.full_like(table[b:b + 1], -1)
-            sub_t[0, :len(pages)] = np.arange(len(pages))
-            rows = slice(cu[b], cu[b + 1])
-            ref = oracle.verify_attention(
-                np64(lay['q'][rows]), np64(lay['k_new'][rows]), np64(lay['v_new'][rows]),
-                np64(lay['k_cache'][torch.from_numpy(pages).to(DEV)]),
-                np64(lay['v_cache'][torch.from_numpy(pages).to(DEV)]), sub_t, ctx[b:b + 1],
-                np.array([0, cu[b + 1] - cu[b]]), batch.P)
+            ref, rows = _seq_ref(lay, batch, b)
             e = max(e, check_attn_out(np64(out[rows]), ref, lay['q'].dtype))
     # the append, bit for bit over the whole pool
     k_exp, v_exp = oracle.append_kv(bits(lay['k_cache']), bits(lay['v_cache']),
@@ -160,6 +166,25 @@ def test_bad_page_and_capacity_are_flagged():
     rows = slice(int(batch.cu_seqlens[2]), int(batch.cu_seqlens[3]))
     assert torch.isnan(out[rows].float()).all()     # skipped sequence untouched
 
+
+
+def test_skipped_sequence_inside_a_workgroup_range():
+    # long contexts: each resident workgroup streams tens of tiles, so ranges
+    # run across the skipped sequence (no tiles) from one valid one to the next
+    w = wl.Workload('skip_mid', B=5, k=3, ragged_k=False, ctx=(20000, 30000))
+    batch = wl.make_batch(w, 91, DEV)
+    lay = wl.make_attn_layer(w, batch, 92, DEV)
+    c2 = batch.ctx_lens.clone()
+    c2[2] = batch.block_table.shape[1] * batch.P    # ctx + T overflows the table
+    b2 = wl.Batch(**{**batch.__dict__, 'ctx_lens': c2})
+    say('skip_mid: B=5, ctx', npi(c2).tolist())
+    out, _, _, err = _run(w, b2, lay)
+    assert err == 2
+    cu = npi(batch.cu_seqlens)
+    assert torch.isnan(out[int(cu[2]):int(cu[3])].float()).all()
+    for b in (0, 1, 3, 4):
+        ref, rows = _seq_ref(lay, batch, b)
+        check_attn_out(np64(out[rows]), ref, lay['q'].dtype)
 
 
 def test_repeated_calls_on_one_workspace_are_identical():
