@@ -25,6 +25,7 @@
 // stride-256 element loads, so any V and any row alignment is supported.
 
 #include "device_common.h"
+#include "exp2_table.h"
 #include "internal.h"
 
 namespace sv {
@@ -42,7 +43,8 @@ __host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChun
 // fma steps with ln 2 split into a double and its remainder),
 //   exp(x) = 2^(k >> 8) * 2^((k & 255) / 256) * (1 + p(r)),
 // p the degree-5 Taylor polynomial of exp(r) - 1 (remainder below 1e-20
-// relative).  The 256 table entries are filled per block with exp2.
+// relative).  Each block copies the 256 entries 2^(j/256) (correctly rounded
+// doubles, exp2_table.h) into LDS.
 // Every step is a full-rate fp64 or integer operation: adding 1.5 * 2^52 to
 // x * 256 / ln 2 (in one fma) rounds it to the nearest integer, ties to even,
 // and leaves that integer in the low word of the sum; the power 2^(k >> 8) is
@@ -51,11 +53,9 @@ __host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChun
 // (e^-700 < 2^-1009, far under the last bit of any sum that holds the row
 // maximum's weight, which is 1), as it is for -inf and NaN.
 constexpr int kExpTab = 256;
-constexpr int kChunksPerWg = 1;  // chunks of one row a workgroup covers
 
 __device__ __forceinline__ void exp_table_init(double* tab) {
-  for (int j = threadIdx.x; j < kExpTab; j += blockDim.x)
-    tab[j] = exp2(static_cast<double>(j) / kExpTab);
+  for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) tab[j] = kExp2Tab[j];
 }
 
 __device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
@@ -232,49 +232,45 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
 // Row r < total_T: target row r; otherwise draft row r - total_T.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
-  const int r = blockIdx.y;
+  const int chunk = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int nc = n_chunks(a.V);
+  const int nc = gridDim.x;
   const void* src = r < a.total_T ? a.target : a.draft;
   const size_t base = static_cast<size_t>(r < a.total_T ? r : r - a.total_T) * a.V;
+  float vals[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
+    vals[e] = ld<T>(src, base + min(chunk * kChunk + e * kThreads + tid, a.V - 1));
   __shared__ float redm[kThreads / 64];
   __shared__ double reds[kThreads / 64];
   __shared__ double tab[kExpTab];
-  exp_table_init(tab);  // read after the first barrier below
-  const int c_end = min(nc, (static_cast<int>(blockIdx.x) + 1) * kChunksPerWg);
-  for (int chunk = blockIdx.x * kChunksPerWg; chunk < c_end; ++chunk) {
-    float vals[kPerThread];
-    float m = -INFINITY;
+  exp_table_init(tab);  // read after the barrier below
+  float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
-      vals[e] = ld<T>(src, base + min(chunk * kChunk + e * kThreads + tid, a.V - 1));
+  for (int e = 0; e < kPerThread; ++e) {
+    if (chunk * kChunk + e * kThreads + tid >= a.V) vals[e] = -INFINITY;
+    m = fmaxf(m, vals[e]);
+  }
+  m = wave_max_f32(m);
+  if ((tid & 63) == 0) redm[tid >> 6] = m;
+  __syncthreads();
+  m = redm[0];
+  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, redm[w]);
+  double s = 0.0;
+  if (m > -INFINITY) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      if (chunk * kChunk + e * kThreads + tid >= a.V) vals[e] = -INFINITY;
-      m = fmaxf(m, vals[e]);
-    }
-    m = wave_max_f32(m);
-    if ((tid & 63) == 0) redm[tid >> 6] = m;
-    __syncthreads();
-    m = redm[0];
-    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, redm[w]);
-    double s = 0.0;
-    if (m > -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e)
-        s += exp_nonpos(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
-    }
-    s = wave_sum_f64(s);
-    if ((tid & 63) == 0) reds[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) {
-      s = reds[0];
-      for (int w = 1; w < kThreads / 64; ++w) s += reds[w];
-      const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
-      reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats)
-          [static_cast<size_t>(r) * nc + chunk] = make_double2(static_cast<double>(m), s);
-    }
-    __syncthreads();  // redm and reds are rewritten by the next chunk
+    for (int e = 0; e < kPerThread; ++e)
+      s += exp_nonpos(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
+  }
+  s = wave_sum_f64(s);
+  if ((tid & 63) == 0) reds[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    s = reds[0];
+    for (int w = 1; w < kThreads / 64; ++w) s += reds[w];
+    const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+    reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats)
+        [static_cast<size_t>(r) * nc + chunk] = make_double2(static_cast<double>(m), s);
   }
 }
 
@@ -396,35 +392,30 @@ __device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
-  const int b = blockIdx.y, tid = threadIdx.x;
-  const int nc = n_chunks(a.V);
+  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
   const int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
   if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
+  float2 lg[kPerThread];
+  load_draw_logits<T>(a, d.y, d.z, d.w, chunk * kChunk + tid, kThreads, lg);
   __shared__ double tab[kExpTab];
   __shared__ double red[kThreads / 64];
   exp_table_init(tab);
   __syncthreads();
-  const int c_end = min(nc, (static_cast<int>(blockIdx.x) + 1) * kChunksPerWg);
-  for (int chunk = blockIdx.x * kChunksPerWg; chunk < c_end; ++chunk) {
-    float2 lg[kPerThread];
-    load_draw_logits<T>(a, d.y, d.z, d.w, chunk * kChunk + tid, kThreads, lg);
-    double s = 0.0;
+  double s = 0.0;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      s += draw_weight(a, d.y, d.w, f, rz, chunk * kChunk + e * kThreads + tid, lg[e], tab);
-    s = wave_sum_f64(s);
-    if ((tid & 63) == 0) red[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) {
-      s = red[0];
-      for (int w = 1; w < kThreads / 64; ++w) s += red[w];
-      reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum)
-          [static_cast<size_t>(b) * nc + chunk] = s;
-    }
-    __syncthreads();  // red is rewritten by the next chunk
+  for (int e = 0; e < kPerThread; ++e)
+    s += draw_weight(a, d.y, d.w, f, rz, chunk * kChunk + e * kThreads + tid, lg[e], tab);
+  s = wave_sum_f64(s);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    s = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) s += red[w];
+    reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum)
+        [static_cast<size_t>(b) * gridDim.x + chunk] = s;
   }
 }
 
@@ -578,10 +569,9 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
   } else {
     const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
-    const int ncw = (nc + kChunksPerWg - 1) / kChunksPerWg;
-    hipLaunchKernelGGL((row_stats_partial<T>), dim3(ncw, rows), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((row_stats_partial<T>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(64), 0, stream, a);
-    hipLaunchKernelGGL((residual_partial<T>), dim3(ncw, a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((final_draw<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
