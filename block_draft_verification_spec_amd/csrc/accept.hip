@@ -154,8 +154,17 @@ __device__ __forceinline__ bool seq_ok(const AcceptArgs& a, int b, int* x0, int*
 __device__ void write_outputs(const AcceptArgs& a, int b, int x0, int acc, int y) {
   const int d0 = x0 - b;
   int32_t* row = a.result + a.B + static_cast<size_t>(b) * a.max_T;
-  for (int j = 0; j < a.max_T; ++j)
-    row[j] = j < acc ? a.draft_tokens[d0 + j] : (j == acc ? y : -1);
+  // the accepted drafts, every load issued before the first store (indices
+  // clamped into the draft array, which is non-empty whenever acc > 0)
+  const int n_drafts = a.total_T - a.B;
+  int tok[kMaxT] = {};
+  if (n_drafts > 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxT; ++j) tok[j] = a.draft_tokens[min(d0 + j, n_drafts - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j)
+    if (j < a.max_T) row[j] = j < acc ? tok[j] : (j == acc ? y : -1);
   a.result[b] = acc;
   if (a.commit_len_out) a.commit_len_out[b] = acc + 1;
   if (a.ctx_lens) a.ctx_lens[b] += acc + 1;
@@ -289,67 +298,91 @@ __device__ double2 row_norm(const double2* stats, int row, int nc, int lane) {
   return make_double2(M, Z);
 }
 
+// Per sequence, 256 threads: every input of the decisions is fetched in
+// parallel (draft tokens, uniforms and the logits at the drafts by wave 0,
+// the row normalisers by the four waves in turn), then thread 0 runs the
+// sequential accept test from LDS.
 template <typename T>
-__global__ __launch_bounds__(64) void decide_reject(AcceptArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void decide_reject(AcceptArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
   int4* dec = reinterpret_cast<int4*>(static_cast<char*>(a.ws) + L.dec);
   int x0, tn;
   if (!seq_ok(a, b, &x0, &tn)) {
-    if (lane == 0) {
+    if (tid == 0) {
       flag_error(a.err, SV_DERR_SEQLEN);
       dec[b] = make_int4(-1, -1, -1, -1);
     }
     return;
   }
   const int d0 = x0 - b;
-  for (int i = 0; i + 1 < tn; ++i) {
-    const int x = a.draft_tokens[d0 + i];
-    if (x < 0 || x >= a.V) {
-      if (lane == 0) {
-        flag_error(a.err, SV_DERR_TOKEN);
-        dec[b] = make_int4(-1, -1, -1, -1);
-      }
-      return;
-    }
+  const int nd = tn - 1;  // drafts
+  __shared__ int xs[kMaxT];
+  __shared__ float lt_s[kMaxT], lq_s[kMaxT], u_s[kMaxT];
+  __shared__ double2 nt_s[kMaxT], nd_s[kMaxT];
+  __shared__ int bad_s;
+  if (tid == 0) bad_s = 0;
+  __syncthreads();
+  if (w == 0 && lane < nd) {
+    const int x = a.draft_tokens[d0 + lane];
+    const float u = a.u_accept[d0 + lane];
+    const bool ok = x >= 0 && x < a.V;
+    const int xc = ok ? x : 0;
+    const float lt = ld<T>(a.target, static_cast<size_t>(x0 + lane) * a.V + xc);
+    const float lq = a.draft ? ld<T>(a.draft, static_cast<size_t>(d0 + lane) * a.V + xc) : 0.f;
+    xs[lane] = x;
+    u_s[lane] = u;
+    lt_s[lane] = lt;
+    lq_s[lane] = lq;
+    if (!ok) bad_s = 1;
   }
   const int nc = n_chunks(a.V);
   const double2* stats = reinterpret_cast<const double2*>(static_cast<const char*>(a.ws) + L.stats);
-  double4* fin = reinterpret_cast<double4*>(static_cast<char*>(a.ws) + L.fin);
-  for (int i = 0; i + 1 < tn; ++i) {
-    const int x = a.draft_tokens[d0 + i];
-    const double2 nt = row_norm(stats, x0 + i, nc, lane);
-    const double p = exp(static_cast<double>(ld<T>(a.target, static_cast<size_t>(x0 + i) * a.V + x)) - nt.x) / nt.y;
-    double q = 1.0;  // point-mass draft distribution when no draft logits are given
-    double2 nd = make_double2(0.0, 0.0);
-    if (a.draft) {
-      nd = row_norm(stats, a.total_T + d0 + i, nc, lane);
-      q = exp(static_cast<double>(ld<T>(a.draft, static_cast<size_t>(d0 + i) * a.V + x)) - nd.x) / nd.y;
+  // rows: target rows 0..nd (the last one for the bonus draw), then draft rows
+  const int n_rows = tn + (a.draft ? nd : 0);
+  for (int r = w; r < n_rows; r += kThreads / 64) {
+    const int row = r < tn ? x0 + r : a.total_T + d0 + (r - tn);
+    const double2 v = row_norm(stats, row, nc, lane);
+    if (lane == 0) {
+      if (r < tn) nt_s[r] = v;
+      else nd_s[r - tn] = v;
     }
-    const double u = static_cast<double>(a.u_accept[d0 + i]);
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  if (bad_s) {
+    flag_error(a.err, SV_DERR_TOKEN);
+    dec[b] = make_int4(-1, -1, -1, -1);
+    return;
+  }
+  double4* fin = reinterpret_cast<double4*>(static_cast<char*>(a.ws) + L.fin);
+  for (int i = 0; i < nd; ++i) {
+    const double2 nt = nt_s[i];
+    const double p = exp(static_cast<double>(lt_s[i]) - nt.x) / nt.y;
+    double q = 1.0;  // point-mass draft distribution when no draft logits are given
+    double2 ndv = make_double2(0.0, 0.0);
+    if (a.draft) {
+      ndv = nd_s[i];
+      q = exp(static_cast<double>(lq_s[i]) - ndv.x) / ndv.y;
+    }
+    const double u = static_cast<double>(u_s[i]);
     if (!(u * q < p)) {
-      if (lane == 0) {
-        // kind 1: residual max(0, p - q); kind 2: p without the draft token
-        dec[b] = a.draft ? make_int4(i, 1, x0 + i, d0 + i) : make_int4(i, 2, x0 + i, x);
-        fin[b] = make_double4(nt.x, nt.y, nd.x, nd.y);
-      }
+      // kind 1: residual max(0, p - q); kind 2: p without the draft token
+      dec[b] = a.draft ? make_int4(i, 1, x0 + i, d0 + i) : make_int4(i, 2, x0 + i, xs[i]);
+      fin[b] = make_double4(nt.x, nt.y, ndv.x, ndv.y);
       return;
     }
   }
   if (a.bonus) {  // every draft accepted: the supplied bonus, no draw
     const int y = a.bonus[b];
-    if (lane == 0) {
-      if (y < 0 || y >= a.V) flag_error(a.err, SV_DERR_TOKEN);
-      else write_outputs(a, b, x0, tn - 1, y);
-      dec[b] = make_int4(-1, -1, -1, -1);
-    }
+    if (y < 0 || y >= a.V) flag_error(a.err, SV_DERR_TOKEN);
+    else write_outputs(a, b, x0, tn - 1, y);
+    dec[b] = make_int4(-1, -1, -1, -1);
     return;
   }
-  const double2 nt = row_norm(stats, x0 + tn - 1, nc, lane);
-  if (lane == 0) {
-    dec[b] = make_int4(tn - 1, 0, x0 + tn - 1, -1);   // kind 0: target row
-    fin[b] = make_double4(nt.x, nt.y, 0.0, 0.0);
-  }
+  const double2 nt = nt_s[tn - 1];
+  dec[b] = make_int4(tn - 1, 0, x0 + tn - 1, -1);   // kind 0: target row
+  fin[b] = make_double4(nt.x, nt.y, 0.0, 0.0);
 }
 
 // Logits of vocabulary entry y (clamped into the row, so the load is always
@@ -448,10 +481,15 @@ __device__ int chunk_search(const AcceptArgs& a, int kind, int rt, int rd, const
   __syncthreads();
   if (tid == 0) {   // exclusive prefix over the 256 thread sums, in order
     double run = base;
-    for (int i = 0; i < kThreads; ++i) {
-      const double v = pre[i];
-      pre[i] = run;
-      run += v;
+    for (int i = 0; i < kThreads; i += 8) {  // eight LDS reads in flight
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = pre[i + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pre[i + j] = run;
+        run += v[j];
+      }
     }
   }
   __syncthreads();
@@ -470,11 +508,45 @@ __device__ int chunk_search(const AcceptArgs& a, int kind, int rt, int rd, const
   return found == 0x7fffffff ? -1 : found;
 }
 
+// Thread 0 walks v[0..n) in index order, staged through LDS 256 entries at a
+// time (every thread loads one), so the walk reads LDS rather than waiting on
+// one global load per entry.  Without t: returns the sum.  With t: returns the
+// first index c whose running sum before it plus v[c] exceeds t with v[c] > 0
+// (-1 if none), and that running sum in *base.  The result is valid in
+// thread 0; block-wide call.
+__device__ double ordered_walk(const double* v, int n, double* stage, bool search, double t,
+                               int* found, double* base) {
+  const int tid = threadIdx.x;
+  double run = 0.0;
+  bool done = false;
+  if (tid == 0) *found = -1;
+  for (int c0 = 0; c0 < n; c0 += kThreads) {
+    const int m = min(kThreads, n - c0);
+    if (tid < m) stage[tid] = v[c0 + tid];
+    __syncthreads();
+    if (tid == 0 && !done) {
+      for (int i = 0; i < m; ++i) {
+        const double x = stage[i];
+        if (search && run + x > t && x > 0.0) {
+          *found = c0 + i;
+          *base = run;
+          done = true;
+          break;
+        }
+        run += x;
+      }
+    }
+    __syncthreads();
+  }
+  return run;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
   int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
+  const float u_fin = a.u_final[b];
   if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
@@ -483,10 +555,12 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   const int nc = n_chunks(a.V);
   double* csum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum) + static_cast<size_t>(b) * nc;
   __shared__ double total_s;
-  if (tid == 0) {
-    double tot = 0.0;
-    for (int c = 0; c < nc; ++c) tot += csum[c];
-    total_s = tot;
+  __shared__ double stage[kThreads];
+  __shared__ int chunk_s;
+  __shared__ double base_s;
+  {
+    const double tot = ordered_walk(csum, nc, stage, false, 0.0, &chunk_s, &base_s);
+    if (tid == 0) total_s = tot;
   }
   __syncthreads();
   double total = total_s;
@@ -511,33 +585,17 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
       }
       __syncthreads();
     }
-    if (tid == 0) {
-      double tot = 0.0;
-      for (int c = 0; c < nc; ++c) tot += csum[c];
-      total_s = tot;
+    {
+      const double tot = ordered_walk(csum, nc, stage, false, 0.0, &chunk_s, &base_s);
+      if (tid == 0) total_s = tot;
     }
     __syncthreads();
     total = total_s;
   }
-  const double t = static_cast<double>(a.u_final[b]) * total;
+  const double t = static_cast<double>(u_fin) * total;
   // chunk whose inclusive running sum first exceeds t
-  __shared__ int chunk_s;
-  __shared__ double base_s;
-  if (tid == 0) {
-    double run = 0.0;
-    int cidx = -1;
-    double base = 0.0;
-    for (int c = 0; c < nc; ++c) {
-      if (run + csum[c] > t && csum[c] > 0.0) {
-        cidx = c;
-        base = run;
-        break;
-      }
-      run += csum[c];
-    }
-    chunk_s = cidx;
-    base_s = base;
-  }
+  if (tid == 0) base_s = 0.0;
+  ordered_walk(csum, nc, stage, true, t, &chunk_s, &base_s);
   __syncthreads();
   int y = -1;
   int chunk = chunk_s;
@@ -554,11 +612,7 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
     y = chunk_search<T>(a, d.y, d.z, d.w, f, rz, tab, chunk, base_s, t, &lastp);
     if (y < 0) y = lastp;
   }
-  if (tid == 0) {
-    int x0, tn;
-    seq_ok(a, b, &x0, &tn);
-    write_outputs(a, b, x0, d.x, y);
-  }
+  if (tid == 0) write_outputs(a, b, d.z - d.x, d.x, y);  // d.z - d.x = first row x0
 }
 
 template <typename T>
@@ -570,7 +624,7 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
   } else {
     const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
     hipLaunchKernelGGL((row_stats_partial<T>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((final_draw<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
   }
