@@ -94,6 +94,34 @@ def test_widths(K):
     _expect_state(st, S)
 
 
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_odd_channels_and_misaligned_input(misaligned):
+    """C not a multiple of 4 (C = 7), or x one element off 16-byte alignment:
+    same oracle bar."""
+    w0 = wl.WORKLOADS[0]
+    geo = {'dk': 3, 'dv': 1, 'H': 1} if not misaligned else {}
+    w = wl.Workload(**{**w0.__dict__, **geo, 'B': 5, 'k': 7, 'ragged_k': True,
+                       'ctx_fixed': None, 'ctx': (10, 20)})
+    batch = wl.make_batch(w, 51, DEV)
+    c = wl.make_conv_layer(w, batch, 52, DEV)
+    commit = wl.make_commit_len(batch, 53, device=DEV)
+    if misaligned:
+        buf = torch.empty(c['x'].numel() + 1, dtype=c['x'].dtype, device=DEV)
+        xm = buf[1:].view_as(c['x'])
+        xm.copy_(c['x'])
+        c = {**c, 'x': xm}
+    say('conv odd/misaligned: C', w.conv_C, 'misaligned', misaligned)
+    out, st, err = _run(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit, silu=True)
+    assert err == 0
+    y, S = _oracle(batch, c, bd.SV_GDN_VERIFY_COMMIT, commit, silu=True)
+    check_gdn_out(np64(out), y, torch.float32)
+    _expect_state(st, S)
+    if misaligned:   # an aligned copy of x gives the same bits
+        c_al = {**c, 'x': c['x'].clone()}
+        out_al, st_al, _ = _run(batch, c_al, bd.SV_GDN_VERIFY_COMMIT, commit, silu=True)
+        assert torch.equal(out_al, out) and torch.equal(st_al, st)
+
+
 def test_modes_agree_and_zero_commit_keeps_state():
     w = wl.WORKLOADS[3]
     batch = wl.make_batch(w, 21, DEV)
