@@ -385,7 +385,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f'bench.py runs on one GPU only (asked for --gpus {args.gpus}): this '
-              'library has no multi-GPU path; see DESIGN.md for how the step would shard.',
+              'library has no multi-GPU path (the step shards by sequence: each GPU would run '
+              'this step on its own sequences, KV pool and state slots).',
               file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
