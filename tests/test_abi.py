@@ -76,6 +76,10 @@ def test_attention_validation():
     assert call(dt=7) == bd.SV_EDTYPE
     assert call(Hq=64, Hkv=2) == bd.SV_ECAPACITY             # 32 heads x 4 > 64 rows
     assert call(q=24) == bd.SV_EINVAL                        # misaligned
+    b2049 = _batch(B=2049, max_T=4, total_T=2049 * 4)
+    assert L.spec_verify_attention(
+        ctypes.byref(b2049), 16, 16, 16, 16, 16, 16, 4, 8, 64, 16, 16, 32, 8, 128, bd.SV_BF16,
+        0.0, 1, 16, 1 << 30, None, None) == bd.SV_ECAPACITY   # more than 2048 sequences
     assert call() == bd.SV_EWORKSPACE                        # workspace too small
     assert 'workspace' in L.sv_last_error().decode()
 

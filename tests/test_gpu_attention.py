@@ -168,6 +168,26 @@ def test_bad_page_and_capacity_are_flagged():
 
 
 
+def test_largest_batch():
+    # 2048 sequences (the bf16 path's limit): every thread of the start-up
+    # scan owns eight sequences; ragged drafts, short contexts
+    w = wl.Workload('b2048', B=2048, k=7, ragged_k=True, ctx=(0, 100))
+    batch = wl.make_batch(w, 95, DEV)
+    lay = wl.make_attn_layer(w, batch, 96, DEV)
+    say('largest batch: B', batch.B, 'total_T', batch.total_T)
+    out, kc, vc, err = _run(w, batch, lay)
+    assert err == 0
+    for b in (0, 1, 255, 256, 511, 1000, 1023, 1024, 1500, 1791, 2000, 2040, 2045, 2046, 2047, 7):
+        ref, rows = _seq_ref(lay, batch, b)
+        check_attn_out(np64(out[rows]), ref, lay['q'].dtype)
+    cu, table, ctx = npi(batch.cu_seqlens), npi(batch.block_table), npi(batch.ctx_lens)
+    k_exp, v_exp = oracle.append_kv(bits(lay['k_cache']), bits(lay['v_cache']),
+                                    bits(lay['k_new']), bits(lay['v_new']), table, ctx, cu,
+                                    batch.P)
+    assert np.array_equal(bits(kc), k_exp)
+    assert np.array_equal(bits(vc), v_exp)
+
+
 def test_skipped_sequence_inside_a_workgroup_range():
     # long contexts: each resident workgroup streams tens of tiles, so ranges
     # run across the skipped sequence (no tiles) from one valid one to the next
