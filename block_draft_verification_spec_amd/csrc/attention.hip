@@ -236,6 +236,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   for (int ww = 0; ww < w; ++ww) excl += s_scan[ww];
   const int N = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
   const int W = gridDim.x, wg = blockIdx.x;
+  if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = N;  // for the combine launch
   const int t_lo = static_cast<int>(static_cast<long long>(wg) * N / W);
   const int t_hi = static_cast<int>(static_cast<long long>(wg + 1) * N / W);
   // the sequence whose tiles hold t_lo: the one thread owning it says so
@@ -746,6 +747,11 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   const int s = b * a.Hkv + g;
   const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
   if (wf >= wl_) return;  // one piece: written by the stream kernel
+  // With fewer tiles than workgroups some ranges [w N / W, (w + 1) N / W)
+  // are empty; such a workgroup between wf and wl wrote no piece (its slot
+  // holds another call's data) and is skipped.
+  const long long Nt = a.seg_meta[2 * a.B * a.Hkv], Wn = a.n_wg;
+  auto empty = [&](int w) { return w * Nt / Wn == (w + 1) * Nt / Wn; };
   const int m = j * G + (h - g * G);
   float acc[D / 64];
 #pragma unroll
@@ -757,7 +763,7 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kFew; ++i) {
       pm[i] = -INFINITY;
-      if (wf + i > wl_) continue;
+      if (wf + i > wl_ || empty(wf + i)) continue;
       const size_t pi = static_cast<size_t>(s + wf + i) * kMaxRows + m;
       pm[i] = a.part_ml[2 * pi];
       pl[i] = a.part_ml[2 * pi + 1];
@@ -778,8 +784,9 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   } else {
     float mm = -INFINITY;
     for (int wg = wf; wg <= wl_; ++wg)
-      mm = fmaxf(mm, a.part_ml[2 * (static_cast<size_t>(s + wg) * kMaxRows + m)]);
+      if (!empty(wg)) mm = fmaxf(mm, a.part_ml[2 * (static_cast<size_t>(s + wg) * kMaxRows + m)]);
     for (int wg = wf; wg <= wl_; ++wg) {
+      if (empty(wg)) continue;
       const size_t pi = static_cast<size_t>(s + wg) * kMaxRows + m;
       const float ms = a.part_ml[2 * pi];
       if (ms == -INFINITY) continue;
@@ -974,7 +981,7 @@ size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D, int max_
   (void)P;
   if (dtype != SV_BF16) return 0;
   const size_t slots = static_cast<size_t>(B) * Hkv + stream_grid_max(D);
-  const size_t meta = (static_cast<size_t>(B) * Hkv * 2 * sizeof(int) + 255) & ~size_t(255);
+  const size_t meta = ((static_cast<size_t>(B) * Hkv * 2 + 1) * sizeof(int) + 255) & ~size_t(255);
   const size_t o_bytes = (slots * kMaxRows * D * sizeof(float) + 255) & ~size_t(255);
   return meta + o_bytes + slots * kMaxRows * 2 * sizeof(float);
 }
@@ -983,7 +990,7 @@ void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_m
                           float** part_o, float** part_ml) {
   (void)n_wg;
   const size_t slots = static_cast<size_t>(B) * Hkv + stream_grid_max(D);
-  const size_t meta = (static_cast<size_t>(B) * Hkv * 2 * sizeof(int) + 255) & ~size_t(255);
+  const size_t meta = ((static_cast<size_t>(B) * Hkv * 2 + 1) * sizeof(int) + 255) & ~size_t(255);
   const size_t o_bytes = (slots * kMaxRows * D * sizeof(float) + 255) & ~size_t(255);
   char* base = static_cast<char*>(ws);
   *seg_meta = reinterpret_cast<int*>(base);

@@ -104,7 +104,8 @@ struct AttnArgs {
   int32_t* err;
   // stream-kernel grid and the pieces of segments cut by range boundaries
   int n_wg;                     // workgroups (grid.x)
-  int* seg_meta;                // [B * Hkv][2]: first and last workgroup of a segment
+  int* seg_meta;                // [B * Hkv][2]: first and last workgroup of a segment,
+                                // then the launch's tile count
   float* part_o;                // [(B * Hkv + n_wg) * 64 rows][D]
   float* part_ml;               // [(B * Hkv + n_wg) * 64 rows][2]
 };

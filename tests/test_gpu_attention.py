@@ -26,7 +26,8 @@ def _run(w, batch, lay, table=None, kc=None, vc=None, write_kv=True):
     dt = bd.SV_BF16 if lay['q'].dtype == torch.bfloat16 else bd.SV_F32
     nbytes = bd.spec_verify_attention_workspace_bytes(
         batch.B, batch.total_T, w.Hq, w.Hkv, w.D, table.shape[1], batch.P, dt)
-    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    # garbage scratch: no result may depend on what the workspace held
+    ws = torch.full((max(nbytes, 1),), 0x7f, dtype=torch.uint8, device=DEV)
     err = err_word()
     bd.spec_verify_attention(sv_batch(batch), lay['q'], lay['k_new'], lay['v_new'], kc, vc,
                              table, batch.ctx_lens, out, write_kv=write_kv,
@@ -205,6 +206,38 @@ def test_skipped_sequence_inside_a_workgroup_range():
     for b in (0, 1, 3, 4):
         ref, rows = _seq_ref(lay, batch, b)
         check_attn_out(np64(out[rows]), ref, lay['q'].dtype)
+
+
+@pytest.mark.parametrize("seed", [5, 15])
+def test_fewer_tiles_than_workgroups_on_a_reused_workspace(seed):
+    # 2 sequences, 3-5 tiles per segment: far fewer tiles than resident
+    # workgroups, so a segment's tiles sit in workgroups with empty ranges
+    # between them; the workspace holds garbage, then another call's partials
+    w = wl.Workload('few', B=2, k=3, ragged_k=False, ctx=(150, 250))
+    batch = wl.make_batch(w, seed, DEV)
+    lay = wl.make_attn_layer(w, batch, seed + 1, DEV)
+    other = wl.make_attn_layer(w, batch, seed + 2, DEV)
+    nbytes = bd.spec_verify_attention_workspace_bytes(
+        batch.B, batch.total_T, w.Hq, w.Hkv, w.D, batch.block_table.shape[1], batch.P,
+        bd.SV_BF16)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device=DEV)   # garbage scratch
+    ref = oracle.verify_attention(np64(lay['q']), np64(lay['k_new']), np64(lay['v_new']),
+                                  np64(lay['k_cache']), np64(lay['v_cache']),
+                                  npi(batch.block_table), npi(batch.ctx_lens),
+                                  npi(batch.cu_seqlens), batch.P)
+    say('few tiles, reused workspace, seed', seed)
+    for src in (None, other):
+        if src is not None:   # leave another call's partials in the workspace
+            bd.spec_verify_attention(sv_batch(batch), src['q'], src['k_new'], src['v_new'],
+                                     src['k_cache'].clone(), src['v_cache'].clone(),
+                                     batch.block_table, batch.ctx_lens,
+                                     torch.empty_like(src['q']), workspace=ws)
+        out = torch.full_like(lay['q'], float('nan'))
+        bd.spec_verify_attention(sv_batch(batch), lay['q'], lay['k_new'], lay['v_new'],
+                                 lay['k_cache'].clone(), lay['v_cache'].clone(),
+                                 batch.block_table, batch.ctx_lens, out, workspace=ws)
+        torch.cuda.synchronize()
+        check_attn_out(np64(out), ref, lay['q'].dtype)
 
 
 def test_repeated_calls_on_one_workspace_are_identical():

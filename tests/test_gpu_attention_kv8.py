@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 def _ws(w, batch, table):
     n = bd.spec_verify_attention_workspace_bytes(batch.B, batch.total_T, w.Hq, w.Hkv, w.D,
                                                  table.shape[1], batch.P, bd.SV_BF16)
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
+    # garbage scratch: no result may depend on what the workspace held
+    return torch.full((max(n, 1),), 0x7f, dtype=torch.uint8, device=DEV)
 
 
 def _run(w, batch, lay, table=None, ctx=None):
