@@ -746,12 +746,14 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   const int g = h / G;
   const int s = b * a.Hkv + g;
   const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
+  const int Ntiles = a.seg_meta[2 * a.B * a.Hkv];
   if (wf >= wl_) return;  // one piece: written by the stream kernel
   // With fewer tiles than workgroups some ranges [w N / W, (w + 1) N / W)
   // are empty; such a workgroup between wf and wl wrote no piece (its slot
   // holds another call's data) and is skipped.
-  const long long Nt = a.seg_meta[2 * a.B * a.Hkv], Wn = a.n_wg;
-  auto empty = [&](int w) { return w * Nt / Wn == (w + 1) * Nt / Wn; };
+  const long long Nt = Ntiles, Wn = a.n_wg;
+  const bool sparse = Nt < Wn;
+  auto empty = [&](int w) { return sparse && w * Nt / Wn == (w + 1) * Nt / Wn; };
   const int m = j * G + (h - g * G);
   float acc[D / 64];
 #pragma unroll
