@@ -139,19 +139,27 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 // --------------------------------------------------------------------------
 // Work split: the (sequence, KV head) segments are laid end to end as one
 // sequence of N 64-key tiles (segment s = b * Hkv + g holds the tiles of
-// sequence b, head g, in position order), and workgroup w of W streams the
-// contiguous range [w N / W, (w + 1) N / W).  Every workgroup gets the same
-// number of tiles whatever the context lengths, and pays its start-up once.
-// A segment cut by range boundaries is computed in pieces; piece (s, w) of a
-// segment writes its partial (max, sum, O) to slot s + w (distinct for every
-// piece, since segments advance with w) and the workgroup that owns the
-// segment's first tile records which workgroups cover the segment; a combine
-// kernel merges the pieces.  A segment covered by one workgroup is written
-// directly.
+// sequence b, head g, in position order).  Each segment is priced at its
+// tiles plus kPieceCost units for the set-up of a piece (bounds, Q, page
+// ids, a first tile with none in flight, and the write of its result);
+// the U units are split evenly, workgroup w of W taking units
+// [w U / W, (w + 1) U / W), and a unit range maps to the tiles it covers
+// (unit r of a segment is its tile max(r - kPieceCost, 0)).  So every
+// workgroup gets the same cost whatever the context lengths: one that starts
+// more segments streams fewer tiles.  A segment cut by range boundaries is
+// computed in pieces; piece (s, w) of a segment writes its partial
+// (max, sum, O) to slot s + w (distinct for every piece, since segments
+// advance with w) and the workgroup that owns the segment's first tile
+// records which workgroups cover the segment; a combine kernel merges the
+// pieces.  A segment covered by one workgroup is written directly.
 constexpr int kMaxB = 2048;        // sequences per call on the bf16 path
 constexpr int kChunkTiles = 256;   // tiles whose page ids are staged at once
 constexpr int kRound = 12;         // tiles per unrolled round (a multiple of PF)
 constexpr int kMaxRows = 64;       // query rows per (sequence, KV head)
+#ifndef SV_ATTN_PIECE_COST
+#define SV_ATTN_PIECE_COST 3
+#endif
+constexpr int kPieceCost = SV_ATTN_PIECE_COST;  // a piece's set-up, in tiles
 
 // One tile's slice of K and V held by a thread.
 template <int KPT>
@@ -160,9 +168,9 @@ struct TileRegs {
   u32x4_t v[KPT];
 };
 
-__host__ __device__ inline int piece_wg(int t, int W, int N) {
-  // the workgroup whose range [w N / W, (w + 1) N / W) holds tile t
-  return static_cast<int>(((static_cast<long long>(t) + 1) * W - 1) / N);
+__host__ __device__ inline int piece_wg(int u, int W, int U) {
+  // the workgroup whose range [w U / W, (w + 1) U / W) holds unit u
+  return static_cast<int>(((static_cast<long long>(u) + 1) * W - 1) / U);
 }
 
 // PF: tiles in flight per workgroup (a ring of register buffers; registers
@@ -182,9 +190,9 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKT * KS + D * VS];
   __shared__ float wm[4][ROWS];
   __shared__ float wl[4][ROWS];
-  __shared__ int s_first[2];                 // the sequence holding tile t_lo, its first tile
+  __shared__ int s_first[5];  // the sequence holding t_lo, its first tile and unit; t_lo, t_hi
   __shared__ int s_ids[kChunkTiles * 4];     // page ids of the current chunk
-  __shared__ int s_scan[kThreads / 64];
+  __shared__ int s_scan[2][kThreads / 64];
   uint16_t* Ks = lds;
   uint16_t* Vt = lds + kKT * KS;
   // V^T column swizzle: key k of row r sits at column k ^ vswz(r), a multiple
@@ -211,49 +219,70 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   for (int i = 0; i <= kPer; ++i) asm volatile("" : "+v"(cuv[i]));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(lv[i]));
-  int part[kPer];
-  int run = 0;
+  int nts[kPer];  // tiles per segment of each sequence (0: no tiles)
+  int run = 0, urun = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = tid * kPer + i;
-    int v = 0;
+    nts[i] = 0;
     if (b < B && attn_seq_valid(a, cuv[i], cuv[i + 1] - cuv[i], lv[i], blockIdx.x == 0))
-      v = seq_tiles(lv[i], cuv[i + 1] - cuv[i]) * Hkv;
-    run += v;
-    part[i] = run;
+      nts[i] = seq_tiles(lv[i], cuv[i + 1] - cuv[i]);
+    run += nts[i] * Hkv;
+    urun += nts[i] > 0 ? (nts[i] + kPieceCost) * Hkv : 0;
   }
-  // inclusive scan of the per-thread totals: within each wave by shuffles,
-  // then the totals of the waves before it
-  int inc = run;
+  // inclusive scans of the per-thread tile and unit totals: within each wave
+  // by shuffles, then the totals of the waves before it
+  int inc = run, uinc = urun;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += y;
+    const int y = __shfl_up(inc, off, 64), yu = __shfl_up(uinc, off, 64);
+    if (lane >= off) {
+      inc += y;
+      uinc += yu;
+    }
   }
-  if (lane == 63) s_scan[w] = inc;
+  if (lane == 63) {
+    s_scan[0][w] = inc;
+    s_scan[1][w] = uinc;
+  }
   __syncthreads();
-  int excl = inc - run;
-  for (int ww = 0; ww < w; ++ww) excl += s_scan[ww];
-  const int N = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+  int excl = inc - run, uexcl = uinc - urun;
+  for (int ww = 0; ww < w; ++ww) {
+    excl += s_scan[0][ww];
+    uexcl += s_scan[1][ww];
+  }
+  const int N = s_scan[0][0] + s_scan[0][1] + s_scan[0][2] + s_scan[0][3];
+  const int U = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
   const int W = gridDim.x, wg = blockIdx.x;
-  if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = N;  // for the combine launch
-  const int t_lo = static_cast<int>(static_cast<long long>(wg) * N / W);
-  const int t_hi = static_cast<int>(static_cast<long long>(wg + 1) * N / W);
-  // the sequence whose tiles hold t_lo: the one thread owning it says so
-  // (sequences without tiles own an empty range and never match)
+  if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = U;  // for the combine launch
+  const int u_lo = static_cast<int>(static_cast<long long>(wg) * U / W);
+  const int u_hi = static_cast<int>(static_cast<long long>(wg + 1) * U / W);
+  // the sequences whose units hold u_lo and u_hi: their owners map them to
+  // tiles (sequences without tiles own no units and never match; unit U maps
+  // to tile N)
   {
-    int pre = excl;
+    int pre = excl, upre = uexcl;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int end = excl + part[i];
-      if (t_lo >= pre && t_lo < end) {
+      const int nt = nts[i], uend = upre + (nt > 0 ? (nt + kPieceCost) * Hkv : 0);
+      auto tile_of = [&](int u) {
+        const int r = u - upre, h = r / (nt + kPieceCost);
+        return pre + h * nt + max(r - h * (nt + kPieceCost) - kPieceCost, 0);
+      };
+      if (u_lo >= upre && u_lo < uend) {
         s_first[0] = tid * kPer + i;
         s_first[1] = pre;
+        s_first[2] = upre;
+        s_first[3] = tile_of(u_lo);
       }
-      pre = end;
+      if (u_hi >= upre && u_hi < uend) s_first[4] = tile_of(u_hi);
+      pre += nt * Hkv;
+      upre = uend;
     }
   }
   __syncthreads();
+  const int t_lo = u_lo < U ? s_first[3] : N;
+  const int t_hi = u_hi < U ? s_first[4] : N;
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
@@ -470,6 +499,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   // Pieces in order: sequence cb (its first tile is cbase) and its Hkv
   // segments of nt_b tiles; past its last tile the next sequence with tiles.
   int cb = t_lo < t_hi ? s_first[0] : B, cbase = t_lo < t_hi ? s_first[1] : 0;
+  int ucbase = t_lo < t_hi ? s_first[2] : 0;  // sequence cb's first unit
   int nt_b = 0;
   bool next_seq = true;
   for (int t = t_lo; t < t_hi;) {
@@ -493,13 +523,15 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     const int s = b * Hkv + g;
     const bool whole = lt_begin == 0 && lt_end == nt_b;
     M = G * T;
-    if (lt_begin == 0 && tid == 0) {
+    if (lt_begin == 0 && tid == 0) {  // the segment's last tile is its unit kPieceCost + nt_b - 1
       a.seg_meta[2 * s] = wg;
-      a.seg_meta[2 * s + 1] = piece_wg(seg_start + nt_b - 1, W, N);
+      a.seg_meta[2 * s + 1] =
+          piece_wg(ucbase + g * (nt_b + kPieceCost) + kPieceCost + nt_b - 1, W, U);
     }
     t = seg_start + lt_end;
     if (t == cbase + Hkv * nt_b) {
       cbase = t;
+      ucbase += Hkv * (nt_b + kPieceCost);
       ++cb;
       next_seq = true;
     }
@@ -746,14 +778,16 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   const int g = h / G;
   const int s = b * a.Hkv + g;
   const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
-  const int Ntiles = a.seg_meta[2 * a.B * a.Hkv];
+  const int Units = a.seg_meta[2 * a.B * a.Hkv];
   if (wf >= wl_) return;  // one piece: written by the stream kernel
-  // With fewer tiles than workgroups some ranges [w N / W, (w + 1) N / W)
+  // With fewer cost units than workgroups some ranges [w U / W, (w + 1) U / W)
   // are empty; such a workgroup between wf and wl wrote no piece (its slot
-  // holds another call's data) and is skipped.
-  const long long Nt = Ntiles, Wn = a.n_wg;
-  const bool sparse = Nt < Wn;
-  auto empty = [&](int w) { return sparse && w * Nt / Wn == (w + 1) * Nt / Wn; };
+  // holds another call's data) and is skipped.  Between the units of the
+  // segment's first and last tiles every unit is a tile, so a non-empty unit
+  // range there is a non-empty piece.
+  const long long Un = Units, Wn = a.n_wg;
+  const bool sparse = Un < Wn;
+  auto empty = [&](int w) { return sparse && w * Un / Wn == (w + 1) * Un / Wn; };
   const int m = j * G + (h - g * G);
   float acc[D / 64];
 #pragma unroll

@@ -105,7 +105,7 @@ struct AttnArgs {
   // stream-kernel grid and the pieces of segments cut by range boundaries
   int n_wg;                     // workgroups (grid.x)
   int* seg_meta;                // [B * Hkv][2]: first and last workgroup of a segment,
-                                // then the launch's tile count
+                                // then the launch's count of cost units
   float* part_o;                // [(B * Hkv + n_wg) * 64 rows][D]
   float* part_ml;               // [(B * Hkv + n_wg) * 64 rows][2]
 };
