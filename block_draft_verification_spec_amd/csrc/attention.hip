@@ -160,6 +160,36 @@ constexpr int kMaxRows = 64;       // query rows per (sequence, KV head)
 #define SV_ATTN_PIECE_COST 3
 #endif
 constexpr int kPieceCost = SV_ATTN_PIECE_COST;  // a piece's set-up, in tiles
+// Share of the units by dispatch round.  Workgroups are placed in order, one
+// per compute unit per round, and a CU's older waves win its arbitration: at
+// three workgroups per CU and equal tile counts the one placed first finished
+// after 189 us, the second after 198 and the last after 229 (MI355X, 16
+// attention layers of 64 sequences with contexts of 2048 to 8192 keys).  The
+// CU's memory path, not the workgroup, sets the rate (the three together
+// stream as fast as a load-only kernel), so the youngest workgroup slows down
+// when given fewer tiles; shorter ranges for later rounds still measured
+// about 1 % faster per layer than equal ones.
+#ifndef SV_ATTN_ROUND_W
+#define SV_ATTN_ROUND_W 64, 61, 53, 53
+#endif
+constexpr int kRoundW[4] = {SV_ATTN_ROUND_W};
+constexpr int round_w_min() {
+  int m = kRoundW[0];
+  for (int i = 1; i < 4; ++i) m = kRoundW[i] < m ? kRoundW[i] : m;
+  return m;
+}
+__host__ __device__ inline int round_w(int r) { return kRoundW[r < 3 ? r : 3]; }
+// Weight of workgroups [0, w): n_cu workgroups per round.
+__host__ __device__ inline long long wg_weight(int w, int n_cu) {
+  long long s = 0;
+  int r = 0;
+  for (; (r + 1) * n_cu <= w; ++r) s += static_cast<long long>(n_cu) * round_w(r);
+  return s + static_cast<long long>(w - r * n_cu) * round_w(r);
+}
+// First unit of workgroup w: U S(w) / S(W).
+__host__ __device__ inline int wg_unit(int w, int W, int n_cu, int U) {
+  return static_cast<int>(static_cast<long long>(U) * wg_weight(w, n_cu) / wg_weight(W, n_cu));
+}
 
 // One tile's slice of K and V held by a thread.
 template <int KPT>
@@ -168,9 +198,17 @@ struct TileRegs {
   u32x4_t v[KPT];
 };
 
-__host__ __device__ inline int piece_wg(int u, int W, int U) {
-  // the workgroup whose range [w U / W, (w + 1) U / W) holds unit u
-  return static_cast<int>(((static_cast<long long>(u) + 1) * W - 1) / U);
+__host__ __device__ inline int piece_wg(int u, int W, int n_cu, int U) {
+  // the workgroup whose range [wg_unit(w), wg_unit(w + 1)) holds unit u: the
+  // last w with U S(w) < (u + 1) S(W), i.e. S(w) <= smax
+  const long long smax = ((static_cast<long long>(u) + 1) * wg_weight(W, n_cu) - 1) / U;
+  int r = 0;
+  long long base = 0;
+  while ((r + 1) * n_cu < W && base + static_cast<long long>(n_cu) * round_w(r) <= smax) {
+    base += static_cast<long long>(n_cu) * round_w(r);
+    ++r;
+  }
+  return min(r * n_cu + static_cast<int>((smax - base) / round_w(r)), W - 1);
 }
 
 // PF: tiles in flight per workgroup (a ring of register buffers; registers
@@ -255,8 +293,8 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   const int U = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
   const int W = gridDim.x, wg = blockIdx.x;
   if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = U;  // for the combine launch
-  const int u_lo = static_cast<int>(static_cast<long long>(wg) * U / W);
-  const int u_hi = static_cast<int>(static_cast<long long>(wg + 1) * U / W);
+  const int u_lo = wg_unit(wg, W, a.n_cu, U);
+  const int u_hi = wg_unit(wg + 1, W, a.n_cu, U);
   // the sequences whose units hold u_lo and u_hi: their owners map them to
   // tiles (sequences without tiles own no units and never match; unit U maps
   // to tile N)
@@ -526,7 +564,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     if (lt_begin == 0 && tid == 0) {  // the segment's last tile is its unit kPieceCost + nt_b - 1
       a.seg_meta[2 * s] = wg;
       a.seg_meta[2 * s + 1] =
-          piece_wg(ucbase + g * (nt_b + kPieceCost) + kPieceCost + nt_b - 1, W, U);
+          piece_wg(ucbase + g * (nt_b + kPieceCost) + kPieceCost + nt_b - 1, W, a.n_cu, U);
     }
     t = seg_start + lt_end;
     if (t == cbase + Hkv * nt_b) {
@@ -780,14 +818,17 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
   const int Units = a.seg_meta[2 * a.B * a.Hkv];
   if (wf >= wl_) return;  // one piece: written by the stream kernel
-  // With fewer cost units than workgroups some ranges [w U / W, (w + 1) U / W)
-  // are empty; such a workgroup between wf and wl wrote no piece (its slot
-  // holds another call's data) and is skipped.  Between the units of the
-  // segment's first and last tiles every unit is a tile, so a non-empty unit
-  // range there is a non-empty piece.
-  const long long Un = Units, Wn = a.n_wg;
-  const bool sparse = Un < Wn;
-  auto empty = [&](int w) { return sparse && w * Un / Wn == (w + 1) * Un / Wn; };
+  // With few cost units some ranges [wg_unit(w), wg_unit(w + 1)) are empty
+  // (never when every workgroup's share U w_r / S(W) is a unit or more); such
+  // a workgroup between wf and wl wrote no piece (its slot holds another
+  // call's data) and is skipped.  Between the units of the segment's first and
+  // last tiles every unit is a tile, so a non-empty unit range there is a
+  // non-empty piece.
+  const int W = a.n_wg, ncu = a.n_cu;
+  const bool sparse = static_cast<long long>(Units) * round_w_min() < wg_weight(W, ncu);
+  auto empty = [&](int w) {
+    return sparse && wg_unit(w, W, ncu, Units) == wg_unit(w + 1, W, ncu, Units);
+  };
   const int m = j * G + (h - g * G);
   float acc[D / 64];
 #pragma unroll
@@ -968,15 +1009,18 @@ const void* stream_kernel_for(int D, int nqt) {
 
 // Resident workgroups of one stream-kernel instance on the current device:
 // the grid that keeps every CU busy without a second wave of workgroups.
-int stream_grid(int D, int nqt, bool kv8) {
+int stream_grid(int D, int nqt, bool kv8, int* n_cu = nullptr) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, bool>, int> cache;
+  static std::map<std::tuple<int, int, int, bool>, std::pair<int, int>> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
   const auto key = std::make_tuple(dev, D, nqt, kv8);
   auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
+  if (it != cache.end()) {
+    if (n_cu) *n_cu = it->second.second;
+    return it->second.first;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
@@ -985,7 +1029,8 @@ int stream_grid(int D, int nqt, bool kv8) {
       per_cu < 1)
     per_cu = 1;
   const int n = cus * per_cu;
-  cache[key] = n;
+  cache[key] = {n, cus};
+  if (n_cu) *n_cu = cus;
   return n;
 }
 
@@ -1034,8 +1079,8 @@ void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_m
   *part_ml = reinterpret_cast<float*>(base + meta + o_bytes);
 }
 
-int attn_stream_grid(int D, int G, int max_T, bool kv8) {
-  return stream_grid(D, nqt_for(G, max_T), kv8);
+int attn_stream_grid(int D, int G, int max_T, bool kv8, int* n_cu) {
+  return stream_grid(D, nqt_for(G, max_T), kv8, n_cu);
 }
 
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype, hipStream_t stream) {
