@@ -239,17 +239,53 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
 
 // ------------------------------------------------------------------ rejection
 // Row r < total_T: target row r; otherwise draft row r - total_T.
+// Entries of one 16-byte load.
 template <typename T>
+constexpr int kVecN = 16 / static_cast<int>(sizeof(typename io<T>::storage));
+
+// VEC: the rows start 16-byte aligned and V is a multiple of kVecN<T>
+// (checked by the launcher), so a thread reads its kPerThread entries with
+// kPerThread / kVecN 16-byte loads, group l * kThreads + tid of the chunk;
+// otherwise one element load per entry at stride kThreads.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
   const int chunk = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x;
   const int nc = gridDim.x;
   const void* src = r < a.total_T ? a.target : a.draft;
   const size_t base = static_cast<size_t>(r < a.total_T ? r : r - a.total_T) * a.V;
+  constexpr int NV = VEC ? kVecN<T> : 1;
+  // vocabulary index of the thread's entry e
+  auto entry = [&](int e) { return chunk * kChunk + ((e / NV) * kThreads + tid) * NV + e % NV; };
   float vals[kPerThread];
+  if constexpr (VEC) {
+    // every load issued before any is used; a group past the row reads the
+    // row's last group and is masked below
+    using S = typename io<T>::storage;
+    const uint4* row = reinterpret_cast<const uint4*>(static_cast<const S*>(src) + base);
+    const int last = a.V / NV - 1;
+    uint4 raw[kPerThread / NV];
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
-    vals[e] = ld<T>(src, base + min(chunk * kChunk + e * kThreads + tid, a.V - 1));
+    for (int l = 0; l < kPerThread / NV; ++l)
+      raw[l] = row[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
+#pragma unroll
+    for (int l = 0; l < kPerThread / NV; ++l) {
+      const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (NV == 8) {  // two bf16 entries per word, the lower first
+          vals[l * NV + 2 * q] = __uint_as_float(w[q] << 16);
+          vals[l * NV + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        } else {
+          vals[l * NV + q] = __uint_as_float(w[q]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
+      vals[e] = ld<T>(src, base + min(entry(e), a.V - 1));
+  }
   __shared__ float redm[kThreads / 64];
   __shared__ double reds[kThreads / 64];
   __shared__ double tab[kExpTab];
@@ -257,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
   float m = -INFINITY;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    if (chunk * kChunk + e * kThreads + tid >= a.V) vals[e] = -INFINITY;
+    if (entry(e) >= a.V) vals[e] = -INFINITY;
     m = fmaxf(m, vals[e]);
   }
   m = wave_max_f32(m);
@@ -623,7 +659,14 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
   } else {
     const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
-    hipLaunchKernelGGL((row_stats_partial<T>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
+    using S = typename io<T>::storage;
+    const bool vec = (static_cast<size_t>(a.V) * sizeof(S)) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
+                     (!a.draft || reinterpret_cast<uintptr_t>(a.draft) % 16 == 0);
+    if (vec)
+      hipLaunchKernelGGL((row_stats_partial<T, true>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((row_stats_partial<T, false>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((final_draw<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
