@@ -47,11 +47,10 @@ __host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChun
 // doubles, exp2_table.h) into LDS.
 // Every step is a full-rate fp64 or integer operation: adding 1.5 * 2^52 to
 // x * 256 / ln 2 (in one fma) rounds it to the nearest integer, ties to even,
-// and leaves that integer in the low word of the sum; the power 2^(k >> 8) is
-// added to the exponent field of the table product, which lies in [1 - 2^-9,
-// 2) and so stays a normal number for x >= -700.  Below -700 the result is 0
-// (e^-700 < 2^-1009, far under the last bit of any sum that holds the row
-// maximum's weight, which is 1), as it is for -inf and NaN.
+// and leaves that integer in the low word of the sum; the power 2^(k >> 8)
+// is applied with one ldexp, exact while the result is normal (x above about
+// -708) and rounded once below, so the result underflows gradually to 0
+// near -745.  x is first clamped to -800, which maps -inf and NaN to 0.
 constexpr int kExpTab = 256;
 
 __device__ __forceinline__ void exp_table_init(double* tab) {
@@ -59,7 +58,7 @@ __device__ __forceinline__ void exp_table_init(double* tab) {
 }
 
 __device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
-  constexpr double kMin = -700.0;
+  constexpr double kMin = -800.0;
   constexpr double kShift = 0x1.8p52;
   constexpr double kInvStep = 256.0 / 0.693147180559945309417232121458176568;
   constexpr double kStepHi = 0x1.62e42fefa39efp-1 / 256.0;   // ln 2 rounded to double, / 256
@@ -73,9 +72,7 @@ __device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
   const double pr =
       r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0 + r * (1.0 / 120.0)))));
   const double t = tab[ki & (kExpTab - 1)];
-  const long long e = __double_as_longlong(fma(t, pr, t)) +
-                      (static_cast<long long>(ki >> 8) << 52);
-  return x >= kMin ? __longlong_as_double(e) : 0.0;
+  return ldexp(fma(t, pr, t), ki >> 8);
 }
 
 // Workspace layout (byte offsets are 256-aligned).
