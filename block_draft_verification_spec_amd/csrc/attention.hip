@@ -34,7 +34,8 @@
 // s per (KV head, channel) for K and for V.  A small kernel first writes the
 // in-flight rows' codes into their slots; the stream kernel then reads every
 // position from the pages (8 KiB per 64-key tile at D = 128, half the bf16
-// bytes), widens the codes to fp16 exactly on the way into LDS and runs the
+// bytes), widens each code c to the fp16 value 1152 + c (exact) on the way
+// into LDS, the constant taken off once per output, and runs the
 // same tiles with fp16 MFMAs: the K scale is folded into Q (q_d s_d rounded to
 // fp16), the V scale applied to the accumulated output channel.
 // fp32 path: one wave per (query token, head), plain VALU online softmax.
@@ -80,16 +81,17 @@ __device__ __forceinline__ uint32_t half16(u32x4_t u, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// Four int8 codes (one 32-bit word) -> four fp16 values, exactly: the byte
-// with its sign bit flipped is u = c + 128 in 0..255; placed under the fp16
-// exponent of 1024 it reads 1024 + u, and subtracting 1152 leaves c.
+// Four int8 codes (one 32-bit word) -> four fp16 values 1152 + c, exactly:
+// the byte with its sign bit flipped is u = c + 128 in 0..255, and placed
+// under the fp16 exponent of 1024 it reads 1024 + u.  The constant is never
+// subtracted per code: in the scores it adds 1152 sum_d q_d s_d to every key
+// of a query row, which the softmax ignores, and in the PV product it adds
+// 1152 times the row's weight sum, which the epilogue takes off once.
+constexpr float kCodeBias = 1152.f;
 __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
   const uint32_t u = w ^ 0x80808080u;
-  const f16x2_t bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
-  const f16x2_t l = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias;
-  const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;
-  lo = __builtin_bit_cast(uint32_t, l);
-  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
@@ -720,9 +722,11 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       for (int ww = 0; ww < 4; ++ww)
         if (wm[ww][m] != -INFINITY) ls += wl[ww][m] * exp2f(wm[ww][m] - mm);
       float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
-      if constexpr (KV8) {  // the V channel scales
+      if constexpr (KV8) {  // the codes' bias (weight sum ls), then the V channel scales
         const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + static_cast<size_t>(g) * D + d4);
-        o = make_float4(o.x * vs.x, o.y * vs.y, o.z * vs.z, o.w * vs.w);
+        const float bias = kCodeBias * ls;
+        o = make_float4((o.x - bias) * vs.x, (o.y - bias) * vs.y, (o.z - bias) * vs.z,
+                        (o.w - bias) * vs.w);
       }
       if (whole) {
         const int j = m / G, hh = m - j * G;
