@@ -230,7 +230,9 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKT * KS + D * VS];
   __shared__ float wm[4][ROWS];
   __shared__ float wl[4][ROWS];
-  __shared__ int s_first[5];  // the sequence holding t_lo, its first tile and unit; t_lo, t_hi
+  // the sequence holding t_lo, its first tile and unit; t_lo, t_hi; that
+  // sequence's first verify row, verify tokens and context length
+  __shared__ int s_first[8];
   __shared__ int s_ids[kChunkTiles * 4];     // page ids of the current chunk
   __shared__ int s_scan[2][kThreads / 64];
   uint16_t* Ks = lds;
@@ -314,6 +316,9 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
         s_first[1] = pre;
         s_first[2] = upre;
         s_first[3] = tile_of(u_lo);
+        s_first[5] = cuv[i];
+        s_first[6] = cuv[i + 1] - cuv[i];
+        s_first[7] = lv[i];
       }
       if (u_hi >= upre && u_hi < uend) s_first[4] = tile_of(u_hi);
       pre += nt * Hkv;
@@ -542,6 +547,13 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   int ucbase = t_lo < t_hi ? s_first[2] : 0;  // sequence cb's first unit
   int nt_b = 0;
   bool next_seq = true;
+  if (t_lo < t_hi) {  // the first sequence's bounds, as the start-up scan read them
+    x0 = s_first[5];
+    T = s_first[6];
+    L = s_first[7];
+    nt_b = seq_tiles(L, T);
+    next_seq = false;
+  }
   for (int t = t_lo; t < t_hi;) {
     if (next_seq) {
       for (; cb < B; ++cb) {  // skipped: sequences that failed validation
