@@ -578,26 +578,40 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  // the decision record, the normalisers and (up to kThreads chunks) the
+  // chunk sums are fetched together, in one round trip
   int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
   const float u_fin = a.u_final[b];
-  if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
+  const int nc = n_chunks(a.V);
+  double* csum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum) + static_cast<size_t>(b) * nc;
+  const bool one_stage = nc <= kThreads;
+  const double cv = one_stage ? csum[min(tid, nc - 1)] : 0.0;
+  if (d.x < 0) return;
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
   __shared__ double tab[kExpTab];
   exp_table_init(tab);
-  const int nc = n_chunks(a.V);
-  double* csum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + L.csum) + static_cast<size_t>(b) * nc;
   __shared__ double total_s;
   __shared__ double stage[kThreads];
   __shared__ int chunk_s;
   __shared__ double base_s;
   {
-    const double tot = ordered_walk(csum, nc, stage, false, 0.0, &chunk_s, &base_s);
+    double tot = 0.0;
+    if (one_stage) {  // the staged sums, added in index order by thread 0
+      stage[tid] = cv;
+      __syncthreads();
+      if (tid == 0)
+        for (int c = 0; c < nc; ++c) tot += stage[c];
+    } else {
+      tot = ordered_walk(csum, nc, stage, false, 0.0, &chunk_s, &base_s);
+    }
     if (tid == 0) total_s = tot;
   }
   __syncthreads();
   double total = total_s;
+  bool staged = one_stage;  // stage[] still holds csum
   if (d.y != 0 && !(total > 0.0)) {
+    staged = false;
     // p == q up to rounding: the residual is empty, draw from p instead.
     d.y = 0;
     __syncthreads();
@@ -627,8 +641,26 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   }
   const double t = static_cast<double>(u_fin) * total;
   // chunk whose inclusive running sum first exceeds t
-  if (tid == 0) base_s = 0.0;
-  ordered_walk(csum, nc, stage, true, t, &chunk_s, &base_s);
+  if (staged) {
+    if (tid == 0) {
+      double run = 0.0, base = 0.0;
+      int found = -1;
+      for (int c = 0; c < nc; ++c) {
+        const double x = stage[c];
+        if (run + x > t && x > 0.0) {
+          found = c;
+          base = run;
+          break;
+        }
+        run += x;
+      }
+      chunk_s = found;
+      base_s = base;
+    }
+  } else {
+    if (tid == 0) base_s = 0.0;
+    ordered_walk(csum, nc, stage, true, t, &chunk_s, &base_s);
+  }
   __syncthreads();
   int y = -1;
   int chunk = chunk_s;
