@@ -456,16 +456,56 @@ __device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int
   return fmax(p - q, 0.0);
 }
 
-template <typename T>
+// VEC: as for row_stats_partial.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
   const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
   const int4 d = reinterpret_cast<const int4*>(static_cast<const char*>(a.ws) + L.dec)[b];
-  if (d.x < 0) return;
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
+  if (d.x < 0) return;
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
+  constexpr int NV = VEC ? kVecN<T> : 1;
+  // vocabulary index of the thread's entry e (as in row_stats_partial)
+  auto entry = [&](int e) { return chunk * kChunk + ((e / NV) * kThreads + tid) * NV + e % NV; };
   float2 lg[kPerThread];
-  load_draw_logits<T>(a, d.y, d.z, d.w, chunk * kChunk + tid, kThreads, lg);
+  if constexpr (VEC) {
+    using S = typename io<T>::storage;
+    const int last = a.V / NV - 1;
+    auto load_row = [&](const void* src, int row, float* out) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const S*>(src) +
+                                                      static_cast<size_t>(row) * a.V);
+      uint4 raw[kPerThread / NV];
+#pragma unroll
+      for (int l = 0; l < kPerThread / NV; ++l)
+        raw[l] = p[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
+#pragma unroll
+      for (int l = 0; l < kPerThread / NV; ++l) {
+        const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (NV == 8) {
+            out[l * NV + 2 * q] = __uint_as_float(w[q] << 16);
+            out[l * NV + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+          } else {
+            out[l * NV + q] = __uint_as_float(w[q]);
+          }
+        }
+      }
+    };
+    float pt[kPerThread], pq[kPerThread];
+    load_row(a.target, d.z, pt);
+    if (d.y == 1) {
+      load_row(a.draft, d.w, pq);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) pq[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) lg[e] = make_float2(pt[e], pq[e]);
+  } else {
+    load_draw_logits<T>(a, d.y, d.z, d.w, chunk * kChunk + tid, kThreads, lg);
+  }
   __shared__ double tab[kExpTab];
   __shared__ double red[kThreads / 64];
   exp_table_init(tab);
@@ -473,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e)
-    s += draw_weight(a, d.y, d.w, f, rz, chunk * kChunk + e * kThreads + tid, lg[e], tab);
+    s += draw_weight(a, d.y, d.w, f, rz, entry(e), lg[e], tab);
   s = wave_sum_f64(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
@@ -697,7 +737,10 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((row_stats_partial<T, false>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL((residual_partial<T>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
+    if (vec)
+      hipLaunchKernelGGL((residual_partial<T, true>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((residual_partial<T, false>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL((final_draw<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
