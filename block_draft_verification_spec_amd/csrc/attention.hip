@@ -825,14 +825,19 @@ __global__ __launch_bounds__(256) void attn_append_kv8(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  int x0, T, L;
-  if (!attn_seq_ok(a, b, &x0, &T, &L, false)) return;
-  if (j >= T) return;
   const int G = a.Hq / a.Hkv;
   const int g = h / G;
   const int s = b * a.Hkv + g;
-  const int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
-  const int Units = a.seg_meta[2 * a.B * a.Hkv];
+  // the segment's piece record and the sequence bounds are fetched together,
+  // with one wait before the first branch (the record is used only once the
+  // sequence is known to be valid)
+  int wf = a.seg_meta[2 * s], wl_ = a.seg_meta[2 * s + 1];
+  int Units = a.seg_meta[2 * a.B * a.Hkv];
+  int x0 = a.cu[b], x1 = a.cu[b + 1], L = a.ctx_lens[b];
+  asm volatile("" : "+s"(wf), "+s"(wl_), "+s"(Units), "+s"(x0), "+s"(x1), "+s"(L));
+  const int T = x1 - x0;
+  if (!attn_seq_valid(a, x0, T, L, false)) return;
+  if (j >= T) return;
   if (wf >= wl_) return;  // one piece: written by the stream kernel
   // With few cost units some ranges [wg_unit(w), wg_unit(w + 1)) are empty
   // (never when every workgroup's share U w_r / S(W) is a unit or more); such
