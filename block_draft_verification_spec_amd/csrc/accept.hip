@@ -167,21 +167,70 @@ __device__ void write_outputs(const AcceptArgs& a, int b, int x0, int acc, int y
   if (a.ctx_lens) a.ctx_lens[b] += acc + 1;
 }
 
-// ------------------------------------------------------------------ greedy
+// ------------------------------------------------------- chunk loads
+// Entries of one 16-byte load.
 template <typename T>
+constexpr int kVecN = 16 / static_cast<int>(sizeof(typename io<T>::storage));
+
+// Vocabulary index of a thread's entry e of a chunk.  VEC (rows 16-byte
+// aligned and V a multiple of kVecN<T>, checked by the launcher): 16-byte
+// group l * kThreads + tid of the chunk holds entries l * kVecN .. of the
+// thread; otherwise entry e sits at stride kThreads.
+template <typename T, bool VEC>
+__device__ __forceinline__ int chunk_entry(int chunk, int tid, int e) {
+  constexpr int NV = VEC ? kVecN<T> : 1;
+  return chunk * kChunk + ((e / NV) * kThreads + tid) * NV + e % NV;
+}
+
+// A thread's kPerThread entries of one chunk of row `row`, every load issued
+// before any is used; an entry past V reads a valid entry of the row and is
+// masked by the caller.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_chunk(const void* src, int row, int V, int chunk, int tid,
+                                           float* out) {
+  using S = typename io<T>::storage;
+  if constexpr (VEC) {
+    constexpr int NV = kVecN<T>;
+    const uint4* p =
+        reinterpret_cast<const uint4*>(static_cast<const S*>(src) + static_cast<size_t>(row) * V);
+    const int last = V / NV - 1;
+    uint4 raw[kPerThread / NV];
+#pragma unroll
+    for (int l = 0; l < kPerThread / NV; ++l)
+      raw[l] = p[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
+#pragma unroll
+    for (int l = 0; l < kPerThread / NV; ++l) {
+      const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (NV == 8) {  // two bf16 entries per word, the lower first
+          out[l * NV + 2 * q] = __uint_as_float(w[q] << 16);
+          out[l * NV + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        } else {
+          out[l * NV + q] = __uint_as_float(w[q]);
+        }
+      }
+    }
+  } else {
+    const size_t base = static_cast<size_t>(row) * V;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      out[e] = ld<T>(src, base + min(chunk_entry<T, false>(chunk, tid, e), V - 1));
+  }
+}
+
+// ------------------------------------------------------------------ greedy
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void row_argmax_partial(AcceptArgs a) {
   const int chunk = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x;
   const int nc = gridDim.x;
-  const size_t base = static_cast<size_t>(row) * a.V;
   unsigned long long best = 0;
   float vals[kPerThread];
+  load_chunk<T, VEC>(a.target, row, a.V, chunk, tid, vals);
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
-    vals[e] = ld<T>(a.target, base + min(chunk * kChunk + e * kThreads + tid, a.V - 1));
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int idx = chunk * kChunk + e * kThreads + tid;
+  for (int e = 0; e < kPerThread; ++e) {  // the key orders ties by index
+    const int idx = chunk_entry<T, VEC>(chunk, tid, e);
     const unsigned long long key = idx < a.V ? argmax_key(vals[e], idx) : 0ull;
     best = key > best ? key : best;
   }
@@ -236,53 +285,16 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
 
 // ------------------------------------------------------------------ rejection
 // Row r < total_T: target row r; otherwise draft row r - total_T.
-// Entries of one 16-byte load.
-template <typename T>
-constexpr int kVecN = 16 / static_cast<int>(sizeof(typename io<T>::storage));
-
-// VEC: the rows start 16-byte aligned and V is a multiple of kVecN<T>
-// (checked by the launcher), so a thread reads its kPerThread entries with
-// kPerThread / kVecN 16-byte loads, group l * kThreads + tid of the chunk;
-// otherwise one element load per entry at stride kThreads.
+// VEC: 16-byte row loads (see chunk_entry).
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
   const int chunk = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x;
   const int nc = gridDim.x;
   const void* src = r < a.total_T ? a.target : a.draft;
-  const size_t base = static_cast<size_t>(r < a.total_T ? r : r - a.total_T) * a.V;
-  constexpr int NV = VEC ? kVecN<T> : 1;
-  // vocabulary index of the thread's entry e
-  auto entry = [&](int e) { return chunk * kChunk + ((e / NV) * kThreads + tid) * NV + e % NV; };
+  auto entry = [&](int e) { return chunk_entry<T, VEC>(chunk, tid, e); };
   float vals[kPerThread];
-  if constexpr (VEC) {
-    // every load issued before any is used; a group past the row reads the
-    // row's last group and is masked below
-    using S = typename io<T>::storage;
-    const uint4* row = reinterpret_cast<const uint4*>(static_cast<const S*>(src) + base);
-    const int last = a.V / NV - 1;
-    uint4 raw[kPerThread / NV];
-#pragma unroll
-    for (int l = 0; l < kPerThread / NV; ++l)
-      raw[l] = row[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
-#pragma unroll
-    for (int l = 0; l < kPerThread / NV; ++l) {
-      const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (NV == 8) {  // two bf16 entries per word, the lower first
-          vals[l * NV + 2 * q] = __uint_as_float(w[q] << 16);
-          vals[l * NV + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-        } else {
-          vals[l * NV + q] = __uint_as_float(w[q]);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e)  // every load issued before any is used
-      vals[e] = ld<T>(src, base + min(entry(e), a.V - 1));
-  }
+  load_chunk<T, VEC>(src, r < a.total_T ? r : r - a.total_T, a.V, chunk, tid, vals);
   __shared__ float redm[kThreads / 64];
   __shared__ double reds[kThreads / 64];
   __shared__ double tab[kExpTab];
@@ -465,46 +477,19 @@ __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
   if (d.x < 0) return;
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
-  constexpr int NV = VEC ? kVecN<T> : 1;
-  // vocabulary index of the thread's entry e (as in row_stats_partial)
-  auto entry = [&](int e) { return chunk * kChunk + ((e / NV) * kThreads + tid) * NV + e % NV; };
+  auto entry = [&](int e) { return chunk_entry<T, VEC>(chunk, tid, e); };
   float2 lg[kPerThread];
-  if constexpr (VEC) {
-    using S = typename io<T>::storage;
-    const int last = a.V / NV - 1;
-    auto load_row = [&](const void* src, int row, float* out) {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const S*>(src) +
-                                                      static_cast<size_t>(row) * a.V);
-      uint4 raw[kPerThread / NV];
-#pragma unroll
-      for (int l = 0; l < kPerThread / NV; ++l)
-        raw[l] = p[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
-#pragma unroll
-      for (int l = 0; l < kPerThread / NV; ++l) {
-        const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (NV == 8) {
-            out[l * NV + 2 * q] = __uint_as_float(w[q] << 16);
-            out[l * NV + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-          } else {
-            out[l * NV + q] = __uint_as_float(w[q]);
-          }
-        }
-      }
-    };
+  {
     float pt[kPerThread], pq[kPerThread];
-    load_row(a.target, d.z, pt);
-    if (d.y == 1) {
-      load_row(a.draft, d.w, pq);
+    load_chunk<T, VEC>(a.target, d.z, a.V, chunk, tid, pt);
+    if (d.y == 1) {  // the residual p - q needs the draft row
+      load_chunk<T, VEC>(a.draft, d.w, a.V, chunk, tid, pq);
     } else {
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) pq[e] = 0.f;
     }
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) lg[e] = make_float2(pt[e], pq[e]);
-  } else {
-    load_draw_logits<T>(a, d.y, d.z, d.w, chunk * kChunk + tid, kThreads, lg);
   }
   __shared__ double tab[kExpTab];
   __shared__ double red[kThreads / 64];
@@ -723,15 +708,19 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
 template <typename T>
 hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
   const int nc = n_chunks(a.V);
+  using S = typename io<T>::storage;
+  // 16-byte row loads: rows 16-byte aligned and V a multiple of the load's entries
+  const bool vec = (static_cast<size_t>(a.V) * sizeof(S)) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
+                   (!a.draft || reinterpret_cast<uintptr_t>(a.draft) % 16 == 0);
   if (a.mode == SV_ACCEPT_GREEDY) {
-    hipLaunchKernelGGL((row_argmax_partial<T>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
+    if (vec)
+      hipLaunchKernelGGL((row_argmax_partial<T, true>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((row_argmax_partial<T, false>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
   } else {
     const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
-    using S = typename io<T>::storage;
-    const bool vec = (static_cast<size_t>(a.V) * sizeof(S)) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
-                     (!a.draft || reinterpret_cast<uintptr_t>(a.draft) % 16 == 0);
     if (vec)
       hipLaunchKernelGGL((row_stats_partial<T, true>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
     else

@@ -147,31 +147,35 @@ def test_rejection_q_equal_p_accepts_everything():
     assert (acc == 3).all()
 
 
+@pytest.mark.parametrize("mode", [bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION])
 @pytest.mark.parametrize("V", [10007, 8200])
-def test_rejection_row_layouts(V):
+def test_row_layouts(mode, V):
     """V = 10007: bf16 rows are not 16-byte aligned, one element load per
     entry.  V = 8200: aligned rows read with 16-byte loads, and a last chunk
     of 8 entries."""
     w = wl.Workload('layout', B=8, k=3, ragged_k=True, ctx=(5, 9), V=V)
     batch = wl.make_batch(w, 21, DEV)
-    a = wl.make_accept(w, batch, 22, 'rejection', DEV)
-    _check(batch, a, bd.SV_ACCEPT_REJECTION)
+    a = wl.make_accept(w, batch, 22, 'greedy' if mode == 0 else 'rejection', DEV)
+    _check(batch, a, mode)
 
 
-def test_rejection_misaligned_logits():
+@pytest.mark.parametrize("mode", [bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION])
+def test_misaligned_logits(mode):
     """Logit rows one element past a 16-byte boundary take the element-load
     path and agree with the oracle."""
     w = wl.Workload('misaligned', B=8, k=3, ragged_k=False, ctx=(5, 9), V=8192)
     batch = wl.make_batch(w, 23, DEV)
-    a = wl.make_accept(w, batch, 24, 'rejection', DEV)
+    a = wl.make_accept(w, batch, 24, 'greedy' if mode == 0 else 'rejection', DEV)
     for key in ('target_logits', 'draft_logits'):
-        t = a[key]
+        t = a.get(key)
+        if t is None:   # greedy: no draft logits
+            continue
         buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
         view = buf[1:].view(t.shape)
         view.copy_(t)
         assert view.data_ptr() % 16 != 0
         a[key] = view
-    _check(batch, a, bd.SV_ACCEPT_REJECTION)
+    _check(batch, a, mode)
 
 
 def test_bad_draft_token_is_flagged():
