@@ -162,6 +162,12 @@ constexpr int kMaxRows = 64;       // query rows per (sequence, KV head)
 #define SV_ATTN_PIECE_COST 3
 #endif
 constexpr int kPieceCost = SV_ATTN_PIECE_COST;  // a piece's set-up, in tiles
+// Wave priority while a wave issues the next tile's loads (0 while it
+// computes), so a CU's waves issue their loads ahead of each other's compute:
+// INT8 pages 2.5 % faster per layer, bf16 unchanged.
+#ifndef SV_ATTN_LOAD_PRIO
+#define SV_ATTN_LOAD_PRIO 3
+#endif
 // Share of the units by dispatch round.  Workgroups are placed in order, one
 // per compute unit per round, and a CU's older waves win its arbitration: at
 // three workgroups per CU and equal tile counts the one placed first finished
@@ -535,7 +541,9 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     __syncthreads();  // previous tile's LDS reads are done
     write_lds(slot);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(SV_ATTN_LOAD_PRIO);  // the next tile's loads issue first
     slot = load_tile(tile + PF);
+    __builtin_amdgcn_s_setprio(0);
     compute_tile(tile);
   };
 
