@@ -21,8 +21,10 @@
 //   greedy:    row_argmax_partial  (chunk x row)  -> decide_greedy (sequence)
 //   rejection: row_stats_partial   (chunk x row)  -> decide_reject (sequence)
 //              -> residual_partial (chunk x seq)  -> final_draw    (sequence)
-// A chunk is 4096 vocabulary entries read by 256 threads with coalesced,
-// stride-256 element loads, so any V and any row alignment is supported.
+// A chunk is 4096 vocabulary entries read by 256 threads: with 16-byte loads
+// when the rows are 16-byte aligned and V is a multiple of the entries of one
+// load, otherwise with coalesced stride-256 element loads, so any V and any
+// row alignment is supported.
 
 #include "device_common.h"
 #include "exp2_table.h"

@@ -144,11 +144,12 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 // sequence b, head g, in position order).  Each segment is priced at its
 // tiles plus kPieceCost units for the set-up of a piece (bounds, Q, page
 // ids, a first tile with none in flight, and the write of its result);
-// the U units are split evenly, workgroup w of W taking units
-// [w U / W, (w + 1) U / W), and a unit range maps to the tiles it covers
-// (unit r of a segment is its tile max(r - kPieceCost, 0)).  So every
-// workgroup gets the same cost whatever the context lengths: one that starts
-// more segments streams fewer tiles.  A segment cut by range boundaries is
+// the U units are split over the W workgroups by weight (kRoundW below),
+// workgroup w taking units [U S(w) / S(W), U S(w + 1) / S(W)) with S(w) the
+// weight of workgroups 0 .. w - 1, and a unit range maps to the tiles it
+// covers (unit r of a segment is its tile max(r - kPieceCost, 0)).  So each
+// workgroup's share of the cost is fixed whatever the context lengths: one
+// that starts more segments streams fewer tiles.  A segment cut by range boundaries is
 // computed in pieces; piece (s, w) of a segment writes its partial
 // (max, sum, O) to slot s + w (distinct for every piece, since segments
 // advance with w) and the workgroup that owns the segment's first tile
