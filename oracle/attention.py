@@ -80,6 +80,7 @@ def verify_attention(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens,
         scale = 1.0 / np.sqrt(D)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     out = np.zeros((total_T, Hq, D), dtype=np.float64)
+    G = Hq // Hkv
     for b in range(len(cu) - 1):
         L = int(ctx_lens[b])
         T = int(cu[b + 1] - cu[b])
@@ -87,11 +88,16 @@ def verify_attention(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens,
         Vc = _f64(gather_context(v_cache, block_table[b], L, page_size))
         K_all = np.concatenate([Kc, k_new[cu[b]:cu[b] + T]], axis=0)
         V_all = np.concatenate([Vc, v_new[cu[b]:cu[b] + T]], axis=0)
-        for h in range(Hq):
-            g = h * Hkv // Hq
-            for j in range(T):
-                n = L + j + 1                      # cached + in-flight 0..j
-                s = (K_all[:n, g, :] @ q[cu[b] + j, h, :]) * scale
-                w = np.exp(s - s.max())
-                out[cu[b] + j, h, :] = (w @ V_all[:n, g, :]) / w.sum()
+        # Query row r of KV head g is (head h = g*G + r % G, token j = r // G);
+        # it sees positions 0 .. L + j (cached, then in-flight 0..j).
+        j_of_row = np.repeat(np.arange(T), G)
+        visible = np.arange(L + T)[None, :] <= (L + j_of_row)[:, None]
+        for g in range(Hkv):
+            Kg = np.ascontiguousarray(K_all[:, g, :])       # [L+T, D]
+            Vg = np.ascontiguousarray(V_all[:, g, :])
+            Qg = q[cu[b]:cu[b] + T, g * G:(g + 1) * G, :].reshape(T * G, D)
+            s = np.where(visible, (Qg @ Kg.T) * scale, -np.inf)
+            w = np.exp(s - s.max(axis=1, keepdims=True))  # exp(-inf) = 0
+            o = (w @ Vg) / w.sum(axis=1, keepdims=True)
+            out[cu[b]:cu[b] + T, g * G:(g + 1) * G, :] = o.reshape(T, G, D)
     return out

@@ -65,19 +65,22 @@ def gdn_step(state, state_slot, q, k, v, alpha, beta, cu_seqlens, commit_len,
         T = int(cu[b + 1] - cu[b])
         c = None if mode == GDN_VERIFY_ONLY else int(commit_len[b])
         n_run = c if mode == GDN_COMMIT_ONLY else T
-        for h in range(H):
-            S = S_bank[slot, h].copy()
-            S_commit = S.copy()                      # c == 0 keeps S_0
-            for t in range(n_run):
-                x = cu[b] + t
-                a_t, b_t = alpha[x, h], beta[x, h]
-                k_t, v_t = k[x, h], v[x, h]
-                S = a_t * (S - b_t * np.outer(S @ k_t, k_t)) \
-                    + b_t * np.outer(v_t, k_t)
-                if o is not None:
-                    o[x, h] = S @ q[x, h]
-                if c is not None and t == c - 1:
-                    S_commit = S.copy()
-            if mode != GDN_VERIFY_ONLY:
-                S_bank[slot, h] = S_commit
+        # The H heads of sequence b are independent recurrences; they are
+        # advanced together, S[h] being head h's [dv, dk] state.
+        S = S_bank[slot].copy()
+        S_commit = S.copy()                          # c == 0 keeps S_0
+        for t in range(n_run):
+            x = cu[b] + t
+            a_t = alpha[x][:, None, None]            # [H, 1, 1]
+            b_t = beta[x][:, None, None]
+            k_t, v_t = k[x], v[x]                    # [H, dk], [H, dv]
+            Sk = np.matmul(S, k_t[:, :, None])       # S_{t-1} k_t, [H, dv, 1]
+            S = a_t * (S - b_t * (Sk * k_t[:, None, :])) \
+                + b_t * (v_t[:, :, None] * k_t[:, None, :])
+            if o is not None:
+                o[x] = np.matmul(S, q[x][:, :, None])[:, :, 0]
+            if c is not None and t == c - 1:
+                S_commit = S.copy()
+        if mode != GDN_VERIFY_ONLY:
+            S_bank[slot] = S_commit
     return o, S_bank
