@@ -80,6 +80,9 @@ class SvStepPending(ctypes.Structure):
 
 _SIGS = {
     'sv_last_error': ([], ctypes.c_char_p),
+    'sv_workspace_bytes': ([_c_i32] * 6, _sz),
+    'sv_read_device_error': ([_vp, _vp], _c_i32),
+    'sv_clear_device_error': ([_vp, _vp], ctypes.c_int),
     'sv_version': ([], ctypes.c_char_p),
     'spec_verify_attention_workspace_bytes': (
         [_c_i32] * 7 + [ctypes.c_int], _sz),
@@ -199,6 +202,24 @@ def make_batch(cu_seqlens, B, max_T, total_T):
 
 def version():
     return lib().sv_version().decode()
+
+
+def sv_workspace_bytes(B, max_T, Hq, D, V, max_pages_per_seq):
+    """One workspace size for every call of such a batch (``sv_workspace_bytes``)."""
+    return lib().sv_workspace_bytes(B, max_T, Hq, D, V, max_pages_per_seq)
+
+
+def read_device_error(err, stream=None):
+    """The device error word after the stream's work (``sv_read_device_error``)."""
+    v = lib().sv_read_device_error(_i32(err, 'err'), _stream(stream))
+    if v < 0:
+        raise SpecVerifyError(SV_EHIP, lib().sv_last_error().decode())
+    return v
+
+
+def clear_device_error(err, stream=None):
+    """Enqueue the zeroing of the device error word (``sv_clear_device_error``)."""
+    _check(lib().sv_clear_device_error(_i32(err, 'err'), _stream(stream)))
 
 
 def spec_verify_attention_workspace_bytes(B, total_T, Hq, Hkv, D,

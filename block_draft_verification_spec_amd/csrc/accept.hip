@@ -169,6 +169,16 @@ __device__ void write_outputs(const AcceptArgs& a, int b, int x0, int acc, int y
   if (a.ctx_lens) a.ctx_lens[b] += acc + 1;
 }
 
+// A skipped sequence (bad lengths, a draft or bonus id outside the
+// vocabulary): accept_len -1, a row of -1 and commit length 0, so a commit
+// that follows keeps its recurrent state; its ctx_lens entry is not changed.
+__device__ void skip_outputs(const AcceptArgs& a, int b) {
+  int32_t* row = a.result + a.B + static_cast<size_t>(b) * a.max_T;
+  for (int j = 0; j < a.max_T; ++j) row[j] = -1;
+  a.result[b] = -1;
+  if (a.commit_len_out) a.commit_len_out[b] = 0;
+}
+
 // ------------------------------------------------------- chunk loads
 // Entries of one 16-byte load.
 template <typename T>
@@ -252,7 +262,10 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
   const int b = blockIdx.x, lane = threadIdx.x;
   int x0, T;
   if (!seq_ok(a, b, &x0, &T)) {
-    if (lane == 0) flag_error(a.err, SV_DERR_SEQLEN);
+    if (lane == 0) {
+      flag_error(a.err, SV_DERR_SEQLEN);
+      skip_outputs(a, b);
+    }
     return;
   }
   const int nc = n_chunks(a.V);
@@ -260,6 +273,15 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
   const unsigned long long* keys =
       reinterpret_cast<const unsigned long long*>(static_cast<const char*>(a.ws) + L.keys);
   const int d0 = x0 - b;
+  // every draft id of the sequence must be in the vocabulary
+  const int xd = lane < T - 1 ? a.draft_tokens[d0 + lane] : 0;
+  if (__builtin_amdgcn_ballot_w64(xd < 0 || xd >= a.V) != 0) {
+    if (lane == 0) {
+      flag_error(a.err, SV_DERR_TOKEN);
+      skip_outputs(a, b);
+    }
+    return;
+  }
   int acc = 0, y = -1;
   for (int i = 0; i < T; ++i) {
     unsigned long long best = 0;
@@ -278,7 +300,10 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
   if (acc == T - 1 && a.bonus) {  // every draft accepted: the supplied bonus
     y = a.bonus[b];
     if (y < 0 || y >= a.V) {
-      if (lane == 0) flag_error(a.err, SV_DERR_TOKEN);
+      if (lane == 0) {
+        flag_error(a.err, SV_DERR_TOKEN);
+        skip_outputs(a, b);
+      }
       return;
     }
   }
@@ -359,6 +384,7 @@ __global__ __launch_bounds__(kThreads) void decide_reject(AcceptArgs a) {
     if (tid == 0) {
       flag_error(a.err, SV_DERR_SEQLEN);
       dec[b] = make_int4(-1, -1, -1, -1);
+      skip_outputs(a, b);
     }
     return;
   }
@@ -400,6 +426,7 @@ __global__ __launch_bounds__(kThreads) void decide_reject(AcceptArgs a) {
   if (bad_s) {
     flag_error(a.err, SV_DERR_TOKEN);
     dec[b] = make_int4(-1, -1, -1, -1);
+    skip_outputs(a, b);
     return;
   }
   double4* fin = reinterpret_cast<double4*>(static_cast<char*>(a.ws) + L.fin);
@@ -422,8 +449,12 @@ __global__ __launch_bounds__(kThreads) void decide_reject(AcceptArgs a) {
   }
   if (a.bonus) {  // every draft accepted: the supplied bonus, no draw
     const int y = a.bonus[b];
-    if (y < 0 || y >= a.V) flag_error(a.err, SV_DERR_TOKEN);
-    else write_outputs(a, b, x0, tn - 1, y);
+    if (y < 0 || y >= a.V) {
+      flag_error(a.err, SV_DERR_TOKEN);
+      skip_outputs(a, b);
+    } else {
+      write_outputs(a, b, x0, tn - 1, y);
+    }
     dec[b] = make_int4(-1, -1, -1, -1);
     return;
   }
@@ -737,7 +768,18 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void fill_i32(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32, dim3((n + 255) / 256), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
 
 size_t accept_workspace_bytes(int B, int total_T, int V, int mode) {
   return accept_ws_layout(B, total_T, V, mode).total;

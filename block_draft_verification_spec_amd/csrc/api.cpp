@@ -83,6 +83,25 @@ sv_status check_attn(const sv_batch* batch, const void* q, const void* k_new, co
   return SV_OK;
 }
 
+// The checks of spec_verify_attention_kv8 beyond those of the bf16 path.
+sv_status check_attn_kv8(const float* k_scale, const float* v_scale, const char* who) {
+  if (!k_scale || !v_scale) return fail(SV_EINVAL, "%s: k_scale and v_scale are required", who);
+  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 15)
+    return fail(SV_EINVAL, "%s: scales must be 16-byte aligned", who);
+  return SV_OK;
+}
+
+sv_status check_attn_workspace(const sv_batch* batch, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t max_pages, int32_t P, sv_dtype dtype,
+                               const void* workspace, size_t workspace_bytes, const char* who) {
+  const size_t need =
+      sv::attn_workspace_bytes(batch->B, batch->total_T, Hq, Hkv, D, max_pages, P, dtype);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
+                workspace ? workspace_bytes : size_t(0));
+  return SV_OK;
+}
+
 sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_new,
                             const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* block_table, int32_t max_pages, int32_t num_pages,
@@ -145,9 +164,8 @@ sv_status check_gdn_common(const sv_batch* batch, void* state, sv_dtype state_dt
   return SV_OK;
 }
 
-sv_status accept_impl(const sv_batch* batch, const sv_accept_args* acc, int32_t* result,
-                      int32_t* commit_len_out, int32_t* ctx_lens_inout, void* workspace,
-                      size_t workspace_bytes, int32_t* err, hipStream_t stream, const char* who) {
+sv_status check_accept(const sv_batch* batch, const sv_accept_args* acc, const int32_t* result,
+                       const void* workspace, size_t workspace_bytes, const char* who) {
   sv_status st = check_batch(batch, who);
   if (st != SV_OK) return st;
   const sv_accept_mode mode = acc->mode;
@@ -169,6 +187,49 @@ sv_status accept_impl(const sv_batch* batch, const sv_accept_args* acc, int32_t*
   if (!workspace || workspace_bytes < need)
     return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
                 workspace ? workspace_bytes : size_t(0));
+  return SV_OK;
+}
+
+sv_status check_gdn_call(const sv_batch* batch, sv_gdn_mode mode, const void* state,
+                         sv_dtype state_dtype, const int32_t* state_slot, int32_t num_slots,
+                         const void* q, const void* k, const void* v, sv_dtype io_dtype,
+                         const float* alpha, const float* beta, const int32_t* commit_len,
+                         const void* out, int32_t H, int32_t dk, int32_t dv,
+                         const sv_gdn_pending* pending, const char* who) {
+  sv_status st = check_gdn_common(batch, const_cast<void*>(state), state_dtype, num_slots,
+                                  io_dtype, H, dk, dv, who);
+  if (st != SV_OK) return st;
+  if (mode != SV_GDN_VERIFY_COMMIT && mode != SV_GDN_VERIFY_ONLY && mode != SV_GDN_COMMIT_ONLY)
+    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
+  if (!k || !v || !alpha || !beta) return fail(SV_EINVAL, "%s: k, v, alpha, beta are required", who);
+  if (mode != SV_GDN_COMMIT_ONLY && (!q || !out))
+    return fail(SV_EINVAL, "%s: q and out are required unless COMMIT_ONLY", who);
+  if (mode != SV_GDN_VERIFY_ONLY && !commit_len)
+    return fail(SV_EINVAL, "%s: commit_len is required unless VERIFY_ONLY", who);
+  if (!state_slot && num_slots < batch->B)
+    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) ||
+      (pending && (misaligned16(pending->k) || misaligned16(pending->v))))
+    return fail(SV_EINVAL, "%s: q, k, v must be 16-byte aligned", who);
+  if (pending) {
+    st = check_batch(&pending->batch, who);
+    if (st != SV_OK) return st;
+    if (pending->batch.B != batch->B)
+      return fail(SV_EINVAL, "%s: pending batch has B=%d, this batch B=%d", who,
+                  pending->batch.B, batch->B);
+    if (!pending->k || !pending->v || !pending->alpha || !pending->beta || !pending->commit_len)
+      return fail(SV_EINVAL, "%s: pending k, v, alpha, beta, commit_len are required", who);
+  }
+  return SV_OK;
+}
+
+sv_status accept_impl(const sv_batch* batch, const sv_accept_args* acc, int32_t* result,
+                      int32_t* commit_len_out, int32_t* ctx_lens_inout, void* workspace,
+                      size_t workspace_bytes, int32_t* err, hipStream_t stream, const char* who) {
+  sv_status st = check_accept(batch, acc, result, workspace, workspace_bytes, who);
+  if (st != SV_OK) return st;
+  const sv_accept_mode mode = acc->mode;
+  const int32_t V = acc->V;
   sv::AcceptArgs a{};
   a.B = batch->B;
   a.total_T = batch->total_T;
@@ -196,7 +257,41 @@ extern "C" {
 
 const char* sv_last_error(void) { return g_last_error.c_str(); }
 
-const char* sv_version(void) { return "specverify 0.1 gfx950"; }
+const char* sv_version(void) { return "specverify 0.2 gfx950"; }
+
+int32_t sv_read_device_error(const int32_t* err, hipStream_t stream) {
+  if (!err) {
+    fail(SV_EINVAL, "sv_read_device_error: err is null");
+    return -1;
+  }
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, err, sizeof(v), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    hip_status(e, "sv_read_device_error");
+    return -1;
+  }
+  ok();
+  return v;
+}
+
+sv_status sv_clear_device_error(int32_t* err, hipStream_t stream) {
+  if (!err) return fail(SV_EINVAL, "sv_clear_device_error: err is null");
+  return hip_status(sv::launch_fill_i32(err, 1, 0, stream), "sv_clear_device_error");
+}
+
+size_t sv_workspace_bytes(int32_t B, int32_t max_T, int32_t Hq, int32_t D, int32_t V,
+                          int32_t max_pages_per_seq) {
+  if (B < 1 || max_T < 1 || max_T > sv::kMaxT || Hq < 1 || D < 1 || V < 1 ||
+      max_pages_per_seq < 1)
+    return 0;
+  const int32_t total_T = B * max_T;
+  // the attention workspace grows with the KV heads: Hq bounds them
+  size_t need = sv::attn_workspace_bytes(B, total_T, Hq, Hq, D, max_pages_per_seq, 16, SV_BF16);
+  need = std::max(need, sv::accept_workspace_bytes(B, total_T, V, SV_ACCEPT_GREEDY));
+  need = std::max(need, sv::accept_workspace_bytes(B, total_T, V, SV_ACCEPT_REJECTION));
+  return need;
+}
 
 size_t spec_verify_attention_workspace_bytes(int32_t B, int32_t total_T, int32_t Hq, int32_t Hkv,
                                              int32_t D, int32_t max_pages_per_seq,
@@ -217,11 +312,9 @@ sv_status spec_verify_attention(const sv_batch* batch, const void* q, const void
                             max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv, D,
                             dtype);
   if (st != SV_OK) return st;
-  const size_t need = sv::attn_workspace_bytes(batch->B, batch->total_T, Hq, Hkv, D,
-                                               max_pages_per_seq, page_size, dtype);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(SV_EWORKSPACE, "spec_verify_attention: workspace needs %zu bytes (got %zu)", need,
-                workspace ? workspace_bytes : size_t(0));
+  st = check_attn_workspace(batch, Hq, Hkv, D, max_pages_per_seq, page_size, dtype, workspace,
+                            workspace_bytes, "spec_verify_attention");
+  if (st != SV_OK) return st;
   sv::AttnArgs a = make_attn_args(batch, q, k_new, v_new, k_cache, v_cache, block_table,
                                   max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv,
                                   D, dtype, scale, write_kv, workspace, err);
@@ -241,14 +334,11 @@ sv_status spec_verify_attention_kv8(const sv_batch* batch, const void* q, const 
                             max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv, D,
                             SV_BF16, who);
   if (st != SV_OK) return st;
-  if (!k_scale || !v_scale) return fail(SV_EINVAL, "%s: k_scale and v_scale are required", who);
-  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 15)
-    return fail(SV_EINVAL, "%s: scales must be 16-byte aligned", who);
-  const size_t need = sv::attn_workspace_bytes(batch->B, batch->total_T, Hq, Hkv, D,
-                                               max_pages_per_seq, page_size, SV_BF16);
-  if (!workspace || workspace_bytes < need)
-    return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
-                workspace ? workspace_bytes : size_t(0));
+  st = check_attn_kv8(k_scale, v_scale, who);
+  if (st != SV_OK) return st;
+  st = check_attn_workspace(batch, Hq, Hkv, D, max_pages_per_seq, page_size, SV_BF16, workspace,
+                            workspace_bytes, who);
+  if (st != SV_OK) return st;
   sv::AttnArgs a = make_attn_args(batch, q, k_new, v_new, k_cache, v_cache, block_table,
                                   max_pages_per_seq, num_pages, page_size, ctx_lens, out, Hq, Hkv,
                                   D, SV_BF16, scale, 1, workspace, err, k_scale, v_scale);
@@ -263,21 +353,9 @@ sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state
                             int32_t dk, int32_t dv, const sv_gdn_pending* pending, int32_t* err,
                             hipStream_t stream) {
   const char* who = "gdn_verify_commit";
-  sv_status st =
-      check_gdn_common(batch, state, state_dtype, num_slots, io_dtype, H, dk, dv, who);
+  sv_status st = check_gdn_call(batch, mode, state, state_dtype, state_slot, num_slots, q, k, v,
+                                io_dtype, alpha, beta, commit_len, out, H, dk, dv, pending, who);
   if (st != SV_OK) return st;
-  if (mode != SV_GDN_VERIFY_COMMIT && mode != SV_GDN_VERIFY_ONLY && mode != SV_GDN_COMMIT_ONLY)
-    return fail(SV_EINVAL, "%s: unknown mode %d", who, static_cast<int>(mode));
-  if (!k || !v || !alpha || !beta) return fail(SV_EINVAL, "%s: k, v, alpha, beta are required", who);
-  if (mode != SV_GDN_COMMIT_ONLY && (!q || !out))
-    return fail(SV_EINVAL, "%s: q and out are required unless COMMIT_ONLY", who);
-  if (mode != SV_GDN_VERIFY_ONLY && !commit_len)
-    return fail(SV_EINVAL, "%s: commit_len is required unless VERIFY_ONLY", who);
-  if (!state_slot && num_slots < batch->B)
-    return fail(SV_EINVAL, "%s: without state_slot, num_slots must be >= B", who);
-  if (misaligned16(q) || misaligned16(k) || misaligned16(v) ||
-      (pending && (misaligned16(pending->k) || misaligned16(pending->v))))
-    return fail(SV_EINVAL, "%s: q, k, v must be 16-byte aligned", who);
   sv::GdnScalars s{};
   s.B = batch->B;
   s.total_T = batch->total_T;
@@ -300,13 +378,6 @@ sv_status gdn_verify_commit(const sv_batch* batch, sv_gdn_mode mode, void* state
   p.beta = beta;
   p.out = out;
   if (pending) {
-    st = check_batch(&pending->batch, "gdn_verify_commit (pending)");
-    if (st != SV_OK) return st;
-    if (pending->batch.B != batch->B)
-      return fail(SV_EINVAL, "%s: pending batch has B=%d, this batch B=%d", who,
-                  pending->batch.B, batch->B);
-    if (!pending->k || !pending->v || !pending->alpha || !pending->beta || !pending->commit_len)
-      return fail(SV_EINVAL, "%s: pending k, v, alpha, beta, commit_len are required", who);
     s.has_pending = 1;
     s.p_total_T = pending->batch.total_T;
     s.p_max_T = pending->batch.max_T;
@@ -633,6 +704,41 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
   if (!workspace || workspace_bytes < need)
     return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
                 workspace ? workspace_bytes : size_t(0));
+
+  // 0. every argument of every layer and of the acceptance is checked before
+  // the first launch, so a refused call has changed no page, state or length
+  // (a retry after fixing it must not replay pending tokens twice)
+  {
+    char what[64];
+    int ia = 0, ig = 0;
+    for (int l = 0; l < n_layers; ++l) {
+      std::snprintf(what, sizeof(what), "%s: layer %d", who, l);
+      if (layer_kind[l] == 1) {
+        const sv_attn_layer& L = attn[ia++];
+        const sv_dtype dt = acfg->kv_format == SV_KV_INT8 ? SV_BF16 : acfg->dtype;
+        st = check_attn(batch, L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, acfg->block_table,
+                        acfg->max_pages_per_seq, acfg->num_pages, acfg->page_size, ctx_lens,
+                        L.out, acfg->Hq, acfg->Hkv, acfg->D, dt, what);
+        if (st == SV_OK && acfg->kv_format == SV_KV_INT8)
+          st = check_attn_kv8(L.k_scale, L.v_scale, what);
+      } else {
+        const sv_gdn_layer& G = gdn[ig];
+        sv_gdn_pending pg{};
+        if (pending) {
+          const sv_gdn_layer& P = pending->layers[ig];
+          pg = sv_gdn_pending{pending->batch, P.k, P.v, P.alpha, P.beta, pending->commit_len};
+        }
+        ++ig;
+        st = check_gdn_call(batch, SV_GDN_VERIFY_ONLY, G.state, gcfg->state_dtype,
+                            gcfg->state_slot, gcfg->num_slots, G.q, G.k, G.v, gcfg->io_dtype,
+                            G.alpha, G.beta, nullptr, G.out, gcfg->H, gcfg->dk, gcfg->dv,
+                            pending ? &pg : nullptr, what);
+      }
+      if (st != SV_OK) return st;
+    }
+    st = check_accept(batch, acc, result, workspace, workspace_bytes, who);
+    if (st != SV_OK) return st;
+  }
 
   // 1. verify every layer in model order
   int ia = 0, ig = 0;

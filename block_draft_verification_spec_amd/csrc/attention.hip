@@ -159,16 +159,11 @@ constexpr int kMaxB = 2048;        // sequences per call on the bf16 path
 constexpr int kChunkTiles = 256;   // tiles whose page ids are staged at once
 constexpr int kRound = 12;         // tiles per unrolled round (a multiple of PF)
 constexpr int kMaxRows = 64;       // query rows per (sequence, KV head)
-#ifndef SV_ATTN_PIECE_COST
-#define SV_ATTN_PIECE_COST 3
-#endif
-constexpr int kPieceCost = SV_ATTN_PIECE_COST;  // a piece's set-up, in tiles
+constexpr int kPieceCost = 3;  // a piece's set-up, in tiles
 // Wave priority while a wave issues the next tile's loads (0 while it
 // computes), so a CU's waves issue their loads ahead of each other's compute:
 // INT8 pages 2.5 % faster per layer, bf16 unchanged.
-#ifndef SV_ATTN_LOAD_PRIO
-#define SV_ATTN_LOAD_PRIO 3
-#endif
+constexpr int kLoadPrio = 3;
 // Share of the units by dispatch round.  Workgroups are placed in order, one
 // per compute unit per round, and a CU's older waves win its arbitration: at
 // three workgroups per CU and equal tile counts the one placed first finished
@@ -178,10 +173,7 @@ constexpr int kPieceCost = SV_ATTN_PIECE_COST;  // a piece's set-up, in tiles
 // stream as fast as a load-only kernel), so the youngest workgroup slows down
 // when given fewer tiles; shorter ranges for later rounds still measured
 // about 1 % faster per layer than equal ones.
-#ifndef SV_ATTN_ROUND_W
-#define SV_ATTN_ROUND_W 64, 61, 53, 53
-#endif
-constexpr int kRoundW[4] = {SV_ATTN_ROUND_W};
+constexpr int kRoundW[4] = {64, 61, 53, 53};
 constexpr int round_w_min() {
   int m = kRoundW[0];
   for (int i = 1; i < 4; ++i) m = kRoundW[i] < m ? kRoundW[i] : m;
@@ -380,7 +372,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     // multiple of KPT)
     const int pos = tile * kKT + toff;
     const int pid = s_ids[min((pos >> ps) - first_page, last_pg)];
-    // a bad page reads page 0: the sequence is flagged
+    // every id is inside the pool: a sequence with a bad one is skipped
     const size_t base =
         ((static_cast<size_t>(max(pid, 0)) * Hkv + g) * P + (pos & (P - 1))) * D + DPC * dc;
     if constexpr (KV8) {
@@ -542,7 +534,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     __syncthreads();  // previous tile's LDS reads are done
     write_lds(slot);
     __syncthreads();
-    __builtin_amdgcn_s_setprio(SV_ATTN_LOAD_PRIO);  // the next tile's loads issue first
+    __builtin_amdgcn_s_setprio(kLoadPrio);  // the next tile's loads issue first
     slot = load_tile(tile + PF);
     __builtin_amdgcn_s_setprio(0);
     compute_tile(tile);
@@ -584,11 +576,9 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     const int s = b * Hkv + g;
     const bool whole = lt_begin == 0 && lt_end == nt_b;
     M = G * T;
-    if (lt_begin == 0 && tid == 0) {  // the segment's last tile is its unit kPieceCost + nt_b - 1
-      a.seg_meta[2 * s] = wg;
-      a.seg_meta[2 * s + 1] =
-          piece_wg(ucbase + g * (nt_b + kPieceCost) + kPieceCost + nt_b - 1, W, a.n_cu, U);
-    }
+    // the segment's last tile is its unit kPieceCost + nt_b - 1
+    const int seg_last_wg =
+        piece_wg(ucbase + g * (nt_b + kPieceCost) + kPieceCost + nt_b - 1, W, a.n_cu, U);
     t = seg_start + lt_end;
     if (t == cbase + Hkv * nt_b) {
       cbase = t;
@@ -635,6 +625,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       for (int dt = 0; dt < NDT; ++dt) oacc[nt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
+    bool seq_bad = false;
     for (int c0 = lt_begin; c0 < lt_end; c0 += kChunkTiles) {
       const int c1 = min(lt_end, c0 + kChunkTiles);
       pos_end = min(c1 * kKT, L + T);  // keys at or past it are masked
@@ -642,16 +633,44 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       const int n_pages = (pos_end - 1) / P - first_page + 1;
       last_tile = (pos_end - 1) / kKT;
       last_pg = n_pages - 1;
+      const int* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
       __syncthreads();  // the previous chunk is done with s_ids and the tile LDS
-      for (int i = tid; i < n_pages; i += kThreads) {
-        int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + first_page + i];
-        if (pid < 0 || pid >= a.num_pages) {
-          bad_page = true;
-          pid = -1;
+      if (c0 == lt_begin) {
+        // The piece's first chunk checks every page id the sequence uses
+        // (positions 0 .. L + T - 1) while it stages its own: a sequence with
+        // an id outside the pool is skipped by all of its pieces (no output,
+        // no append) and flagged.  Four loads per thread are issued before
+        // any is used.
+        const int npg = (L + T - 1) / P + 1;
+        int bad = 0;
+        for (int i0 = 0; i0 < npg; i0 += 4 * kThreads) {
+          int pid[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pid[u] = bt[min(i0 + u * kThreads + tid, npg - 1)];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads + tid, li = i - first_page;
+            if (i < npg) {
+              bad |= (pid[u] < 0 || pid[u] >= a.num_pages) ? 1 : 0;
+              if (li >= 0 && li < n_pages) s_ids[li] = pid[u];
+            }
+          }
         }
-        s_ids[i] = pid;
+        // one flag per wave (s_scan is free after the start-up), one barrier
+        const bool wave_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+        if (lane == 0) s_scan[0][w] = wave_bad ? 1 : 0;
+        __syncthreads();
+        seq_bad = (s_scan[0][0] | s_scan[0][1] | s_scan[0][2] | s_scan[0][3]) != 0;
+        if (lt_begin == 0 && tid == 0) {  // the combine's record of the segment
+          // first > last: nothing to merge (a skipped sequence)
+          a.seg_meta[2 * s] = seq_bad ? 1 : wg;
+          a.seg_meta[2 * s + 1] = seq_bad ? 0 : seg_last_wg;
+        }
+        if (seq_bad) break;
+      } else {  // later chunks of a long piece: ids already checked
+        for (int i = tid; i < n_pages; i += kThreads) s_ids[i] = bt[first_page + i];
+        __syncthreads();
       }
-      __syncthreads();
 
       r0 = load_tile(c0);
       if constexpr (PF > 1) r1 = load_tile(c0 + 1);
@@ -692,6 +711,11 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
               *reinterpret_cast<const uint4*>(vn + off_n);
         }
       }
+    }
+
+    if (seq_bad) {
+      if (tid == 0) bad_page = true;
+      continue;
     }
 
     // ---- merge the four waves in a fixed order
@@ -802,14 +826,38 @@ __device__ __forceinline__ uint32_t quant4(uint2 x, float4 s) {
   return w;
 }
 
+// True if every page id sequence b uses for positions 0 .. n - 1 (n >= 1) is
+// inside the pool.  Block-wide (every thread of the block calls it); each
+// wave reduces by ballot, the waves through LDS.
+__device__ bool seq_pages_ok(const AttnArgs& a, int b, int n) {
+  __shared__ int wave_bad[4];
+  const int tid = threadIdx.x, nw = (blockDim.x + 63) / 64;
+  const int npg = (n - 1) / a.P + 1;
+  const int* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+  int bad = 0;
+  for (int i = tid; i < npg; i += blockDim.x) {
+    const int pid = bt[i];
+    bad |= (pid < 0 || pid >= a.num_pages) ? 1 : 0;
+  }
+  const bool wb = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if ((tid & 63) == 0) wave_bad[tid >> 6] = wb ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+  for (int i = 0; i < nw; ++i) any |= wave_bad[i];
+  __syncthreads();  // the flags may be written again by a later call
+  return any == 0;
+}
+
 __global__ __launch_bounds__(256) void attn_append_kv8(AttnArgs a) {
   const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int x0, T, L;
   if (!attn_seq_ok(a, b, &x0, &T, &L, false)) return;  // the stream kernel flags it
   if (j >= T) return;
+  // a sequence with a page id outside the pool is not appended (the stream
+  // kernel flags and skips it)
+  if (!seq_pages_ok(a, b, L + T)) return;
   const int p = L + j;
   const int pid = a.block_table[static_cast<size_t>(b) * a.max_pages + p / a.P];
-  if (pid < 0 || pid >= a.num_pages) return;          // flagged by the stream kernel
   const int HD = a.Hkv * a.D;
   const size_t src = static_cast<size_t>(x0 + j) * HD;
   for (int c4 = tid; c4 < HD / 4; c4 += 256) {
@@ -929,34 +977,34 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
   __shared__ float qs[128];
   __shared__ float ws[64];
   __shared__ long long offs[64];
+  // a sequence with a page id outside the pool is flagged and skipped: no
+  // output, no append
+  if (!seq_pages_ok(a, b, L + T)) {
+    if (h == 0 && j == 0 && lane == 0) flag_error(a.err, SV_DERR_PAGE);
+    return;
+  }
   for (int d = lane; d < D; d += 64) qs[d] = q[d];
   // write-through of this token's K/V, once per KV head
   if (a.write_kv && h % G == 0) {
     const long long po = page_offset(a, b, g, L + j, 0);
-    if (po >= 0) {
-      for (int d = lane; d < D; d += 64) {
-        static_cast<float*>(a.k_cache)[po + d] = kn[(static_cast<size_t>(x0 + j) * a.Hkv + g) * D + d];
-        static_cast<float*>(a.v_cache)[po + d] = vn[(static_cast<size_t>(x0 + j) * a.Hkv + g) * D + d];
-      }
-    } else if (lane == 0) {
-      flag_error(a.err, SV_DERR_PAGE);
+    for (int d = lane; d < D; d += 64) {
+      static_cast<float*>(a.k_cache)[po + d] = kn[(static_cast<size_t>(x0 + j) * a.Hkv + g) * D + d];
+      static_cast<float*>(a.v_cache)[po + d] = vn[(static_cast<size_t>(x0 + j) * a.Hkv + g) * D + d];
     }
   }
   __syncthreads();
   const int n = L + j + 1;
   float m_run = -INFINITY, l_run = 0.f;
   float o[2] = {0.f, 0.f};
-  bool bad = false;
   for (int base = 0; base < n; base += 64) {
     const int p = base + lane;
     float s = -INFINITY;
-    long long off = -2;  // -2: in flight, -1: bad page
+    long long off = -2;  // -2: in flight
     if (p < n) {
       const float* kr;
       if (p < L) {
-        off = page_offset(a, b, g, p, 0);
-        kr = off >= 0 ? kc + off : nullptr;
-        if (off < 0) bad = true;
+        off = page_offset(a, b, g, p, 0);  // inside the pool (checked above)
+        kr = kc + off;
       } else {
         kr = kn + (static_cast<size_t>(x0 + p - L) * a.Hkv + g) * D;
       }
@@ -990,7 +1038,6 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
     m_run = m_new;
     __syncthreads();
   }
-  if (bad) flag_error(a.err, SV_DERR_PAGE);
   float* out = static_cast<float*>(a.out) + (static_cast<size_t>(x0 + j) * a.Hq + h) * D;
   const float inv = 1.f / l_run;
   if (lane < D) out[lane] = o[0] * inv;

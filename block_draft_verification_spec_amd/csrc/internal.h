@@ -139,6 +139,8 @@ struct AcceptArgs {
 };
 
 size_t accept_workspace_bytes(int B, int total_T, int V, int mode);
+// Fill n int32 words with v on the stream (a kernel, so it can be captured).
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, sv_dtype dtype,
                          hipStream_t stream);
 

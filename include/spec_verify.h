@@ -29,8 +29,13 @@
  *     context that overflows the block table, T_b outside 1..max_T, a commit
  *     length outside 0..T_b, a draft token outside 0..V-1, a state slot
  *     outside the bank); the affected
- *     sequence is then skipped (its outputs are left untouched).  The caller
- *     clears the word.
+ *     sequence is then skipped: attention, GDN and short-conv calls leave its
+ *     outputs, pages and states untouched (a bad page id anywhere in a
+ *     sequence's block-table range skips the whole sequence, append
+ *     included); acceptance writes accept_len -1, a row of -1 and commit
+ *     length 0 for it and leaves its ctx_lens entry, so a commit or deferred
+ *     replay that follows keeps its recurrent state.  The caller clears the
+ *     word (sv_clear_device_error) and reads it (sv_read_device_error).
  *   - Calls that run on the same buffers must be ordered on one stream; two
  *     calls that share a workspace or a state / cache buffer must not overlap.
  */
@@ -414,6 +419,31 @@ SV_API sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers,
     const sv_accept_args* acc, int32_t* ctx_lens, int32_t* result,
     int32_t* commit_len, sv_schedule schedule, const sv_step_pending* pending,
     void* workspace, size_t workspace_bytes, int32_t* err, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sizing and errors.
+ *
+ * sv_workspace_bytes: one workspace size that serves every call of a batch
+ * of at most B sequences of at most max_T verify tokens (attention of either
+ * page format with up to Hq KV heads of head size D over block tables of
+ * max_pages_per_seq pages, acceptance of either mode over V entries, and the
+ * step).  0 for a size outside the limits.  The per-call queries above give
+ * tighter sizes.
+ *
+ * sv_read_device_error: the value of the caller's device error word `err`
+ * (the SV_DERR_* bits the kernels OR into it) once `stream` has run the work
+ * enqueued before the call.  It copies the word to the host and waits for
+ * the stream, so it is the one call that blocks and must not be made while
+ * the stream is being captured.  Returns the bits (>= 0), or -1 if the copy
+ * failed (sv_last_error() says why).
+ *
+ * sv_clear_device_error: enqueues a kernel that zeroes the error word (no
+ * memset node, so it may be captured into a graph with the step).
+ * ------------------------------------------------------------------------ */
+SV_API size_t sv_workspace_bytes(int32_t B, int32_t max_T, int32_t Hq, int32_t D, int32_t V,
+                                 int32_t max_pages_per_seq);
+SV_API int32_t sv_read_device_error(const int32_t* err, hipStream_t stream);
+SV_API sv_status sv_clear_device_error(int32_t* err, hipStream_t stream);
 
 /* Host: text of the calling thread's last non-OK status ("" if none). */
 SV_API const char* sv_last_error(void);

@@ -239,6 +239,57 @@ def test_step_validation():
     assert st == bd.SV_EINVAL and 'attention' in L.sv_last_error().decode()
 
 
+def _hybrid_step(L, last_gdn_q=16, k_scale=16, acc_res=16):
+    """A 4-layer step (GDN, GDN, GDN, attention) with fake aligned pointers."""
+    b = _batch()
+    kinds = (ctypes.c_uint8 * 4)(0, 0, 0, 1)
+    acfg = bd.SvAttnConfig(32, 8, 128, 64, 8, 4, 16, bd.SV_BF16, 0.0,
+                           bd.SV_KV_INT8 if k_scale != 16 else bd.SV_KV_PLAIN)
+    lay = (bd.SvAttnLayer * 1)(bd.SvAttnLayer(16, 16, 16, 16, 16, 16, k_scale, 16))
+    gcfg = bd.SvGdnConfig(4, 128, 128, 2, None, bd.SV_BF16, bd.SV_F32)
+    g = [bd.SvGdnLayer(16, 16, 16, 16, 16, 16, 16) for _ in range(2)]
+    g.append(bd.SvGdnLayer(16, last_gdn_q, 16, 16, 16, 16, 16))
+    gl = (bd.SvGdnLayer * 3)(*g)
+    acc = bd.SvAcceptArgs(0, bd.SV_BF16, 100, 16, None, 16, None, None)
+    return L.spec_verify_step(ctypes.byref(b), 4, kinds, ctypes.byref(acfg), lay,
+                              ctypes.byref(gcfg), gl, ctypes.byref(acc), 16, acc_res, 16, 0,
+                              None, 16, 1 << 30, None, None)
+
+
+@pytest.mark.parametrize('bad,layer', [
+    (dict(last_gdn_q=24), 'layer 2'),        # misaligned q of the last GDN layer
+    (dict(k_scale=None), 'layer 3'),         # INT8 attention layer without scales
+    (dict(acc_res=None), 'result'),          # acceptance output missing
+])
+def test_step_checks_every_layer_before_any_launch(bad, layer):
+    """A refused step returns before its first launch: on a host without a GPU
+    any launch would fail with SV_EHIP, so a host-side refusal of the last
+    layer (or of the acceptance) proves no earlier layer was launched."""
+    L = bd.lib()
+    st = _hybrid_step(L, **bad)
+    assert st in (bd.SV_EINVAL, bd.SV_EDTYPE), L.sv_last_error().decode()
+    assert layer in L.sv_last_error().decode()
+
+
+def test_device_error_calls_validate():
+    L = bd.lib()
+    assert L.sv_read_device_error(None, None) == -1
+    assert 'null' in L.sv_last_error().decode()
+    assert L.sv_clear_device_error(None, None) == bd.SV_EINVAL
+
+
+def test_aggregate_workspace_covers_every_call():
+    L = bd.lib()
+    B, T, Hq, Hkv, D, V, mp = 64, 4, 32, 8, 128, 151936, 130
+    agg = L.sv_workspace_bytes(B, T, Hq, D, V, mp)
+    for dt in (bd.SV_BF16, bd.SV_F32):
+        assert agg >= L.spec_verify_attention_workspace_bytes(B, B * T, Hq, Hkv, D, mp, 64, dt)
+    for mode in (bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION):
+        assert agg >= L.spec_accept_workspace_bytes(B, B * T, V, mode)
+    assert L.sv_workspace_bytes(B, 9, Hq, D, V, mp) == 0          # max_T beyond the limit
+    assert L.sv_workspace_bytes(0, T, Hq, D, V, mp) == 0
+
+
 def test_workspace_sizes_are_consistent():
     L = bd.lib()
     a = L.spec_verify_attention_workspace_bytes(64, 256, 32, 8, 128, 130, 64, bd.SV_BF16)

@@ -183,9 +183,14 @@ def test_bad_draft_token_is_flagged():
     batch = wl.make_batch(w, 0, DEV)
     a = wl.make_accept(w, batch, 1, 'rejection', DEV)
     a['draft_tokens'][1] = w.V + 5
-    acc, out, commit, ctx, err = _run(batch, a, bd.SV_ACCEPT_REJECTION)
-    assert err & 16
-    assert commit[0] == -7 and ctx[0] == batch.ctx[0]       # sequence 0 skipped
+    for mode in (bd.SV_ACCEPT_REJECTION, bd.SV_ACCEPT_GREEDY):
+        acc, out, commit, ctx, err = _run(batch, a, mode)
+        assert err == 16                                     # SV_DERR_TOKEN only
+        # sequence 0 skipped: accept_len -1, a row of -1, commit length 0,
+        # ctx_lens kept; sequence 1 decided as usual
+        assert acc[0] == -1 and (out[0] == -1).all()
+        assert commit[0] == 0 and ctx[0] == batch.ctx[0]
+        assert acc[1] >= 0 and commit[1] == acc[1] + 1
 
 
 # ------------------------------------------------ point-mass drafts, supplied bonus
@@ -231,4 +236,5 @@ def test_bad_bonus_is_flagged_and_skipped():
     acc, out, commit, ctx, err = _run(batch, a, bd.SV_ACCEPT_GREEDY, bonus=bonus)
     assert err & 16
     assert acc[0] == batch.max_T - 1 and out[0, batch.max_T - 1] == 3
-    assert acc[1] == -7 and commit[1] == -7                  # skipped, untouched
+    assert acc[1] == -1 and (out[1] == -1).all() and commit[1] == 0   # skipped
+    assert ctx[1] == batch.ctx[1]

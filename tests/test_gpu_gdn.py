@@ -165,6 +165,71 @@ def test_deferred_pending_then_verify():
     assert torch.equal(st_two, st)
 
 
+def _edge_gates(batch, w, seed):
+    """Per (token, head): alpha from {0, 1e-12, 1e-6, 0.5, 1}, beta from {0, 1}."""
+    g = wl.generator(seed)
+    alphas = torch.tensor([0.0, 1e-12, 1e-6, 0.5, 1.0])
+    betas = torch.tensor([0.0, 1.0])
+    shape = (batch.total_T, w.H)
+    a = alphas[torch.randint(0, 5, shape, generator=g)].float().contiguous().to(DEV)
+    b = betas[torch.randint(0, 2, shape, generator=g)].float().contiguous().to(DEV)
+    return a, b
+
+
+def _min_decay(alpha, cu):
+    """Smallest running product of the alphas within a sequence (in fp32, as
+    the kernel keeps its deferred decay)."""
+    al = alpha.cpu().numpy()
+    m = 1.0
+    for b in range(len(cu) - 1):
+        run = np.ones(al.shape[1], np.float32)
+        for x in range(cu[b], cu[b + 1]):
+            run = run * al[x]
+            m = min(m, float(run.min()))
+    return m
+
+
+@pytest.mark.parametrize('deferred', [False, True])
+def test_gate_edge_values(deferred):
+    """alpha = 0 and alphas whose running product falls below 2^-20 (the
+    kernel then applies the decay to the state registers at once), beta 0 or
+    1, committed at every c_b in 0..T_b; deferred: the same gates in the
+    replayed pending tokens, then a verify from the replayed state."""
+    w = wl.WORKLOADS[2]
+    batch = wl.make_batch(w, 31, DEV)
+    g = wl.make_gdn_layer(w, batch, 32, DEV)
+    g['alpha'], g['beta'] = _edge_gates(batch, w, 33)
+    cu = npi(batch.cu_seqlens)
+    assert _min_decay(g['alpha'], cu) < 2.0 ** -20
+    commit = (torch.arange(batch.B) % (max(batch.T) + 1)).to(torch.int32).to(DEV)
+    say('GDN edge gates, deferred' if deferred else 'GDN edge gates, verify+commit')
+    if not deferred:
+        out, st, err = _run(batch, g, bd.SV_GDN_VERIFY_COMMIT, commit)
+        assert err == 0
+        o_ref, S_ref = _oracle(batch, g, oracle.GDN_VERIFY_COMMIT, commit)
+        e_s = check_gdn_state(np64(st), S_ref)
+        e_o = check_gdn_out(np64(out), o_ref, torch.bfloat16)
+        say(f'  state err {e_s:.2e}  out err {e_o:.2e}')
+        _, st2, _ = _run(batch, g, bd.SV_GDN_COMMIT_ONLY, commit)
+        assert torch.equal(st2, st)
+        return
+    cur = wl.make_gdn_layer(w, batch, 34, DEV)
+    cur['alpha'], cur['beta'] = _edge_gates(batch, w, 35)
+    cur['state'] = g['state']
+    pend = bd.make_gdn_pending(sv_batch(batch), g['k'], g['v'], g['alpha'], g['beta'], commit)
+    out, st, err = _run(batch, cur, bd.SV_GDN_VERIFY_ONLY, None, pending=pend)
+    assert err == 0
+    _, S_mid = _oracle(batch, g, oracle.GDN_COMMIT_ONLY, commit)
+    e_s = check_gdn_state(np64(st), S_mid)
+    o_ref, _ = oracle.gdn_step(S_mid, None, np64(cur['q']), np64(cur['k']), np64(cur['v']),
+                               np64(cur['alpha']), np64(cur['beta']), cu, None,
+                               oracle.GDN_VERIFY_ONLY)
+    e_o = check_gdn_out(np64(out), o_ref, torch.bfloat16)
+    say(f'  state err {e_s:.2e}  out err {e_o:.2e}')
+    _, st_two, _ = _run(batch, g, bd.SV_GDN_COMMIT_ONLY, commit)
+    assert torch.equal(st_two, st)
+
+
 def test_bad_commit_length_is_flagged_and_skipped():
     w = wl.WORKLOADS[0]
     batch = wl.make_batch(w, 0, DEV)

@@ -34,7 +34,7 @@ def make_step(w, batch, seed, mode, state_dtype=torch.float32):
 
 
 def run_step(w, batch, layers, acc, mode, schedule=bd.SV_SCHEDULE_TWO_PHASE, pending=None,
-             ctx=None):
+             ctx=None, commit_fill=-7):
     dt_a = bd.SV_BF16 if w.attn_dtype == torch.bfloat16 else bd.SV_F32
     dt_g = bd.SV_BF16 if w.gdn_dtype == torch.bfloat16 else bd.SV_F32
     a_layers = [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
@@ -54,7 +54,7 @@ def run_step(w, batch, layers, acc, mode, schedule=bd.SV_SCHEDULE_TWO_PHASE, pen
     ws = torch.zeros(max(1, bd.spec_verify_step_workspace_bytes(sb, args)), dtype=torch.uint8,
                      device=DEV)
     result = torch.full((batch.B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
-    commit = torch.full((batch.B,), -7, dtype=torch.int32, device=DEV)
+    commit = torch.full((batch.B,), commit_fill, dtype=torch.int32, device=DEV)
     ctx = (batch.ctx_lens if ctx is None else ctx).clone()
     err = err_word()
     bd.spec_verify_step(sb, args, ctx, result, commit, schedule=schedule, pending=pending,
@@ -290,3 +290,81 @@ def test_step_with_int8_kv_pages():
                                    np64(b0['alpha']), np64(b0['beta']), cu, a_ref + 1,
                                    oracle.GDN_COMMIT_ONLY)
             check_gdn_state(np64(l['state']), S)
+
+
+@pytest.mark.parametrize("mode", [bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION])
+def test_out_of_vocabulary_draft_skips_the_sequence(mode):
+    """A draft id outside the vocabulary flags SV_DERR_TOKEN and skips its
+    sequence: accept_len -1, a row of -1, commit length 0 (over a commit
+    buffer that held a valid length from an earlier step), ctx_lens kept, so
+    the batched two-phase commit and a later deferred flush leave its GDN
+    states bit for bit.  Every other sequence matches the oracle."""
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1)})
+    batch = wl.make_batch(w, 25, DEV)
+    name = 'greedy' if mode == bd.SV_ACCEPT_GREEDY else 'rejection'
+    layers, acc = make_step(w, batch, 26, name)
+    bad_b = 3
+    cu = npi(batch.cu_seqlens)
+    good_drafts = acc['draft_tokens'].clone()
+    acc['draft_tokens'][cu[bad_b] - bad_b + 1] = w.V + 5       # its second draft
+    ref = oracle_step(w, batch, layers, dict(acc, draft_tokens=good_drafts), mode)
+    before = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in l.items()}
+              for l in layers]
+    say('out-of-vocabulary draft, mode', name)
+    res = run_step(w, batch, layers, acc, mode, commit_fill=2)
+    assert res['err'] == 16, res['err']                          # SV_DERR_TOKEN
+    others = [b for b in range(batch.B) if b != bad_b]
+    assert res['acc'][bad_b] == -1 and (res['out'][bad_b] == -1).all()
+    assert int(res['commit'][bad_b]) == 0
+    assert int(res['ctx'][bad_b]) == batch.ctx[bad_b]
+    np.testing.assert_array_equal(res['acc'][others], ref['accept_len'][others])
+    np.testing.assert_array_equal(res['out'][others], ref['out_tokens'][others])
+    np.testing.assert_array_equal(npi(res['commit'])[others], ref['commit_len'][others])
+    np.testing.assert_array_equal(npi(res['ctx'])[others], ref['ctx_lens'][others])
+    for i, (l, b0) in enumerate(zip(layers, before)):
+        if l['kind'] == 'gdn':
+            assert torch.equal(l['state'][bad_b], b0['state'][bad_b])
+            S_ref = ref['state'][i]
+            check_gdn_state(np64(l['state'][others]), S_ref[others])
+            # a deferred flush with this commit buffer keeps it too
+            st = l['state'].clone()
+            bd.gdn_verify_commit(sv_batch(batch), bd.SV_GDN_COMMIT_ONLY, st, l['q'], l['k'],
+                                 l['v'], l['alpha'], l['beta'], res['commit'], l['out'])
+            torch.cuda.synchronize()
+            assert torch.equal(st[bad_b], b0['state'][bad_b])
+
+
+def test_refused_step_changes_nothing():
+    """A step whose last GDN layer is refused on the host (misaligned q)
+    returns the error before any launch: no page, state, length, pending
+    replay or output has changed, so a retry after the fix replays the
+    pending tokens exactly once."""
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(2)})
+    batch = wl.make_batch(w, 27, DEV, reserve=8)
+    layers, acc = make_step(w, batch, 28, 'rejection')
+    gdn = [l for l in layers if l['kind'] == 'gdn']
+    commit_prev = wl.make_commit_len(batch, 29, device=DEV)
+    pl = [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'], l['out'])
+          for l in gdn]
+    arr = (bd.SvGdnLayer * len(pl))(*pl)
+    pend = bd.SvStepPending(sv_batch(batch), arr, commit_prev.data_ptr())
+    before = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in l.items()}
+              for l in layers]
+    # the last GDN layer's q, shifted by one bf16 element: not 16-byte aligned
+    q_bad = torch.empty(gdn[-1]['q'].numel() + 8, dtype=gdn[-1]['q'].dtype, device=DEV)
+    good_q = gdn[-1]['q']
+    gdn[-1]['q'] = q_bad[1:1 + good_q.numel()].view(good_q.shape)
+    ctx = batch.ctx_lens.clone()
+    with pytest.raises(bd.SpecVerifyError) as ei:
+        run_step(w, batch, layers, acc, bd.SV_ACCEPT_REJECTION,
+                 schedule=bd.SV_SCHEDULE_DEFERRED, pending=pend, ctx=ctx)
+    assert 'aligned' in str(ei.value)
+    torch.cuda.synchronize()
+    for l, b0 in zip(layers, before):
+        for key in ('state', 'k_cache', 'v_cache', 'out'):
+            if key in l:
+                assert torch.equal(l[key], b0[key]) or (
+                    key == 'out' and torch.isnan(l[key].float()).all()), key
+    assert torch.equal(ctx, batch.ctx_lens)

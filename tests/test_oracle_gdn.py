@@ -3,6 +3,9 @@
 * a hand-derived two-token example with exact binary fractions
   (tests/golden/gdn_two_token_2x2.txt);
 * special cases: alpha = 1, beta = 0 leaves the state unchanged bit for bit;
+  alpha = 0, beta = 1 with a unit key stores v k^T and outputs v (k . q);
+  alpha = 0, beta = 0 zeroes the state; beta = 0 scales it by the product of
+  the alphas, however small;
   beta = 1 with a unit key makes S_t k_t = v_t for any alpha; with q = k and a
   unit key, o_t = alpha (1 - beta) S_{t-1} k + beta v;
 * an independent formulation: the unrolled product
@@ -95,6 +98,41 @@ def test_beta_one_unit_key_stores_value():
         for h in range(3):
             np.testing.assert_allclose(S[b, h] @ c['k'][b, h], c['v'][b, h],
                                        rtol=0, atol=1e-13)
+
+
+def test_zero_and_tiny_decay_closed_forms():
+    """Gates at the edge of their range.  alpha = 0 and beta = 1 with a unit
+    key: every token forgets the state and stores v k^T, so S_t = v_t k_t^T
+    and o_t = v_t (k_t . q_t); alpha = 0 and beta = 0 zero the state and the
+    output; beta = 0 with a tiny alpha scales the state by the product of the
+    alphas (1e-12 * 1e-6 ... far below 2^-20)."""
+    rng = np.random.default_rng(12)
+    T = [1, 2, 3, 4]
+    c = _rand_case(rng, T)
+    c['alpha'][:] = 0.0
+    c['beta'][:] = 1.0
+    o, S = oracle.gdn_step(c['state'], None, c['q'], c['k'], c['v'], c['alpha'], c['beta'],
+                           c['cu'], np.array(T), GDN_VERIFY_COMMIT)
+    for b in range(len(T)):
+        last = c['cu'][b + 1] - 1
+        for h in range(3):
+            np.testing.assert_allclose(S[b, h], np.outer(c['v'][last, h], c['k'][last, h]),
+                                       rtol=0, atol=1e-15)
+            for x in range(c['cu'][b], c['cu'][b + 1]):
+                np.testing.assert_allclose(o[x, h], c['v'][x, h] * (c['k'][x, h] @ c['q'][x, h]),
+                                           rtol=0, atol=1e-14)
+    c['beta'][:] = 0.0
+    o, S = oracle.gdn_step(c['state'], None, c['q'], c['k'], c['v'], c['alpha'], c['beta'],
+                           c['cu'], np.array(T), GDN_VERIFY_COMMIT)
+    assert not S.any() and not o.any()
+    c['alpha'] = np.where(np.arange(len(c['alpha']))[:, None] % 2 == 0, 1e-12, 1e-6) \
+        * np.ones_like(c['alpha'])
+    _, S = oracle.gdn_step(c['state'], None, c['q'], c['k'], c['v'], c['alpha'], c['beta'],
+                           c['cu'], np.array(T), GDN_VERIFY_COMMIT)
+    for b in range(len(T)):
+        prod = np.prod(c['alpha'][c['cu'][b]:c['cu'][b + 1]], axis=0)
+        for h in range(3):
+            np.testing.assert_allclose(S[b, h], prod[h] * c['state'][b, h], rtol=1e-14, atol=0)
 
 
 def test_output_closed_form_with_q_equal_k():
