@@ -118,6 +118,9 @@ _SIGS = {
     'spec_accept_args': (
         [ctypes.POINTER(SvBatch), ctypes.POINTER(SvAcceptArgs), _vp, _vp, _vp, _vp, _sz, _vp,
          _vp], ctypes.c_int),
+    'spec_accept_noalloc': (
+        [ctypes.POINTER(SvBatch), ctypes.POINTER(SvAcceptArgs), _vp, _vp, _vp, _vp, _vp],
+        ctypes.c_int),
     'spec_accept': (
         [ctypes.POINTER(SvBatch), ctypes.c_int, _vp, _vp, ctypes.c_int, _c_i32,
          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
@@ -401,6 +404,19 @@ def spec_accept(batch, mode, target_logits, draft_tokens, result,
         _ptr(u_accept), _ptr(u_final), _i32(result, 'result'),
         _i32(commit_len_out, 'commit_len_out'), _i32(ctx_lens_inout, 'ctx_lens'),
         _ptr(workspace), ws_n, _i32(err, 'err'), _stream(stream)))
+
+
+def spec_accept_noalloc(batch, mode, target_logits, draft_tokens, result, draft_logits=None,
+                        u_accept=None, u_final=None, commit_len_out=None, ctx_lens_inout=None,
+                        err=None, stream=None, bonus_tokens=None):
+    """Acceptance with the library's own scratch (``spec_accept_noalloc``): no
+    workspace argument, nothing allocated."""
+    acc = accept_args(mode, target_logits, draft_tokens, draft_logits, u_accept, u_final,
+                      bonus_tokens)
+    _check(lib().spec_accept_noalloc(
+        ctypes.byref(batch), ctypes.byref(acc), _i32(result, 'result'),
+        _i32(commit_len_out, 'commit_len_out'), _i32(ctx_lens_inout, 'ctx_lens'),
+        _i32(err, 'err'), _stream(stream)))
 
 
 class StepArgs:

@@ -26,11 +26,40 @@
 // load, otherwise with coalesced stride-256 element loads, so any V and any
 // row alignment is supported.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "exp2_table.h"
 #include "internal.h"
 
 namespace sv {
+
+// Scratch of spec_accept_noalloc: kAcceptScratchBytes in every GPU's copy of
+// this code object, kept until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it names a stand-in, not device
+// memory): accept_scratch() returns the device address of the current GPU's
+// copy.  Every call on one GPU shares it; calls that overlap on a GPU race.
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+
+hipError_t accept_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 namespace {
 
 constexpr int kChunk = 4096;

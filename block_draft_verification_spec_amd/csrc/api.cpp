@@ -164,8 +164,9 @@ sv_status check_gdn_common(const sv_batch* batch, void* state, sv_dtype state_dt
   return SV_OK;
 }
 
-sv_status check_accept(const sv_batch* batch, const sv_accept_args* acc, const int32_t* result,
-                       const void* workspace, size_t workspace_bytes, const char* who) {
+// Every acceptance argument except the workspace.
+sv_status check_accept_args(const sv_batch* batch, const sv_accept_args* acc,
+                            const int32_t* result, const char* who) {
   sv_status st = check_batch(batch, who);
   if (st != SV_OK) return st;
   const sv_accept_mode mode = acc->mode;
@@ -183,7 +184,14 @@ sv_status check_accept(const sv_batch* batch, const sv_accept_args* acc, const i
   if (mode == SV_ACCEPT_REJECTION &&
       (!acc->u_final || (batch->total_T > batch->B && !acc->u_accept)))
     return fail(SV_EINVAL, "%s: rejection needs u_accept and u_final", who);
-  const size_t need = sv::accept_workspace_bytes(batch->B, batch->total_T, V, mode);
+  return SV_OK;
+}
+
+sv_status check_accept(const sv_batch* batch, const sv_accept_args* acc, const int32_t* result,
+                       const void* workspace, size_t workspace_bytes, const char* who) {
+  sv_status st = check_accept_args(batch, acc, result, who);
+  if (st != SV_OK) return st;
+  const size_t need = sv::accept_workspace_bytes(batch->B, batch->total_T, acc->V, acc->mode);
   if (!workspace || workspace_bytes < need)
     return fail(SV_EWORKSPACE, "%s: workspace needs %zu bytes (got %zu)", who, need,
                 workspace ? workspace_bytes : size_t(0));
@@ -223,11 +231,24 @@ sv_status check_gdn_call(const sv_batch* batch, sv_gdn_mode mode, const void* st
   return SV_OK;
 }
 
+sv_status launch_accept_checked(const sv_batch* batch, const sv_accept_args* acc,
+                                int32_t* result, int32_t* commit_len_out,
+                                int32_t* ctx_lens_inout, void* workspace, int32_t* err,
+                                hipStream_t stream, const char* who);
+
 sv_status accept_impl(const sv_batch* batch, const sv_accept_args* acc, int32_t* result,
                       int32_t* commit_len_out, int32_t* ctx_lens_inout, void* workspace,
                       size_t workspace_bytes, int32_t* err, hipStream_t stream, const char* who) {
   sv_status st = check_accept(batch, acc, result, workspace, workspace_bytes, who);
   if (st != SV_OK) return st;
+  return launch_accept_checked(batch, acc, result, commit_len_out, ctx_lens_inout, workspace,
+                               err, stream, who);
+}
+
+sv_status launch_accept_checked(const sv_batch* batch, const sv_accept_args* acc,
+                                int32_t* result, int32_t* commit_len_out,
+                                int32_t* ctx_lens_inout, void* workspace, int32_t* err,
+                                hipStream_t stream, const char* who) {
   const sv_accept_mode mode = acc->mode;
   const int32_t V = acc->V;
   sv::AcceptArgs a{};
@@ -653,6 +674,24 @@ sv_status spec_accept_args(const sv_batch* batch, const sv_accept_args* acc, int
   if (!acc) return fail(SV_EINVAL, "spec_accept_args: acc is null");
   return accept_impl(batch, acc, result, commit_len_out, ctx_lens_inout, workspace,
                      workspace_bytes, err, stream, "spec_accept_args");
+}
+
+sv_status spec_accept_noalloc(const sv_batch* batch, const sv_accept_args* acc, int32_t* result,
+                              int32_t* commit_len_out, int32_t* ctx_lens_inout, int32_t* err,
+                              hipStream_t stream) {
+  const char* who = "spec_accept_noalloc";
+  if (!acc) return fail(SV_EINVAL, "%s: acc is null", who);
+  sv_status st = check_accept_args(batch, acc, result, who);
+  if (st != SV_OK) return st;
+  const size_t need = sv::accept_workspace_bytes(batch->B, batch->total_T, acc->V, acc->mode);
+  if (need > sv::kAcceptScratchBytes)
+    return fail(SV_ECAPACITY, "%s: this batch needs %zu bytes of scratch, the library holds %zu",
+                who, need, sv::kAcceptScratchBytes);
+  void* scratch_ptr = nullptr;
+  st = hip_status(sv::accept_scratch(&scratch_ptr), who);
+  if (st != SV_OK) return st;
+  return launch_accept_checked(batch, acc, result, commit_len_out, ctx_lens_inout, scratch_ptr,
+                               err, stream, who);
 }
 
 size_t spec_verify_step_workspace_bytes(const sv_batch* batch, const sv_attn_config* acfg,

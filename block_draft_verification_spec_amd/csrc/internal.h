@@ -139,6 +139,11 @@ struct AcceptArgs {
 };
 
 size_t accept_workspace_bytes(int B, int total_T, int V, int mode);
+// Scratch of the allocation-free acceptance: a device array of the library,
+// one per GPU.  accept_scratch gives the current device's address (looked up
+// once per device with that device current).
+constexpr size_t kAcceptScratchBytes = size_t(8) << 20;
+hipError_t accept_scratch(void** ptr);
 // Fill n int32 words with v on the stream (a kernel, so it can be captured).
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, sv_dtype dtype,

@@ -298,6 +298,20 @@ SV_API sv_status spec_accept_args(const sv_batch* batch, const sv_accept_args* a
     int32_t* result, int32_t* commit_len_out, int32_t* ctx_lens_inout,
     void* workspace, size_t workspace_bytes, int32_t* err, hipStream_t stream);
 
+/* The same acceptance for callers that cannot allocate or pass a workspace
+ * (code under graph capture, tight serving loops, hosts that forbid device
+ * allocation): the scratch is a device array inside the library, 8 MiB on
+ * every GPU it runs on, held until the process ends.  A batch whose
+ * spec_accept_workspace_bytes() exceeds 8 MiB (2^23 bytes) is refused with
+ * SV_ECAPACITY.  It calls no allocator; its first call on a GPU looks up that
+ * GPU's scratch address (make it outside a graph capture).  Every call on one
+ * GPU shares the scratch: calls that overlap on one GPU (two streams, two
+ * threads) race and must be ordered by the caller.  Results are those of
+ * spec_accept_args with the same arguments. */
+SV_API sv_status spec_accept_noalloc(const sv_batch* batch, const sv_accept_args* acc,
+    int32_t* result, int32_t* commit_len_out, int32_t* ctx_lens_inout, int32_t* err,
+    hipStream_t stream);
+
 SV_API sv_status spec_accept(const sv_batch* batch, sv_accept_mode mode,
     const void* target_logits, const void* draft_logits, sv_dtype logit_dtype,
     int32_t V, const int32_t* draft_tokens, const float* u_accept,
