@@ -1,21 +1,29 @@
 """Benchmark of the block speculative-verification step on one MI355X.
 
-Workload: the full hybrid verify step (64 layers, GDN,GDN,GDN,ATT x 16;
-B = 64 sequences, k = 3 drafts, contexts ~U[2048, 8192], 32q/8kv heads,
-D = 128, bf16 paged KV in 64-token pages; 48 GDN layers with 32 heads,
-dk = dv = 128, fp32 state; acceptance over V = 151936 bf16 logits),
-synthetic seeded inputs resident in HBM before timing starts.
+Default workload (--workload 3, hybrid_step_64l): the full hybrid verify
+step (64 layers, GDN,GDN,GDN,ATT x 16; B = 64 sequences, k = 3 drafts,
+contexts ~U[2048, 8192], 32q/8kv heads, D = 128, bf16 paged KV in 64-token
+pages; 48 GDN layers with 32 heads, dk = dv = 128, fp32 state; acceptance
+over V = 151936 bf16 logits), synthetic seeded inputs resident in HBM before
+timing starts.  --workload 0 / 4 run the tiny fp32 step and the 256-sequence
+stress step the same way; --workload 1 / 2 time one paged-attention call /
+one GDN verify+commit call per step, rotating over buffer sets of >= 1 GB in
+total so the last-level cache cannot serve them.
 
 A step = one call of spec_verify_step: every layer's verify pass, the
 acceptance, the GDN commit (deferred schedule: folded into the next step's
 verify pass; the timed region ends with a flush so every accepted token of
-every timed step is committed) and the ctx_lens update.
+every timed step is committed) and the ctx_lens update.  The same steps are
+also captured into HIP graphs and replayed (reported beside the eager
+figures).
 
 Prints one JSON line.  value = verified draft tokens per second (sum_b k_b
-per step).  Also reported: algorithmic HBM bytes per step and GB/s (% of the
-8 TB/s peak), the roofline of the dominant kernel (the paged attention call,
-timed over back-to-back launches with HIP events on the stream it runs on),
-and the CPU oracle timed on a bounded sample of the same workload.
+per step) over the timed steps; the per-step median, p10 and p90 come from
+HIP events between the steps.  Also reported: algorithmic HBM bytes per
+step and GB/s (% of the 8 TB/s peak and of the copy / read rates measured
+in the same run), the roofline of the dominant kernel (timed over
+back-to-back launches with HIP events on the stream it runs on), and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
@@ -41,6 +49,9 @@ def parse():
     p.add_argument('--accept', choices=['rejection', 'greedy'], default='rejection')
     p.add_argument('--schedule', choices=['deferred', 'two_phase'], default='deferred')
     p.add_argument('--no-cpu-baseline', action='store_true')
+    p.add_argument('--no-graph', action='store_true', help='skip the graph-replay timing')
+    p.add_argument('--no-next-rows', action='store_true',
+                   help='skip the side timings of the NEXT rows (hybrid step only)')
     p.add_argument('--attn-reps', type=int, default=3,
                    help='passes over the attention layers for the per-launch timing')
     p.add_argument('--seed', type=int, default=3)
@@ -276,25 +287,33 @@ def measured_traffic():
     return int(float(vals['fetch_bytes_per_launch']) + float(vals['write_bytes_per_launch']))
 
 
-def attn_bytes(w, batch):
-    """Algorithmic HBM bytes of one attention layer (one launch)."""
-    s = 2  # bf16
-    ctx = sum(batch.ctx)
+def elem_size(dtype):
+    import torch
+    return torch.finfo(dtype).bits // 8
+
+
+def attn_bytes(w, batch, ctx=None):
+    """Algorithmic HBM bytes of one attention layer (one launch) at the given
+    contexts (default: the batch's)."""
+    s = elem_size(w.attn_dtype)
+    ctx_sum = sum(batch.ctx if ctx is None else ctx)
     T = batch.total_T
-    kv_ctx = ctx * w.Hkv * w.D * 2 * s
+    kv_ctx = ctx_sum * w.Hkv * w.D * 2 * s
     per_tok = w.Hq * w.D * s + 2 * w.Hkv * w.D * s + 2 * w.Hkv * w.D * s + w.Hq * w.D * s
-    return kv_ctx + T * per_tok + batch.B * batch.block_table.shape[1] * 4
+    return int(kv_ctx + T * per_tok + batch.B * batch.block_table.shape[1] * 4)
 
 
 def gdn_bytes(w, batch):
-    s = 2
+    """One GDN layer: the state read and written once (the method's minimum),
+    q, k, v, the gates and the outputs."""
+    s = elem_size(w.gdn_dtype)
     T = batch.total_T
     return (2 * batch.B * w.H * w.dv * w.dk * 4 + T * w.H * (2 * w.dk + w.dv) * s
             + T * w.H * 8 + T * w.H * w.dv * s)
 
 
 def accept_bytes(w, batch, mode):
-    s = 2
+    s = elem_size(w.logit_dtype)
     T = batch.total_T
     b = T * w.V * s
     if mode == 'rejection':
@@ -302,12 +321,70 @@ def accept_bytes(w, batch, mode):
     return b
 
 
-def cpu_baseline(w, batch, layers, acc, mode, draft_tokens_per_step, budget):
+def ceilings(dev):
+    """Rates of plain streaming kernels on this GPU, measured in this run:
+    a device copy of 2 GiB (read + write bytes), row sums of a 4 GiB fp32
+    array in rows of 4096 (read bytes: the output is 1/4096 of the input)
+    and a fill of 2 GiB (write bytes)."""
+    import torch
+    n = 1 << 31
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes):
+        for _ in range(2):
+            fn()
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    copy = rate(lambda: y.copy_(x), 2 * n)
+    write = rate(lambda: y.fill_(1.0), n)
+    del x, y
+    z = torch.ones(2 * n // 4, dtype=torch.float32, device=dev)
+    read = rate(lambda: z.view(-1, 4096).sum(dim=1), 2 * n)
+    del z
+    torch.cuda.empty_cache()
+    return {'copy_GBps': copy, 'read_GBps': read, 'write_GBps': write,
+            'how': 'torch copy_ of 2 GiB (read + write bytes), row sums over 4 GiB in rows of '
+                   '4096 fp32 (read bytes), fill of 2 GiB (write bytes); 5 repetitions each '
+                   'between HIP events'}
+
+
+def percentiles(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {'median': round(float(np.median(a)), 4), 'p10': round(float(np.percentile(a, 10)), 4),
+            'p90': round(float(np.percentile(a, 90)), 4), 'n': int(a.size)}
+
+
+def timed_calls(stream, calls):
+    """Run the callables back to back on `stream` with a HIP event before
+    each one and after the last; returns the per-call times (ms) and the
+    total (ms)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i, c in enumerate(calls):
+        c()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))]
+    return per, ev[0].elapsed_time(ev[-1])
+
+
+def cpu_baseline(w, batch, layers, acc, mode, draft_tokens_per_step, budget, commit=None):
     """The oracle as it stands, on a bounded sample, scaled to one step.
 
     Within a time budget: GDN layers on the full batch, one at a time (at
-    least one); attention of one layer, one sequence at a time (its pages
-    only; at least one), scaled to the whole batch by context length;
+    least one), each the oracle step's two passes (verify, then the commit of
+    the accepted tokens; with `commit` given and no acceptance, the single
+    verify-and-commit pass); attention of one layer, one sequence at a time (its
+    pages only; at least one), scaled to the whole batch by context length;
     acceptance on all rows.  The per-layer costs are then multiplied by the
     layer counts of the step.
     """
@@ -325,85 +402,109 @@ def cpu_baseline(w, batch, layers, acc, mode, draft_tokens_per_step, budget):
     cu = i64(batch.cu_seqlens)
     ctx = i64(batch.ctx_lens)
     table = i64(batch.block_table)
-    # acceptance on the full batch
-    ai = [f64(acc['target_logits']), i64(acc['draft_tokens'])]
-    t0 = time.perf_counter()
-    if mode == 'greedy':
-        oracle.greedy_accept(ai[0], ai[1], cu, batch.max_T)
-    else:
-        oracle.rejection_accept(ai[0], f64(acc['draft_logits']), ai[1], f64(acc['u_accept']),
-                                f64(acc['u_final']), cu, batch.max_T)
-    t_acc = time.perf_counter() - t0
-    # GDN layers on the full batch
-    gdn = [l for l in layers if l['kind'] == 'gdn']
-    t_gdn_sum, n_gdn_done = 0.0, 0
-    for g in gdn:
-        args = (f64(g['state']), None, f64(g['q']), f64(g['k']), f64(g['v']),
-                f64(g['alpha']), f64(g['beta']), cu, None, oracle.GDN_VERIFY_ONLY)
+    parts = []
+    t_acc = 0.0
+    if acc is not None:
+        ai = [f64(acc['target_logits']), i64(acc['draft_tokens'])]
         t0 = time.perf_counter()
-        oracle.gdn_step(*args)
+        if mode == 'greedy':
+            a_len, _ = oracle.greedy_accept(ai[0], ai[1], cu, batch.max_T)
+        else:
+            a_len, _ = oracle.rejection_accept(ai[0], f64(acc['draft_logits']), ai[1],
+                                               f64(acc['u_accept']), f64(acc['u_final']), cu,
+                                               batch.max_T)
+        t_acc = time.perf_counter() - t0
+        commit = a_len + 1
+        parts.append(f'{mode} acceptance on all rows')
+    gdn = [l for l in layers if l['kind'] == 'gdn']
+    t_gdn, n_gdn_done, t_gdn_sum = 0.0, 0, 0.0
+    for g in gdn:
+        S, q, k, v = f64(g['state']), f64(g['q']), f64(g['k']), f64(g['v'])
+        al, be = f64(g['alpha']), f64(g['beta'])
+        t0 = time.perf_counter()
+        if acc is not None:
+            oracle.gdn_step(S, None, q, k, v, al, be, cu, None, oracle.GDN_VERIFY_ONLY)
+            oracle.gdn_step(S, None, None, k, v, al, be, cu, commit, oracle.GDN_COMMIT_ONLY)
+        else:
+            oracle.gdn_step(S, None, q, k, v, al, be, cu, i64(commit), oracle.GDN_VERIFY_COMMIT)
         t_gdn_sum += time.perf_counter() - t0
         n_gdn_done += 1
         if t_gdn_sum > 0.4 * budget:
             break
-    t_gdn = t_gdn_sum / n_gdn_done
-    # attention, sequence by sequence
-    a = next(l for l in layers if l['kind'] == 'attn')
-    t_att_sample, seqs = 0.0, []
-    for b in range(batch.B):
-        pages = table[b][table[b] >= 0]
-        idx = torch.from_numpy(pages).to(a['k_cache'].device)
-        kc, vc = f64(a['k_cache'][idx]), f64(a['v_cache'][idx])
-        sub_t = np.arange(len(pages))[None, :]
-        rows = slice(cu[b], cu[b + 1])
-        q, kn, vn = f64(a['q'][rows]), f64(a['k_new'][rows]), f64(a['v_new'][rows])
-        t0 = time.perf_counter()
-        oracle.verify_attention(q, kn, vn, kc, vc, sub_t, ctx[b:b + 1],
-                                np.array([0, cu[b + 1] - cu[b]]), batch.P)
-        t_att_sample += time.perf_counter() - t0
-        seqs.append(b)
-        if t_att_sample > 0.5 * budget:
-            break
-    t_att = t_att_sample * float(ctx.sum()) / float(ctx[seqs].sum())
-    n_att = sum(1 for l in layers if l['kind'] == 'attn')
-    n_gdn = len(layers) - n_att
+    if n_gdn_done:
+        t_gdn = t_gdn_sum / n_gdn_done
+        parts.append(f'{n_gdn_done} GDN layer(s) on all {batch.B} sequences (verify and commit)')
+    att = [l for l in layers if l['kind'] == 'attn']
+    t_att, t_att_sample, seqs = 0.0, 0.0, []
+    if att:
+        a = att[0]
+        for b in range(batch.B):
+            pages = table[b][table[b] >= 0]
+            idx = torch.from_numpy(pages).to(a['k_cache'].device)
+            kc, vc = f64(a['k_cache'][idx]), f64(a['v_cache'][idx])
+            sub_t = np.arange(len(pages))[None, :]
+            rows = slice(cu[b], cu[b + 1])
+            q, kn, vn = f64(a['q'][rows]), f64(a['k_new'][rows]), f64(a['v_new'][rows])
+            t0 = time.perf_counter()
+            oracle.verify_attention(q, kn, vn, kc, vc, sub_t, ctx[b:b + 1],
+                                    np.array([0, cu[b + 1] - cu[b]]), batch.P)
+            oracle.append_kv(kc, vc, kn, vn, sub_t, ctx[b:b + 1],
+                             np.array([0, cu[b + 1] - cu[b]]), batch.P)
+            t_att_sample += time.perf_counter() - t0
+            seqs.append(b)
+            if t_att_sample > 0.5 * budget:
+                break
+        t_att = t_att_sample * float(max(ctx.sum(), 1)) / float(max(ctx[seqs].sum(), 1))
+        parts.append(f'attention (verify + append) of one layer for {len(seqs)} of {batch.B} '
+                     'sequences, scaled by context length')
+    n_att = len(att)
+    n_gdn = len(gdn)
     t_step = n_att * t_att + n_gdn * t_gdn + t_acc
     return {
         'value': draft_tokens_per_step / t_step, 'unit': 'verified draft tokens/s',
         'cores': int(threads), 'kind': 'oracle',
-        'sample': (f'{n_gdn_done} GDN layer(s) on all {batch.B} sequences, attention of one '
-                   f'layer for {len(seqs)} of {batch.B} sequences (scaled by context length), '
-                   f'{mode} acceptance on all rows; per-layer times scaled to {n_gdn} GDN + '
-                   f'{n_att} attention layers per step'),
+        'sample': '; '.join(parts) + f'; per-layer times scaled to {n_gdn} GDN + {n_att} '
+                  'attention layers per step',
         'seconds_measured': round(t_gdn_sum + t_att_sample + t_acc, 2),
-        'seconds_per_step_extrapolated': round(t_step, 2),
-        'affinity_cpus': len(os.sched_getaffinity(0)),
+        'seconds_per_step_extrapolated': round(t_step, 3),
+        'nproc': os.cpu_count(), 'affinity_cpus': len(os.sched_getaffinity(0)),
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f'bench.py runs on one GPU only (asked for --gpus {args.gpus}): this '
-              'library has no multi-GPU path (the step shards by sequence: each GPU would run '
-              'this step on its own sequences, KV pool and state slots).',
-              file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
+def base_line(w, args, steps, warmup, value, ms_step, config):
+    import torch
+    return {
+        'metric': 'verified draft tokens/sec at 1 GPU + achieved HBM GB/s (% of MI355X peak)',
+        'value': round(value, 1), 'unit': 'verified draft tokens/s',
+        'n_gpus': 1, 'steps': steps, 'warmup': warmup, 'ms_per_step': round(ms_step, 4),
+        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None,
+        'dtype': 'bf16' if w.attn_dtype != torch.float32 else 'f32',
+        'data': 'synthetic (seeded; no model weights)', 'config': config,
+    }
+
+
+def graph_replay_ms(make_graphs, replay_plan, finish, stream, steps):
+    """Capture HIP graphs (make_graphs returns them after an eager lead-in),
+    replay them `steps` times per replay_plan(i), finish() (the flush), all
+    between HIP events; returns the per-replay times and the total / steps."""
+    import torch
+    graphs = make_graphs()
+    calls = [(lambda i=i: graphs[replay_plan(i)].replay()) for i in range(steps)]
+    calls.append(finish)
+    per, total = timed_calls(stream, calls)
+    return per[:steps], total / steps
+
+
+def run_step_workload(w, args, dev, ceil):
+    """Workloads with attention and GDN layers and acceptance: the step."""
     import torch
 
     import workloads as wl
     from block_draft_verification_spec_amd import binding as bd
-
-    dev = 'cuda'
-    torch.cuda.set_device(0)
-    w = wl.WORKLOADS[args.workload]
-    mode = args.accept
+    mode = args.accept if args.accept in w.accept_modes else w.accept_modes[-1]
     steps, warmup = args.steps, args.warmup
-    # room in every block table for the tokens all steps commit
-    batch = wl.make_batch(w, args.seed, dev, reserve=w.max_T * (steps + warmup + 2))
+    # room in every block table for the tokens all eager and graph steps commit
+    batch = wl.make_batch(w, args.seed, dev, reserve=w.max_T * (2 * (steps + warmup) + 8))
     layers = []
     for i, kind in enumerate(w.layers):
         if kind == 'attn':
@@ -443,16 +544,18 @@ def main():
     sched = bd.SV_SCHEDULE_DEFERRED if deferred else bd.SV_SCHEDULE_TWO_PHASE
     # pending tokens of the previous step: the same input buffers (their
     # values do not change the work), with the previous step's commit lengths
-    pend_arr = (bd.SvGdnLayer * len(gdn_layers))(*gdn_layers)
+    pend_arr = (bd.SvGdnLayer * max(1, len(gdn_layers)))(*gdn_layers)
+    pends = [bd.SvStepPending(sb, pend_arr, commits[j].data_ptr()) for j in range(2)]
     state = {'n': 0}
+
+    def step_call(out_j, pend_j):
+        bd.spec_verify_step(sb, step_args, ctx, result, commits[out_j], schedule=sched,
+                            pending=pends[pend_j] if pend_j is not None else None,
+                            workspace=ws, err=err)
 
     def one_step():
         i = state['n']
-        pend = None
-        if deferred and i > 0:
-            pend = bd.SvStepPending(sb, pend_arr, commits[(i - 1) % 2].data_ptr())
-        bd.spec_verify_step(sb, step_args, ctx, result, commits[i % 2], schedule=sched,
-                            pending=pend, workspace=ws, err=err)
+        step_call(i % 2, (i - 1) % 2 if deferred and i > 0 else None)
         state['n'] = i + 1
 
     def flush():
@@ -471,120 +574,319 @@ def main():
     assert int(err.item()) == 0, f'device error flag {int(err.item())}'
     print('[bench] warmup done', file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
+    ctx_start = ctx.clone()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        one_step()
-    flush()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    per, total = timed_calls(stream, [one_step] * steps + [flush])
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / steps
+    ms_step = total / steps
     assert int(err.item()) == 0, f'device error flag {int(err.item())}'
+    c_last = (ctx - ctx_start).double() / steps          # tokens committed per step
     accepted = result[:batch.B].double().mean().item()
     print(f'[bench] timed {steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / steps:.3f})',
           file=sys.stderr, flush=True)
+    # the contexts the timed steps attended at, averaged over the steps
+    ctx_mean = (ctx_start.double() + c_last * (steps - 1) / 2.0).tolist()
+
+    graph = None
+    if not args.no_graph:
+        def make_graphs():
+            # eager lead-in so the first graph has a pending commit to replay
+            one_step()
+            torch.cuda.synchronize()
+            gs = []
+            pairs = [(1, 0), (0, 1)] if deferred else [(0, None)]
+            for out_j, pend_j in pairs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, capture_error_mode='thread_local'):
+                    step_call(out_j, pend_j)
+                gs.append(g)
+            return gs
+
+        def finish():
+            state['n'] = steps + 1      # the last replay wrote commits[steps % 2]
+            flush()
+        gper, gms = graph_replay_ms(make_graphs, lambda i: i % (2 if deferred else 1),
+                                    finish, stream, steps)
+        assert int(err.item()) == 0, f'device error flag {int(err.item())}'
+        graph = {'ms_per_step': round(gms, 4), 'step_ms': percentiles(gper),
+                 'value': round((batch.total_T - batch.B) / (gms * 1e-3), 1),
+                 'how': 'the same step captured into HIP graphs (one per commit buffer) and '
+                        'replayed back to back, flush included'}
+        print(f'[bench] graph replay: {gms:.3f} ms/step', file=sys.stderr, flush=True)
 
     # ---- per-part timing and the dominant kernel's per-launch duration
     att_layers = [l for l in layers if l['kind'] == 'attn']
-    nbytes_a = bd.spec_verify_attention_workspace_bytes(
-        batch.B, batch.total_T, w.Hq, w.Hkv, w.D, batch.block_table.shape[1], batch.P, dt_a)
+    gdn_l = [l for l in layers if l['kind'] == 'gdn']
     ctx_fixed = ctx.clone()
-    # back to back over every attention layer, attn_reps times, between two
-    # events on the launch stream: the mean per launch (both kernels of a
-    # launch and the gap to the next launch)
     n_launch = 0
-    s0 = torch.cuda.Event(enable_timing=True)
-    s1 = torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
+    calls = []
     for _ in range(args.attn_reps):
         for l in att_layers:
-            bd.spec_verify_attention(sb, l['q'], l['k_new'], l['v_new'], l['k_cache'],
-                                     l['v_cache'], batch.block_table, ctx_fixed, l['out'],
-                                     workspace=ws, err=err)
-            n_launch += 1
-    s1.record(stream)
-    torch.cuda.synchronize()
-    att_ms_mean = s0.elapsed_time(s1) / n_launch
-    # attention bytes at the contexts the timed calls used
-    cur_ctx = ctx_fixed.tolist()
-    b_att = attn_bytes(w, wl.Batch(**{**batch.__dict__, 'ctx': cur_ctx}))
-    gdn_l = [l for l in layers if l['kind'] == 'gdn']
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for l in gdn_l:
-        bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_COMMIT, l['state'], l['q'], l['k'], l['v'],
-                             l['alpha'], l['beta'], commits[0], l['out'])
-    g1.record(stream)
-    torch.cuda.synchronize()
-    gdn_ms = g0.elapsed_time(g1) / max(1, len(gdn_l))
-
-    # acceptance alone (same logits, uniforms and workspace), back to back
+            calls.append(lambda l=l: bd.spec_verify_attention(
+                sb, l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
+                batch.block_table, ctx_fixed, l['out'], workspace=ws, err=err))
+    _, att_total = timed_calls(stream, calls)
+    n_launch = len(calls)
+    att_ms_mean = att_total / n_launch
+    b_att = attn_bytes(w, batch, ctx_fixed.tolist())
+    _, g_total = timed_calls(stream, [
+        (lambda l=l: bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_COMMIT, l['state'], l['q'],
+                                          l['k'], l['v'], l['alpha'], l['beta'], commits[0],
+                                          l['out'])) for l in gdn_l])
+    gdn_ms = g_total / max(1, len(gdn_l))
     acc_reps = 20
-    a0 = torch.cuda.Event(enable_timing=True)
-    a1 = torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(acc_reps):
-        bd.spec_accept(sb, amode, acc['target_logits'], acc['draft_tokens'], result,
-                       draft_logits=acc.get('draft_logits'), u_accept=acc.get('u_accept'),
-                       u_final=acc.get('u_final'), workspace=ws, err=err)
-    a1.record(stream)
-    torch.cuda.synchronize()
-    acc_ms = a0.elapsed_time(a1) / acc_reps
+    _, a_total = timed_calls(stream, [
+        (lambda: bd.spec_accept(sb, amode, acc['target_logits'], acc['draft_tokens'], result,
+                                draft_logits=acc.get('draft_logits'),
+                                u_accept=acc.get('u_accept'), u_final=acc.get('u_final'),
+                                workspace=ws, err=err))] * acc_reps)
+    acc_ms = a_total / acc_reps
 
-    conv = short_conv_timing(w, batch, sb, commits[0], stream, dev)
-    gdn_sd = gdn_state_dtype_timing(w, batch, sb, commits[0], stream, dev)
-    kv8 = attn_kv8_timing(w, batch, sb, ctx_fixed, ws, stream, dev)
-    ckpt = checkpoint_timing(w, batch, sb, commits[0], stream, dev)
+    next_rows = None
+    if w.name == 'hybrid_step_64l' and not args.no_next_rows:
+        next_rows = {'short_conv': short_conv_timing(w, batch, sb, commits[0], stream, dev),
+                     'gdn_state_dtype': gdn_state_dtype_timing(w, batch, sb, commits[0], stream,
+                                                               dev),
+                     'attention_int8_kv': attn_kv8_timing(w, batch, sb, ctx_fixed, ws, stream,
+                                                          dev),
+                     'checkpoint_commit': checkpoint_timing(w, batch, sb, commits[0], stream,
+                                                            dev)}
 
     T = batch.total_T
     n_att, n_gdn = len(att_layers), len(gdn_l)
     draft_per_step = T - batch.B
-    ctx_mid = [c for c in cur_ctx]
-    b_step = (n_att * attn_bytes(w, wl.Batch(**{**batch.__dict__, 'ctx': ctx_mid}))
-              + n_gdn * gdn_bytes(w, batch) + accept_bytes(w, batch, mode))
+    b_step = (n_att * attn_bytes(w, batch, ctx_mean) + n_gdn * gdn_bytes(w, batch)
+              + accept_bytes(w, batch, mode))
+    pc = percentiles(per[:steps])
     gbs = b_step / (ms_step * 1e-3) / 1e9
+    gbs_med = b_step / (pc['median'] * 1e-3) / 1e9
     achieved = b_att / (att_ms_mean * 1e-3) / 1e9
-
-    line = {
-        'metric': 'verified draft tokens/sec at 1 GPU + achieved HBM GB/s (% of MI355X peak)',
-        'value': round(draft_per_step / (ms_step * 1e-3), 1),
-        'unit': 'verified draft tokens/s',
-        'n_gpus': 1, 'steps': steps, 'warmup': warmup,
-        'ms_per_step': round(ms_step, 4),
-        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None,
-        'dtype': 'bf16',
-        'data': 'synthetic (seeded; no model weights)',
-        'config': {'workload': w.name, 'layers': f'{n_gdn} GDN + {n_att} attention',
-                   'batch': batch.B, 'drafts_per_seq': w.k, 'ctx': list(w.ctx),
-                   'Hq_Hkv_D': [w.Hq, w.Hkv, w.D], 'page': batch.P,
-                   'gdn_H_dk_dv': [w.H, w.dk, w.dv], 'vocab': w.V, 'accept': mode,
-                   'schedule': args.schedule},
-        'step_hbm': {'algorithmic_bytes': b_step, 'GBps': round(gbs, 1),
-                     'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4)},
-        'roofline': {'kernel': 'spec_verify_attention, one layer '
-                               '(attn_stream_bf16 + attn_combine_bf16 launches)',
+    line = base_line(w, args, steps, warmup, draft_per_step / (ms_step * 1e-3), ms_step, {
+        'workload': w.name, 'layers': f'{n_gdn} GDN + {n_att} attention',
+        'batch': batch.B, 'drafts_per_seq': f'U{{1..{w.k}}}' if w.ragged_k else w.k,
+        'ctx': list(w.ctx), 'Hq_Hkv_D': [w.Hq, w.Hkv, w.D], 'page': batch.P,
+        'gdn_H_dk_dv': [w.H, w.dk, w.dv], 'vocab': w.V, 'accept': mode,
+        'schedule': args.schedule})
+    line.update({
+        'step_ms': pc,
+        'graph': graph,
+        'step_hbm': {'algorithmic_bytes': int(b_step), 'GBps': round(gbs, 1),
+                     'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4),
+                     'GBps_at_median': round(gbs_med, 1),
+                     'frac_of_measured_read': round(gbs / ceil['read_GBps'], 4),
+                     'contexts': 'mean over the timed steps'},
+        'ceilings': ceil,
+        'roofline': {'kernel': ('spec_verify_attention, one layer (attn_stream_bf16 + '
+                                'attn_combine_bf16 launches)' if dt_a == bd.SV_BF16 else
+                                'spec_verify_attention, one layer (attn_f32)'),
                      'bound': 'hbm', 'achieved': round(achieved, 1), 'peak': HBM_PEAK_GBS,
                      'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
-                     'traffic': measured_traffic(), 'traffic_unit': 'HBM bytes per launch',
-                     'bytes_per_launch': b_att,
+                     'frac_of_measured_read': round(achieved / ceil['read_GBps'], 4),
+                     'traffic': measured_traffic() if w.name == 'hybrid_step_64l' else None,
+                     'traffic_unit': 'HBM bytes per launch', 'bytes_per_launch': b_att,
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4),
                      'acceptance': round(acc_ms, 4)},
-        'next_rows': {'short_conv': conv, 'gdn_state_dtype': gdn_sd, 'attention_int8_kv': kv8,
-                      'checkpoint_commit': ckpt},
+        'next_rows': next_rows,
         'mean_accept_len': round(accepted, 3),
-        'dtype_detail': 'bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance',
-    }
+        'dtype_detail': ('bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance'
+                         if dt_a == bd.SV_BF16 else
+                         'fp32 I/O and accumulation, fp32 GDN state, fp64 acceptance'),
+    })
     if not args.no_cpu_baseline:
         print('[bench] timing the CPU oracle on a bounded sample', file=sys.stderr, flush=True)
         line['cpu_baseline'] = cpu_baseline(w, batch, layers, acc, mode, draft_per_step,
                                            args.cpu_budget)
+    return line
+
+
+def rotation_sets(nbytes_per_set, min_total=1 << 30, min_sets=4):
+    return max(min_sets, -(-min_total // nbytes_per_set))
+
+
+def run_attention_workload(w, args, dev, ceil):
+    """Paged verification attention alone: a step is one spec_verify_attention
+    call over the batch (KV write-through included), rotating over
+    independent buffer sets (pools, q, k_new, v_new) of >= 1 GB in total."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    steps, warmup = args.steps, args.warmup
+    batch = wl.make_batch(w, args.seed, dev)
+    b_call = attn_bytes(w, batch)
+    n_sets = rotation_sets(b_call)
+    sets = []
+    for i in range(n_sets):
+        lay = wl.make_attn_layer(w, batch, 1000 + i, dev)
+        lay['out'] = torch.empty_like(lay['q'])
+        sets.append(lay)
+    sb = bd.make_batch(batch.cu_seqlens, batch.B, batch.max_T, batch.total_T)
+    ws = torch.zeros(max(1, bd.spec_verify_attention_workspace_bytes(
+        batch.B, batch.total_T, w.Hq, w.Hkv, w.D, batch.block_table.shape[1], batch.P,
+        bd.SV_BF16)), dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print(f'[bench] inputs ready: {w.name}, {n_sets} buffer sets of {b_call / 1e6:.0f} MB',
+          file=sys.stderr, flush=True)
+
+    def call(i):
+        l = sets[i % n_sets]
+        bd.spec_verify_attention(sb, l['q'], l['k_new'], l['v_new'], l['k_cache'],
+                                 l['v_cache'], batch.block_table, batch.ctx_lens, l['out'],
+                                 workspace=ws, err=err)
+    for i in range(warmup):
+        call(i)
+    stream = torch.cuda.current_stream()
+    per, total = timed_calls(stream, [(lambda i=i: call(i)) for i in range(steps)])
+    ms = total / steps
+    assert int(err.item()) == 0
+    graph = None
+    if not args.no_graph:
+        def make_graphs():
+            gs = []
+            for i in range(n_sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, capture_error_mode='thread_local'):
+                    call(i)
+                gs.append(g)
+            return gs
+        gper, gms = graph_replay_ms(make_graphs, lambda i: i % n_sets, lambda: None, stream,
+                                    steps)
+        graph = {'ms_per_step': round(gms, 4), 'step_ms': percentiles(gper),
+                 'how': 'each buffer set\'s call captured into a HIP graph, replayed in turn'}
+    draft = batch.total_T - batch.B
+    pc = percentiles(per)
+    gbs = b_call / (ms * 1e-3) / 1e9
+    line = base_line(w, args, steps, warmup, draft / (ms * 1e-3), ms, {
+        'workload': w.name, 'layers': '1 attention (the call alone)', 'batch': batch.B,
+        'drafts_per_seq': w.k, 'ctx': list(w.ctx), 'Hq_Hkv_D': [w.Hq, w.Hkv, w.D],
+        'page': batch.P, 'buffer_sets': n_sets,
+        'rotation_bytes': int(n_sets * b_call)})
+    line.update({
+        'step_ms': pc, 'graph': graph,
+        'step_hbm': {'algorithmic_bytes': int(b_call), 'GBps': round(gbs, 1),
+                     'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4),
+                     'GBps_at_median': round(b_call / (pc['median'] * 1e-3) / 1e9, 1),
+                     'frac_of_measured_read': round(gbs / ceil['read_GBps'], 4)},
+        'ceilings': ceil,
+        'roofline': {'kernel': 'spec_verify_attention (attn_stream_bf16 + attn_combine_bf16)',
+                     'bound': 'hbm', 'achieved': round(gbs, 1), 'peak': HBM_PEAK_GBS,
+                     'unit': 'GB/s', 'frac': round(gbs / HBM_PEAK_GBS, 4),
+                     'frac_of_measured_read': round(gbs / ceil['read_GBps'], 4),
+                     'traffic': None, 'bytes_per_launch': int(b_call),
+                     'launch_ms': round(ms, 4), 'launches': steps},
+    })
+    if not args.no_cpu_baseline:
+        line['cpu_baseline'] = cpu_baseline(w, batch, [dict(sets[0], kind='attn')], None, None,
+                                           draft, args.cpu_budget)
+    return line
+
+
+def run_gdn_workload(w, args, dev, ceil):
+    """GDN verify + commit alone: a step is one gdn_verify_commit call
+    (VERIFY_COMMIT, commit lengths from the 70 % keep recipe), rotating over
+    independent buffer sets (state bank, q, k, v, gates) of >= 1 GB."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    steps, warmup = args.steps, args.warmup
+    batch = wl.make_batch(w, args.seed, dev)
+    commit = wl.make_commit_len(batch, args.seed + 1, device=dev)
+    b_call = gdn_bytes(w, batch)
+    n_sets = rotation_sets(b_call)
+    sets = []
+    for i in range(n_sets):
+        g = wl.make_gdn_layer(w, batch, 1000 + i, dev)
+        g['out'] = torch.empty_like(g['v'])
+        sets.append(g)
+    sb = bd.make_batch(batch.cu_seqlens, batch.B, batch.max_T, batch.total_T)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print(f'[bench] inputs ready: {w.name}, {n_sets} buffer sets of {b_call / 1e6:.0f} MB',
+          file=sys.stderr, flush=True)
+
+    def call(i):
+        g = sets[i % n_sets]
+        bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_COMMIT, g['state'], g['q'], g['k'], g['v'],
+                             g['alpha'], g['beta'], commit, g['out'], err=err)
+    for i in range(warmup):
+        call(i)
+    stream = torch.cuda.current_stream()
+    per, total = timed_calls(stream, [(lambda i=i: call(i)) for i in range(steps)])
+    ms = total / steps
+    assert int(err.item()) == 0
+    graph = None
+    if not args.no_graph:
+        def make_graphs():
+            gs = []
+            for i in range(n_sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, capture_error_mode='thread_local'):
+                    call(i)
+                gs.append(g)
+            return gs
+        gper, gms = graph_replay_ms(make_graphs, lambda i: i % n_sets, lambda: None, stream,
+                                    steps)
+        graph = {'ms_per_step': round(gms, 4), 'step_ms': percentiles(gper),
+                 'how': 'each buffer set\'s call captured into a HIP graph, replayed in turn'}
+    draft = batch.total_T - batch.B
+    pc = percentiles(per)
+    gbs = b_call / (ms * 1e-3) / 1e9
+    line = base_line(w, args, steps, warmup, draft / (ms * 1e-3), ms, {
+        'workload': w.name, 'layers': '1 GDN (the call alone, VERIFY_COMMIT)',
+        'batch': batch.B, 'drafts_per_seq': w.k, 'gdn_H_dk_dv': [w.H, w.dk, w.dv],
+        'state': 'fp32', 'buffer_sets': n_sets, 'rotation_bytes': int(n_sets * b_call)})
+    line.update({
+        'step_ms': pc, 'graph': graph,
+        'step_hbm': {'algorithmic_bytes': int(b_call), 'GBps': round(gbs, 1),
+                     'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4),
+                     'GBps_at_median': round(b_call / (pc['median'] * 1e-3) / 1e9, 1),
+                     'frac_of_measured_copy': round(gbs / ceil['copy_GBps'], 4)},
+        'ceilings': ceil,
+        'roofline': {'kernel': 'gdn_verify_commit (gdn_kernel)', 'bound': 'hbm',
+                     'achieved': round(gbs, 1), 'peak': HBM_PEAK_GBS, 'unit': 'GB/s',
+                     'frac': round(gbs / HBM_PEAK_GBS, 4),
+                     'frac_of_measured_copy': round(gbs / ceil['copy_GBps'], 4),
+                     'traffic': None, 'bytes_per_launch': int(b_call),
+                     'launch_ms': round(ms, 4), 'launches': steps},
+    })
+    if not args.no_cpu_baseline:
+        line['cpu_baseline'] = cpu_baseline(w, batch, [dict(sets[0], kind='gdn')], None, None,
+                                           draft, args.cpu_budget, commit=commit)
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f'bench.py runs on one GPU only (asked for --gpus {args.gpus}): this '
+              'library has no multi-GPU path (the step shards by sequence: each GPU would run '
+              'this step on its own sequences, KV pool and state slots).',
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import torch
+
+    import workloads as wl
+
+    dev = 'cuda'
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    ceil = ceilings(dev)
+    print(f'[bench] ceilings: {ceil["copy_GBps"]} GB/s copy, {ceil["read_GBps"]} GB/s read',
+          file=sys.stderr, flush=True)
+    kinds = set(w.layers)
+    if kinds == {'attn'}:
+        line = run_attention_workload(w, args, dev, ceil)
+    elif kinds == {'gdn'}:
+        line = run_gdn_workload(w, args, dev, ceil)
+    else:
+        line = run_step_workload(w, args, dev, ceil)
     print(json.dumps(line), flush=True)
 
 
