@@ -504,7 +504,7 @@ def run_step_workload(w, args, dev, ceil):
     mode = args.accept if args.accept in w.accept_modes else w.accept_modes[-1]
     steps, warmup = args.steps, args.warmup
     # room in every block table for the tokens all eager and graph steps commit
-    batch = wl.make_batch(w, args.seed, dev, reserve=w.max_T * (2 * (steps + warmup) + 8))
+    batch = wl.make_batch(w, args.seed, dev, reserve=w.max_T * (3 * (steps + warmup) + 8))
     layers = []
     for i, kind in enumerate(w.layers):
         if kind == 'attn':
@@ -642,6 +642,13 @@ def run_step_workload(w, args, dev, ceil):
                                 workspace=ws, err=err))] * acc_reps)
     acc_ms = a_total / acc_reps
 
+    with_conv = None
+    if w.name == 'hybrid_step_64l' and not args.no_next_rows:
+        with_conv = step_with_conv_timing(w, batch, layers, acc, amode, sb, ws, ctx, err, steps,
+                                          warmup, stream, dev, sched, deferred)
+        print(f'[bench] step with short conv: {with_conv["ms_per_step"]:.3f} ms/step',
+              file=sys.stderr, flush=True)
+
     next_rows = None
     if w.name == 'hybrid_step_64l' and not args.no_next_rows:
         next_rows = {'short_conv': short_conv_timing(w, batch, sb, commits[0], stream, dev),
@@ -688,6 +695,7 @@ def run_step_workload(w, args, dev, ceil):
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4),
                      'acceptance': round(acc_ms, 4)},
+        'step_with_short_conv': with_conv,
         'next_rows': next_rows,
         'mean_accept_len': round(accepted, 3),
         'dtype_detail': ('bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance'
@@ -699,6 +707,85 @@ def run_step_workload(w, args, dev, ceil):
         line['cpu_baseline'] = cpu_baseline(w, batch, layers, acc, mode, draft_per_step,
                                            args.cpu_budget)
     return line
+
+
+def conv_bytes(w, batch, pend_rows):
+    """One short-conv layer: state read + write, inputs and outputs, the
+    replayed pending inputs, taps and bias."""
+    s, C, K, T, B = elem_size(w.gdn_dtype), w.conv_C, w.conv_K, batch.total_T, batch.B
+    return 2 * B * (K - 1) * C * s + 2 * T * C * s + pend_rows * C * s + C * K * 4 + C * 4
+
+
+def step_with_conv_timing(w, batch, layers, acc, amode, sb, ws, ctx, err, steps, warmup,
+                          stream, dev, sched, deferred):
+    """The same step with every GDN layer's short convolution (C = the q, k
+    and v features, K = 4, SiLU) run beside its GDN verify in one launch
+    (two-phase: committed in the batched commit launch), timed the same way."""
+    import torch
+
+    import workloads as wl
+    from block_draft_verification_spec_amd import binding as bd
+    convs = {}
+    g_layers = []
+    for i, l in enumerate(layers):
+        if l['kind'] == 'gdn':
+            c = wl.make_conv_layer(w, batch, 8000 + i, dev)
+            c['out'] = torch.empty_like(c['x'])
+            convs[i] = c
+            g_layers.append(bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'],
+                                         l['beta'], l['out'], conv=c))
+    dt = bd.SV_BF16 if w.attn_dtype == torch.bfloat16 else bd.SV_F32
+    args = bd.StepArgs(
+        [1 if l['kind'] == 'attn' else 0 for l in layers],
+        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table, dt),
+        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'])
+         for l in layers if l['kind'] == 'attn'],
+        bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt, conv_C=w.conv_C, conv_K=w.conv_K,
+                      conv_activation=bd.SV_ACT_SILU), g_layers,
+        bd.accept_args(amode, acc['target_logits'], acc['draft_tokens'],
+                       acc.get('draft_logits'), acc.get('u_accept'), acc.get('u_final')))
+    result = torch.empty(batch.B * (1 + batch.max_T), dtype=torch.int32, device=dev)
+    commits = [torch.zeros(batch.B, dtype=torch.int32, device=dev) for _ in range(2)]
+    arr = (bd.SvGdnLayer * len(g_layers))(*g_layers)
+    pends = [bd.SvStepPending(sb, arr, commits[j].data_ptr()) for j in range(2)]
+    st = {'n': 0}
+
+    def one_step():
+        i = st['n']
+        bd.spec_verify_step(sb, args, ctx, result, commits[i % 2], schedule=sched,
+                            pending=pends[(i - 1) % 2] if deferred and i > 0 else None,
+                            workspace=ws, err=err)
+        st['n'] = i + 1
+
+    def flush():
+        if deferred and st['n'] > 0:
+            last = commits[(st['n'] - 1) % 2]
+            for i, l in enumerate(layers):
+                if l['kind'] == 'gdn':
+                    bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, l['state'], l['q'], l['k'],
+                                         l['v'], l['alpha'], l['beta'], last, l['out'])
+                    c = convs[i]
+                    bd.short_conv_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, c['state'], c['x'],
+                                                c['weight'], c['bias'], last, c['out'],
+                                                activation=bd.SV_ACT_SILU)
+            st['n'] = 0
+
+    for _ in range(warmup):
+        one_step()
+    flush()
+    torch.cuda.synchronize()
+    per, total = timed_calls(stream, [one_step] * steps + [flush])
+    assert int(err.item()) == 0, f'device error flag {int(err.item())}'
+    ms = total / steps
+    pend_rows = int(commits[0].sum().item()) if deferred else 0
+    b_conv = len(convs) * conv_bytes(w, batch, pend_rows)
+    del convs
+    return {'ms_per_step': round(ms, 4), 'step_ms': percentiles(per[:steps]),
+            'value': round((batch.total_T - batch.B) / (ms * 1e-3), 1),
+            'conv_layers': len(g_layers), 'conv_C_K': [w.conv_C, w.conv_K],
+            'conv_bytes_per_step': int(b_conv),
+            'how': 'every GDN layer\'s short convolution in its GDN verify launch '
+                   '(deferred: pending inputs replayed), the flush included'}
 
 
 def rotation_sets(nbytes_per_set, min_total=1 << 30, min_sets=4):

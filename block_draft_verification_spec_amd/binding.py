@@ -20,6 +20,7 @@ SV_GDN_VERIFY_COMMIT, SV_GDN_VERIFY_ONLY, SV_GDN_COMMIT_ONLY = 0, 1, 2
 SV_ACCEPT_GREEDY, SV_ACCEPT_REJECTION = 0, 1
 SV_SCHEDULE_TWO_PHASE, SV_SCHEDULE_DEFERRED = 0, 1
 SV_KV_PLAIN, SV_KV_INT8 = 0, 1
+SV_ACT_NONE, SV_ACT_SILU = 0, 1
 SV_DERR = {1: 'PAGE', 2: 'CAPACITY', 4: 'SEQLEN', 8: 'COMMIT', 16: 'TOKEN',
            32: 'SLOT'}
 
@@ -49,7 +50,9 @@ class SvAttnLayer(ctypes.Structure):
 
 class SvGdnLayer(ctypes.Structure):
     _fields_ = [('state', _vp), ('q', _vp), ('k', _vp), ('v', _vp),
-                ('alpha', _vp), ('beta', _vp), ('out', _vp)]
+                ('alpha', _vp), ('beta', _vp), ('out', _vp),
+                ('conv_state', _vp), ('conv_x', _vp), ('conv_out', _vp),
+                ('conv_weight', _vp), ('conv_bias', _vp)]
 
 
 class SvAttnConfig(ctypes.Structure):
@@ -63,7 +66,8 @@ class SvAttnConfig(ctypes.Structure):
 class SvGdnConfig(ctypes.Structure):
     _fields_ = [('H', _c_i32), ('dk', _c_i32), ('dv', _c_i32),
                 ('num_slots', _c_i32), ('state_slot', _vp),
-                ('io_dtype', ctypes.c_int), ('state_dtype', ctypes.c_int)]
+                ('io_dtype', ctypes.c_int), ('state_dtype', ctypes.c_int),
+                ('conv_C', _c_i32), ('conv_K', _c_i32), ('conv_activation', _c_i32)]
 
 
 class SvAcceptArgs(ctypes.Structure):
@@ -299,10 +303,6 @@ def make_gdn_pending(batch, k, v, alpha, beta, commit_len):
                         _i32(commit_len, 'commit_len'))
 
 
-SV_ACT_NONE = 0
-SV_ACT_SILU = 1
-
-
 def short_conv_verify_commit(batch, mode, state, x, weight, bias, commit_len, out,
                              state_slot=None, activation=SV_ACT_NONE, pending=None, err=None,
                              stream=None):
@@ -452,9 +452,12 @@ def state_dtype(state):
     raise ValueError(f'state must be float32 or float16, not {state.dtype}')
 
 
-def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None, state_dtype=SV_F32):
+def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None, state_dtype=SV_F32,
+               conv_C=0, conv_K=0, conv_activation=SV_ACT_NONE):
+    """GDN layer shapes of the step; conv_C > 0 runs every GDN layer's short
+    convolution (width conv_K) in the step too."""
     return SvGdnConfig(H, dk, dv, num_slots, _i32(state_slot, 'state_slot'), io_dtype,
-                       state_dtype)
+                       state_dtype, int(conv_C), int(conv_K), int(conv_activation))
 
 
 def attn_layer(q, k_new, v_new, k_cache, v_cache, out, k_scale=None, v_scale=None):
@@ -462,9 +465,17 @@ def attn_layer(q, k_new, v_new, k_cache, v_cache, out, k_scale=None, v_scale=Non
                        _ptr(v_cache), _ptr(out), _ptr(k_scale), _ptr(v_scale))
 
 
-def gdn_layer(state, q, k, v, alpha, beta, out):
+def gdn_layer(state, q, k, v, alpha, beta, out, conv=None):
+    """One GDN layer of the step; conv: None, or a dict with the layer's short
+    convolution tensors 'state', 'x', 'out', 'weight', 'bias' (bias may be
+    None)."""
+    c = conv or {}
+    if c and (c['weight'].dtype != torch.float32 or
+              (c.get('bias') is not None and c['bias'].dtype != torch.float32)):
+        raise ValueError('conv weight and bias must be float32')
     return SvGdnLayer(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                      _ptr(beta), _ptr(out))
+                      _ptr(beta), _ptr(out), _ptr(c.get('state')), _ptr(c.get('x')),
+                      _ptr(c.get('out')), _ptr(c.get('weight')), _ptr(c.get('bias')))
 
 
 def accept_args(mode, target_logits, draft_tokens, draft_logits=None,

@@ -520,6 +520,39 @@ sv_status check_conv_common(const sv_batch* batch, const void* state, const int3
   return SV_OK;
 }
 
+// The short convolution of a GDN layer inside the step.
+sv_status check_step_conv(const sv_batch* batch, const sv_gdn_config* g, const sv_gdn_layer& L,
+                          const sv_gdn_layer* P, const char* who) {
+  if (g->conv_C < 1) return SV_OK;
+  if (g->conv_K < 2 || g->conv_K > 8)
+    return fail(SV_EINVAL, "%s: conv_K must be in 2..8 (got %d)", who, g->conv_K);
+  if (g->conv_activation != SV_ACT_NONE && g->conv_activation != SV_ACT_SILU)
+    return fail(SV_EINVAL, "%s: unknown conv activation %d", who, g->conv_activation);
+  if (!L.conv_state || !L.conv_x || !L.conv_out || !L.conv_weight)
+    return fail(SV_EINVAL, "%s: conv_state, conv_x, conv_out and conv_weight are required", who);
+  if (P && !P->conv_x) return fail(SV_EINVAL, "%s: the pending conv_x is required", who);
+  (void)batch;
+  return SV_OK;
+}
+
+sv::ConvArgs step_conv_args(const sv_batch* batch, const sv_gdn_config* g, int mode,
+                            const int32_t* commit_len, int32_t* err) {
+  sv::ConvArgs a{};
+  a.B = batch->B;
+  a.total_T = batch->total_T;
+  a.max_T = batch->max_T;
+  a.cu = batch->cu_seqlens;
+  a.mode = mode;
+  a.state_slot = g->state_slot;
+  a.num_slots = g->num_slots;
+  a.commit_len = commit_len;
+  a.C = g->conv_C;
+  a.K = g->conv_K;
+  a.activation = g->conv_activation;
+  a.err = err;
+  return a;
+}
+
 }  // namespace
 
 sv_status gdn_verify_checkpoint(const sv_batch* batch, const void* state, sv_dtype state_dtype,
@@ -772,6 +805,9 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
                             gcfg->state_slot, gcfg->num_slots, G.q, G.k, G.v, gcfg->io_dtype,
                             G.alpha, G.beta, nullptr, G.out, gcfg->H, gcfg->dk, gcfg->dv,
                             pending ? &pg : nullptr, what);
+        if (st == SV_OK)
+          st = check_step_conv(batch, gcfg, G, pending ? &pending->layers[ig - 1] : nullptr,
+                               what);
       }
       if (st != SV_OK) return st;
     }
@@ -811,11 +847,61 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
         pg.commit_len = pending->commit_len;
         pp = &pg;
       }
-      ++ig;
-      st = gdn_verify_commit(batch, SV_GDN_VERIFY_ONLY, G.state, gcfg->state_dtype,
-                             gcfg->state_slot,
-                             gcfg->num_slots, G.q, G.k, G.v, gcfg->io_dtype, G.alpha, G.beta,
-                             nullptr, G.out, gcfg->H, gcfg->dk, gcfg->dv, pp, err, stream);
+      if (gcfg->conv_C > 0) {
+        // the layer's GDN verify and its short convolution in one launch
+        sv::GdnScalars s{};
+        s.B = batch->B;
+        s.total_T = batch->total_T;
+        s.max_T = batch->max_T;
+        s.cu = batch->cu_seqlens;
+        s.mode = SV_GDN_VERIFY_ONLY;
+        s.state_slot = gcfg->state_slot;
+        s.num_slots = gcfg->num_slots;
+        s.H = gcfg->H;
+        s.dk = gcfg->dk;
+        s.dv = gcfg->dv;
+        s.err = err;
+        sv::GdnFullPtrs p{};
+        p.state = G.state;
+        p.q = G.q;
+        p.k = G.k;
+        p.v = G.v;
+        p.alpha = G.alpha;
+        p.beta = G.beta;
+        p.out = G.out;
+        sv::ConvArgs c = step_conv_args(batch, gcfg, SV_GDN_VERIFY_ONLY, nullptr, err);
+        c.state = G.conv_state;
+        c.x = G.conv_x;
+        c.weight = G.conv_weight;
+        c.bias = G.conv_bias;
+        c.out = G.conv_out;
+        if (pending) {
+          s.has_pending = 1;
+          s.p_total_T = pending->batch.total_T;
+          s.p_max_T = pending->batch.max_T;
+          s.p_cu = pending->batch.cu_seqlens;
+          s.p_commit = pending->commit_len;
+          p.pk = pg.k;
+          p.pv = pg.v;
+          p.palpha = pg.alpha;
+          p.pbeta = pg.beta;
+          c.has_pending = 1;
+          c.p_total_T = pending->batch.total_T;
+          c.p_max_T = pending->batch.max_T;
+          c.p_cu = pending->batch.cu_seqlens;
+          c.p_commit = pending->commit_len;
+          c.px = pending->layers[ig].conv_x;
+        }
+        st = hip_status(sv::launch_gdn_conv(s, p, c, gcfg->io_dtype, gcfg->state_dtype, stream),
+                        who);
+        ++ig;
+      } else {
+        ++ig;
+        st = gdn_verify_commit(batch, SV_GDN_VERIFY_ONLY, G.state, gcfg->state_dtype,
+                               gcfg->state_slot, gcfg->num_slots, G.q, G.k, G.v,
+                               gcfg->io_dtype, G.alpha, G.beta, nullptr, G.out, gcfg->H,
+                               gcfg->dk, gcfg->dv, pp, err, stream);
+      }
     }
     if (st != SV_OK) return st;
   }
@@ -849,9 +935,12 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
         if (!G.state || !G.k || !G.v || !G.alpha || !G.beta)
           return fail(SV_EINVAL, "%s: GDN layer %d lacks state/k/v/alpha/beta", who, l0 + i);
         t.l[i] = sv::GdnCommitPtrs{G.state, G.k, G.v, G.alpha, G.beta};
+        t.c[i] = sv::ConvCommitPtrs{G.conv_state, G.conv_x};
       }
-      st = hip_status(
-          sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, gcfg->state_dtype, stream), who);
+      const sv::ConvArgs c = step_conv_args(batch, gcfg, SV_GDN_COMMIT_ONLY, commit_len, err);
+      st = hip_status(sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, gcfg->state_dtype,
+                                                  stream, gcfg->conv_C > 0 ? &c : nullptr),
+                      who);
       if (st != SV_OK) return st;
     }
   }

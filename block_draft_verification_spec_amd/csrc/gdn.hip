@@ -32,6 +32,7 @@
 // stored state is g S' and storing never changes the registers, so outputs
 // do not depend on where (or whether) the state is stored.
 
+#include "conv_block.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -473,17 +474,60 @@ __global__ __launch_bounds__(256) void gdn_commit_prefix_kernel(GdnScalars s, co
   for (size_t i = tid; i < n16; i += 256) dst[i] = src[i];
 }
 
-template <typename IO, typename ST, int DK>
-__global__ __launch_bounds__(kThreads) void gdn_commit_multi_kernel(GdnScalars s,
-                                                                    GdnCommitTable t) {
-  const int rb = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z % s.B;
-  const int layer = blockIdx.z / s.B;
+// The batched two-phase commit: one block per (64-row block, head,
+// sequence, layer), the row block fastest; with CONV, the layers' short
+// convolutions follow as blocks of 256 channels per (sequence, layer).
+template <typename IO, typename ST, int DK, bool CONV>
+__global__ __launch_bounds__(kThreads) void gdn_commit_multi_kernel(GdnScalars s, GdnCommitTable t,
+                                                                    ConvArgs c, int n_gdn_blocks) {
+  const int blk = blockIdx.x;
+  if (CONV && blk >= n_gdn_blocks) {
+    const int ncb = (c.C + kConvThreads - 1) / kConvThreads;
+    const int r = blk - n_gdn_blocks;
+    const int cblk = r % ncb, b = (r / ncb) % c.B, layer = r / (ncb * c.B);
+    ConvArgs cl = c;
+    cl.state = t.c[layer].state;
+    cl.x = t.c[layer].x;
+    conv_block_any<IO>(cl, b, cblk);
+    return;
+  }
+  const int nrb = s.dv / kRowsPerBlock;
+  const int rb = blk % nrb, h = (blk / nrb) % s.H;
+  const int z = blk / (nrb * s.H);
+  const int b = z % s.B, layer = z / s.B;
   const GdnCommitPtrs& p = t.l[layer];
   __shared__ GdnSmem<DK> sm;
   gdn_tile<IO, ST, DK, true>(sm, s, p.state, p.k, p.k, p.v, p.alpha, p.beta, p.state,
                          p.k, p.v, p.alpha, p.beta, b, h, rb,
                    rb == 0 && h == 0 && layer == 0);
+}
+
+// A layer's GDN verify / commit and its short convolution in one launch.  The
+// conv's blocks (256 channels of one sequence each: a few dependent memory
+// round trips, little traffic) are spread evenly among the GDN's (row block
+// fastest, as in gdn_kernel; bound by the state traffic), so their latency
+// overlaps the GDN's streaming instead of trailing it: block i is the conv
+// block floor(i Nc / N) when floor((i + 1) Nc / N) moves past it.
+template <typename IO, typename ST, int DK>
+__global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GdnScalars s, GdnFullPtrs p,
+                                                            ConvArgs c, int n_gdn_blocks) {
+  const int ncb = (c.C + kConvThreads - 1) / kConvThreads;
+  const long long n_conv = static_cast<long long>(ncb) * c.B;
+  const long long n_all = n_conv + n_gdn_blocks;
+  const long long i = blockIdx.x;
+  const int c_lo = static_cast<int>(i * n_conv / n_all);
+  const int c_hi = static_cast<int>((i + 1) * n_conv / n_all);
+  if (c_hi > c_lo) {
+    conv_block_any<IO>(c, c_lo / ncb, c_lo % ncb);
+    return;
+  }
+  const int blk = static_cast<int>(i) - c_lo;  // GDN blocks before this one
+  __shared__ GdnSmem<DK> sm;
+  const int nrb = s.dv / kRowsPerBlock;
+  const int rb = blk % nrb, h = (blk / nrb) % s.H, b = blk / (nrb * s.H);
+  gdn_tile<IO, ST, DK, false, false>(sm, s, p.state, p.q, p.k, p.v, p.alpha, p.beta, p.out,
+                                     p.pk, p.pv, p.palpha, p.pbeta, b, h, rb,
+                                     rb == 0 && h == 0);
 }
 
 template <typename IO, typename ST>
@@ -502,16 +546,51 @@ void launch_gdn_t(const GdnScalars& s, const GdnFullPtrs& p, hipStream_t stream)
   }
 }
 
+// kernel arguments of the batched commit stay within the 4 KiB argument block
+static_assert(sizeof(GdnScalars) + sizeof(GdnCommitTable) + sizeof(ConvArgs) + sizeof(int) + 64 <=
+                  4096,
+              "batched commit arguments exceed 4 KiB");
+
 template <typename IO, typename ST>
 void launch_commit_t(const GdnScalars& s, const GdnCommitTable& t, int n_layers,
-                     hipStream_t stream) {
-  const dim3 grid(s.dv / kRowsPerBlock, s.H, s.B * n_layers);
+                     hipStream_t stream, const ConvArgs* conv) {
+  const int n_gdn = (s.dv / kRowsPerBlock) * s.H * s.B * n_layers;
+  ConvArgs c{};
+  int n_conv = 0;
+  if (conv) {
+    c = *conv;
+    n_conv = (c.C + kConvThreads - 1) / kConvThreads * c.B * n_layers;
+  }
+  const dim3 grid(n_gdn + n_conv);
+  if (conv) {
+    if (s.dk == 128)
+      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128, true>), grid, dim3(kThreads), 0,
+                         stream, s, t, c, n_gdn);
+    else
+      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 64, true>), grid, dim3(kThreads), 0,
+                         stream, s, t, c, n_gdn);
+  } else {
+    if (s.dk == 128)
+      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128, false>), grid, dim3(kThreads), 0,
+                         stream, s, t, c, n_gdn);
+    else
+      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 64, false>), grid, dim3(kThreads), 0,
+                         stream, s, t, c, n_gdn);
+  }
+}
+
+template <typename IO, typename ST>
+void launch_gdn_conv_t(const GdnScalars& s, const GdnFullPtrs& p, const ConvArgs& c,
+                       hipStream_t stream) {
+  const int n_gdn = (s.dv / kRowsPerBlock) * s.H * s.B;
+  const int n_conv = (c.C + kConvThreads - 1) / kConvThreads * c.B;
+  const dim3 grid(n_gdn + n_conv);
   if (s.dk == 128)
-    hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128>), grid, dim3(kThreads), 0, stream,
-                       s, t);
+    hipLaunchKernelGGL((gdn_conv_kernel<IO, ST, 128>), grid, dim3(kThreads), 0, stream, s, p, c,
+                       n_gdn);
   else
-    hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 64>), grid, dim3(kThreads), 0, stream,
-                       s, t);
+    hipLaunchKernelGGL((gdn_conv_kernel<IO, ST, 64>), grid, dim3(kThreads), 0, stream, s, p, c,
+                       n_gdn);
 }
 
 }  // namespace
@@ -531,14 +610,27 @@ hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io_dt,
 
 hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
                                    int n_layers, sv_dtype io_dt, sv_dtype state_dt,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const ConvArgs* conv) {
   const bool h = state_dt == SV_F16;
   if (io_dt == SV_BF16) {
-    if (h) launch_commit_t<bf16_t, _Float16>(s, t, n_layers, stream);
-    else launch_commit_t<bf16_t, float>(s, t, n_layers, stream);
+    if (h) launch_commit_t<bf16_t, _Float16>(s, t, n_layers, stream, conv);
+    else launch_commit_t<bf16_t, float>(s, t, n_layers, stream, conv);
   } else {
-    if (h) launch_commit_t<float, _Float16>(s, t, n_layers, stream);
-    else launch_commit_t<float, float>(s, t, n_layers, stream);
+    if (h) launch_commit_t<float, _Float16>(s, t, n_layers, stream, conv);
+    else launch_commit_t<float, float>(s, t, n_layers, stream, conv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_conv(const GdnScalars& s, const GdnFullPtrs& p, const ConvArgs& c,
+                           sv_dtype io_dt, sv_dtype state_dt, hipStream_t stream) {
+  const bool h = state_dt == SV_F16;
+  if (io_dt == SV_BF16) {
+    if (h) launch_gdn_conv_t<bf16_t, _Float16>(s, p, c, stream);
+    else launch_gdn_conv_t<bf16_t, float>(s, p, c, stream);
+  } else {
+    if (h) launch_gdn_conv_t<float, _Float16>(s, p, c, stream);
+    else launch_gdn_conv_t<float, float>(s, p, c, stream);
   }
   return hipGetLastError();
 }

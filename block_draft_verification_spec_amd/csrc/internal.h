@@ -70,8 +70,14 @@ struct GdnCommitPtrs {
   const float* alpha; const float* beta;
 };
 
+struct ConvCommitPtrs {
+  void* state;                  // [num_slots][K-1][C]
+  const void* x;                // [total_T][C]
+};
+
 struct GdnCommitTable {
   GdnCommitPtrs l[kGdnLayersPerLaunch];
+  ConvCommitPtrs c[kGdnLayersPerLaunch];  // used when the launch commits convs too
 };
 
 hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io,
@@ -79,10 +85,16 @@ hipError_t launch_gdn(const GdnScalars& s, const GdnFullPtrs& p, sv_dtype io,
 // CommitPrefix: state[slot_b] = ckpt[b][window - T_b + c_b - 1] where c_b >= 1.
 hipError_t launch_gdn_commit_prefix(const GdnScalars& s, const void* ckpt, void* state,
                                     sv_dtype state_dtype, hipStream_t stream);
-// COMMIT_ONLY over n_layers (<= kGdnLayersPerLaunch) layers in one launch.
+// COMMIT_ONLY over n_layers (<= kGdnLayersPerLaunch) layers in one launch;
+// with conv (its scalars; state and x per layer from t.c) the layers' short
+// convolutions are committed in the same launch.
 hipError_t launch_gdn_commit_multi(const GdnScalars& s, const GdnCommitTable& t,
                                    int n_layers, sv_dtype io, sv_dtype state_dtype,
-                                   hipStream_t stream);
+                                   hipStream_t stream, const ConvArgs* conv = nullptr);
+// The GDN verify / commit of a layer and its short convolution in one launch
+// (the conv's blocks after the GDN's; they share no data).
+hipError_t launch_gdn_conv(const GdnScalars& s, const GdnFullPtrs& p, const ConvArgs& conv,
+                           sv_dtype io, sv_dtype state_dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

@@ -370,12 +370,17 @@ SV_API sv_status short_conv_commit_prefix(const sv_batch* batch,
  *   1. every layer in model order: attention layers run
  *      spec_verify_attention (write_kv = 1), or spec_verify_attention_kv8
  *      when acfg->kv_format is SV_KV_INT8; GDN layers run their verify pass
- *      (deferred schedule: applying the pending tokens first and storing);
+ *      (deferred schedule: applying the pending tokens first and storing),
+ *      and, with gcfg->conv_C > 0, their short convolution's verify pass in
+ *      the same launch (the pages keep the two as separate operators, each
+ *      with its own state: the step takes both operators' inputs and
+ *      neither reads the other's output);
  *   2. spec_accept -> result, commit_len = accept_len + 1;
  *   3. two-phase schedule: one launch applies the first commit_len tokens of
- *      every GDN layer and stores the states (deferred schedule: nothing, the
- *      next step's verify pass does it; call gdn_verify_commit in
- *      COMMIT_ONLY mode on the pending tokens to flush);
+ *      every GDN layer (and its convolution) and stores the states (deferred
+ *      schedule: nothing, the next step's verify pass does it; call
+ *      gdn_verify_commit and short_conv_verify_commit in COMMIT_ONLY mode on
+ *      the pending tokens to flush);
  *   4. ctx_lens += commit_len.
  * Attention layers share block_table / ctx_lens; GDN layers share
  * state_slot.  `layer_kind` (host) holds 0 = GDN, 1 = attention, in model
@@ -395,6 +400,12 @@ typedef struct {
 typedef struct {
   void* state; const void* q; const void* k; const void* v;
   const float* alpha; const float* beta; void* out;
+  /* the layer's short convolution (used when sv_gdn_config.conv_C > 0; see
+   * short_conv_verify_commit): rolling state [num_slots, K-1, C] in the io
+   * dtype (updated in place, slots as for `state`), inputs conv_x and
+   * outputs conv_out [total_T, C], taps fp32 [C, K], bias fp32 [C] or NULL */
+  void* conv_state; const void* conv_x; void* conv_out;
+  const float* conv_weight; const float* conv_bias;
 } sv_gdn_layer;
 
 typedef struct {
@@ -410,13 +421,18 @@ typedef struct {
   const int32_t* state_slot;   /* [B] or NULL */
   sv_dtype io_dtype;
   sv_dtype state_dtype;        /* SV_F32 or SV_F16 */
+  /* the short convolution of every GDN layer: channels (0: none), width
+   * 2..8, activation SV_ACT_NONE / SV_ACT_SILU; its state and inputs use
+   * io_dtype and the GDN layers' state slots */
+  int32_t conv_C, conv_K, conv_activation;
 } sv_gdn_config;
 
 
 
 /* Pending tokens of every GDN layer for the deferred schedule (host struct;
- * `layers` is a host array of n_gdn entries whose k, v, alpha, beta point at
- * the previous step's inputs; q and out are unused). */
+ * `layers` is a host array of n_gdn entries whose k, v, alpha, beta (and
+ * conv_x) point at the previous step's inputs; the other pointers are
+ * unused). */
 typedef struct {
   sv_batch batch;
   const sv_gdn_layer* layers;

@@ -368,3 +368,122 @@ def test_refused_step_changes_nothing():
                 assert torch.equal(l[key], b0[key]) or (
                     key == 'out' and torch.isnan(l[key].float()).all()), key
     assert torch.equal(ctx, batch.ctx_lens)
+
+
+def _conv_step_args(w, batch, layers, convs, acc, mode, K, act):
+    """StepArgs whose GDN layers carry their short convolution."""
+    g_layers = []
+    gi = 0
+    for l in layers:
+        if l['kind'] == 'gdn':
+            g_layers.append(bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'],
+                                         l['beta'], l['out'], conv=convs[gi]))
+            gi += 1
+    return bd.StepArgs(
+        [1 if l['kind'] == 'attn' else 0 for l in layers],
+        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table,
+                       bd.SV_BF16),
+        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'])
+         for l in layers if l['kind'] == 'attn'],
+        bd.gdn_config(w.H, w.dk, w.dv, batch.B, bd.SV_BF16, conv_C=w.conv_C, conv_K=K,
+                      conv_activation=act), g_layers,
+        bd.accept_args(mode, acc['target_logits'], acc['draft_tokens'],
+                       acc.get('draft_logits'), acc.get('u_accept'), acc.get('u_final')))
+
+
+@pytest.mark.parametrize("K,act", [(4, bd.SV_ACT_SILU), (3, bd.SV_ACT_NONE)])
+@pytest.mark.parametrize("schedule", [bd.SV_SCHEDULE_TWO_PHASE, bd.SV_SCHEDULE_DEFERRED])
+def test_step_with_short_conv(schedule, K, act):
+    """Every GDN layer's short convolution inside the step (one launch with
+    the GDN verify; two-phase: committed in the batched commit launch;
+    deferred: the next step replays its pending inputs).  Two steps, then a
+    flush; conv outputs against oracle.conv_step (bf16 tolerance), committed
+    conv states bit for bit, GDN states, outputs and acceptance as usual."""
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1), 'conv_K': K, 'H': 4})
+    batch = wl.make_batch(w, 31, DEV, reserve=8)
+    mode = bd.SV_ACCEPT_REJECTION
+    layers, acc = make_step(w, batch, 32, 'rejection')
+    convs = []
+    for i in range(sum(1 for l in layers if l['kind'] == 'gdn')):
+        c = wl.make_conv_layer(w, batch, 3300 + i, DEV)
+        c['out'] = torch.full_like(c['x'], float('nan'))
+        convs.append(c)
+    init_state = [l['state'].clone() if l['kind'] == 'gdn' else None for l in layers]
+    init_conv = [c['state'].clone() for c in convs]
+    pools = [(l['k_cache'].clone(), l['v_cache'].clone()) if l['kind'] == 'attn' else None
+             for l in layers]
+    args = _conv_step_args(w, batch, layers, convs, acc, mode, K, act)
+    sb = sv_batch(batch)
+    ws = torch.zeros(bd.spec_verify_step_workspace_bytes(sb, args), dtype=torch.uint8,
+                     device=DEV)
+    ctx = batch.ctx_lens.clone()
+    err = err_word()
+    results = [torch.full((batch.B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
+               for _ in range(2)]
+    commits = [torch.full((batch.B,), -7, dtype=torch.int32, device=DEV) for _ in range(2)]
+    say('step with short conv, schedule', schedule, 'K', K)
+    bd.spec_verify_step(sb, args, ctx, results[0], commits[0], schedule=schedule,
+                        workspace=ws, err=err)
+    torch.cuda.synchronize()
+    conv_out1 = [c['out'].clone() for c in convs]
+    pend = None
+    pend_arr = (bd.SvGdnLayer * len(args.gdn))(*args.gdn)
+    if schedule == bd.SV_SCHEDULE_DEFERRED:
+        pend = bd.SvStepPending(sb, pend_arr, commits[0].data_ptr())
+    bd.spec_verify_step(sb, args, ctx, results[1], commits[1], schedule=schedule,
+                        pending=pend, workspace=ws, err=err)
+    if schedule == bd.SV_SCHEDULE_DEFERRED:     # flush the second step's tokens
+        gi = 0
+        for l in layers:
+            if l['kind'] == 'gdn':
+                bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, l['state'], l['q'], l['k'],
+                                     l['v'], l['alpha'], l['beta'], commits[1], l['out'])
+                c = convs[gi]
+                bd.short_conv_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, c['state'], c['x'],
+                                            c['weight'], c['bias'], commits[1], c['out'],
+                                            activation=act)
+                gi += 1
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    cu = npi(batch.cu_seqlens)
+    a_ref, o_ref = oracle.rejection_accept(np64(acc['target_logits']), np64(acc['draft_logits']),
+                                           npi(acc['draft_tokens']), np64(acc['u_accept']),
+                                           np64(acc['u_final']), cu, batch.max_T)
+    r = npi(results[0])
+    np.testing.assert_array_equal(r[:batch.B], a_ref)
+    np.testing.assert_array_equal(npi(commits[0]), a_ref + 1)
+    np.testing.assert_array_equal(npi(commits[1]), a_ref + 1)
+    c1 = a_ref + 1
+    silu = act == bd.SV_ACT_SILU
+    gi = 0
+    for i, l in enumerate(layers):
+        if l['kind'] != 'gdn':
+            continue
+        cv = convs[gi]
+        xs, wt, bs = np64(cv['x']), np64(cv['weight']), np64(cv['bias'])
+        y1, S1 = oracle.conv_step(np64(init_conv[gi]), None, xs, wt, bs, cu, c1,
+                                  oracle.CONV_VERIFY_COMMIT, silu=silu)
+        y2, S2 = oracle.conv_step(S1, None, xs, wt, bs, cu, c1, oracle.CONV_VERIFY_COMMIT,
+                                  silu=silu)
+        check_gdn_out(np64(conv_out1[gi]), y1, torch.bfloat16)
+        check_gdn_out(np64(cv['out']), y2, torch.bfloat16)
+        assert np.array_equal(bits(cv['state']), bits_of(S2, cv['state']))
+        # the GDN state beside it: two commits of c1 tokens
+        _, G1 = oracle.gdn_step(np64(init_state[i]), None, None, np64(l['k']), np64(l['v']),
+                                np64(l['alpha']), np64(l['beta']), cu, c1,
+                                oracle.GDN_COMMIT_ONLY)
+        _, G2 = oracle.gdn_step(G1, None, None, np64(l['k']), np64(l['v']), np64(l['alpha']),
+                                np64(l['beta']), cu, c1, oracle.GDN_COMMIT_ONLY)
+        check_gdn_state(np64(l['state']), G2)
+        gi += 1
+    for i, l in enumerate(layers):       # the attention layers are untouched by the conv
+        if l['kind'] == 'attn':
+            ref = oracle.verify_attention(np64(l['q']), np64(l['k_new']), np64(l['v_new']),
+                                          *oracle.append_kv(np64(pools[i][0]), np64(pools[i][1]),
+                                                            np64(l['k_new']), np64(l['v_new']),
+                                                            npi(batch.block_table),
+                                                            npi(batch.ctx_lens), cu, batch.P),
+                                          npi(batch.block_table), npi(batch.ctx_lens) + c1, cu,
+                                          batch.P)
+            check_attn_out(np64(l['out']), ref, torch.bfloat16)
