@@ -880,10 +880,11 @@ __global__ __launch_bounds__(256) void attn_append_kv8(AttnArgs a) {
 //   m = max_i m_i, l = sum_i e^(m_i - m) l_i, o = sum_i e^(m_i - m) O_i / l
 // --------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
-  const int h = blockIdx.x, j = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void attn_combine_bf16(AttnArgs a) {
+  // blocks (KV head, sequence, z) share the segment's M = G T_b query rows
+  // by 256-float4 slices, one float4 of one row per thread
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x + blockIdx.z * kThreads;
   const int G = a.Hq / a.Hkv;
-  const int g = h / G;
   const int s = b * a.Hkv + g;
   // the segment's piece record and the sequence bounds are fetched together,
   // with one wait before the first branch (the record is used only once the
@@ -894,7 +895,6 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   asm volatile("" : "+s"(wf), "+s"(wl_), "+s"(Units), "+s"(x0), "+s"(x1), "+s"(L));
   const int T = x1 - x0;
   if (!attn_seq_valid(a, x0, T, L, false)) return;
-  if (j >= T) return;
   if (wf >= wl_) return;  // one piece: written by the stream kernel
   // With few cost units some ranges [wg_unit(w), wg_unit(w + 1)) are empty
   // (never when every workgroup's share U w_r / S(W) is a unit or more); such
@@ -904,58 +904,56 @@ __global__ __launch_bounds__(64) void attn_combine_bf16(AttnArgs a) {
   // non-empty piece.
   const int W = a.n_wg, ncu = a.n_cu;
   const bool sparse = static_cast<long long>(Units) * round_w_min() < wg_weight(W, ncu);
-  auto empty = [&](int w) {
-    return sparse && wg_unit(w, W, ncu, Units) == wg_unit(w + 1, W, ncu, Units);
-  };
-  const int m = j * G + (h - g * G);
-  float acc[D / 64];
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  float ls = 0.f;
   constexpr int kFew = 4;  // pieces fetched at once (one round trip)
-  if (wl_ - wf < kFew) {
-    float pm[kFew], pl[kFew], po[kFew][D / 64];
-#pragma unroll
-    for (int i = 0; i < kFew; ++i) {
-      pm[i] = -INFINITY;
-      if (wf + i > wl_ || empty(wf + i)) continue;
-      const size_t pi = static_cast<size_t>(s + wf + i) * kMaxRows + m;
-      pm[i] = a.part_ml[2 * pi];
-      pl[i] = a.part_ml[2 * pi + 1];
-#pragma unroll
-      for (int e = 0; e < D / 64; ++e) po[i][e] = a.part_o[pi * D + lane + 64 * e];
-    }
-    float mm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kFew; ++i) mm = fmaxf(mm, pm[i]);
-#pragma unroll
-    for (int i = 0; i < kFew; ++i) {
-      if (pm[i] == -INFINITY) continue;
-      const float f = exp2f(pm[i] - mm);
-      ls += f * pl[i];
-#pragma unroll
-      for (int e = 0; e < D / 64; ++e) acc[e] += f * po[i][e];
-    }
-  } else {
-    float mm = -INFINITY;
-    for (int wg = wf; wg <= wl_; ++wg)
-      if (!empty(wg)) mm = fmaxf(mm, a.part_ml[2 * (static_cast<size_t>(s + wg) * kMaxRows + m)]);
-    for (int wg = wf; wg <= wl_; ++wg) {
-      if (empty(wg)) continue;
-      const size_t pi = static_cast<size_t>(s + wg) * kMaxRows + m;
-      const float ms = a.part_ml[2 * pi];
-      if (ms == -INFINITY) continue;
-      const float f = exp2f(ms - mm);
-      ls += f * a.part_ml[2 * pi + 1];
-#pragma unroll
-      for (int e = 0; e < D / 64; ++e) acc[e] += f * a.part_o[pi * D + lane + 64 * e];
-    }
+  int pws[kFew], np = 0;
+  for (int w = wf; w <= wl_; ++w) {
+    if (sparse && wg_unit(w, W, ncu, Units) == wg_unit(w + 1, W, ncu, Units)) continue;
+    if (np < kFew) pws[np] = w;
+    ++np;
   }
-  const size_t row = static_cast<size_t>(x0 + j) * a.Hq + h;
-  const float inv = 1.f / ls;
+  const int M = G * T;
+  for (int i = tid; i < M * (D / 4); i += kThreads * gridDim.z) {
+    const int m = i / (D / 4), d4 = (i - m * (D / 4)) * 4;
+    float mm = -INFINITY, ls = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](float pm, float pl, float4 po) __attribute__((always_inline)) {
+      if (pm == -INFINITY) return;
+      const float mn = fmaxf(mm, pm);
+      const float fo = mm == -INFINITY ? 0.f : exp2f(mm - mn), fp = exp2f(pm - mn);
+      ls = ls * fo + pl * fp;
+      acc = make_float4(acc.x * fo + po.x * fp, acc.y * fo + po.y * fp, acc.z * fo + po.z * fp,
+                        acc.w * fo + po.w * fp);
+      mm = mn;
+    };
+    if (np <= kFew) {
+      float2 ml[kFew];
+      float4 po[kFew];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e)
-    static_cast<uint16_t*>(a.out)[row * D + lane + 64 * e] = f32_to_bf16(acc[e] * inv);
+      for (int q = 0; q < kFew; ++q) {  // pieces past np re-read piece 0, unused
+        const size_t pi = static_cast<size_t>(s + pws[q < np ? q : 0]) * kMaxRows + m;
+        ml[q] = *reinterpret_cast<const float2*>(a.part_ml + 2 * pi);
+        po[q] = *reinterpret_cast<const float4*>(a.part_o + pi * D + d4);
+      }
+#pragma unroll
+      for (int q = 0; q < kFew; ++q)
+        if (q < np) add(ml[q].x, ml[q].y, po[q]);
+    } else {
+      for (int w = wf; w <= wl_; ++w) {
+        if (sparse && wg_unit(w, W, ncu, Units) == wg_unit(w + 1, W, ncu, Units)) continue;
+        const size_t pi = static_cast<size_t>(s + w) * kMaxRows + m;
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * pi);
+        add(ml.x, ml.y, *reinterpret_cast<const float4*>(a.part_o + pi * D + d4));
+      }
+    }
+    // row m -> (token m / G, head g G + m % G)
+    const int j = m / G, hh = m - j * G;
+    const size_t row = static_cast<size_t>(x0 + j) * a.Hq + g * G + hh;
+    const float inv = 1.f / ls;
+    uint2 pk;
+    pk.x = f32_to_bf16(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
+    pk.y = f32_to_bf16(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + d4) = pk;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -1160,6 +1158,13 @@ int attn_stream_grid(int D, int G, int max_T, bool kv8, int* n_cu) {
   return stream_grid(D, nqt_for(G, max_T), kv8, n_cu);
 }
 
+// Blocks of the combine per segment: one float4 of the segment's rows per
+// thread (G max_T rows of D / 4 float4s).
+int combine_z(const AttnArgs& a, int D) {
+  const int items = (a.Hq / a.Hkv) * a.max_T * (D / 4);
+  return (items + kThreads - 1) / kThreads;
+}
+
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype, hipStream_t stream) {
   if (dtype == SV_F32) {
     hipLaunchKernelGGL(attn_f32, dim3(a.Hq, a.max_T, a.B), dim3(64), 0, stream, a);
@@ -1183,9 +1188,11 @@ hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype, hipStream_t strea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.D == 128)
-    hipLaunchKernelGGL((attn_combine_bf16<128>), dim3(a.Hq, a.max_T, a.B), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((attn_combine_bf16<128>), dim3(a.Hkv, a.B, combine_z(a, 128)), dim3(kThreads),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((attn_combine_bf16<64>), dim3(a.Hq, a.max_T, a.B), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((attn_combine_bf16<64>), dim3(a.Hkv, a.B, combine_z(a, 64)), dim3(kThreads),
+                       0, stream, a);
   return hipGetLastError();
 }
 
