@@ -26,7 +26,9 @@
 // load, otherwise with coalesced stride-256 element loads, so any V and any
 // row alignment is supported.
 
+#include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "exp2_table.h"
@@ -68,14 +70,20 @@ constexpr int kPerThread = kChunk / kThreads;
 
 __host__ __device__ inline int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
+// Whether chunk `chunk` of a row reaches past V (only the row's last chunk
+// can): its entries past V are loaded from inside the row and must be masked.
+__device__ __forceinline__ bool chunk_has_tail(int chunk, int V) { return (chunk + 1) * kChunk > V; }
+
 // exp(x) for x <= 0 in fp64 for the per-entry work, by the table-driven
 // method of P. T. P. Tang (ACM TOMS 15(2), 1989): with k the integer nearest
 // to x * 256 / ln 2 and r = x - k ln2 / 256 (|r| <= ln2 / 512, taken in two
 // fma steps with ln 2 split into a double and its remainder),
 //   exp(x) = 2^(k >> 8) * 2^((k & 255) / 256) * (1 + p(r)),
-// p the degree-5 Taylor polynomial of exp(r) - 1 (remainder below 1e-20
-// relative).  Each block copies the 256 entries 2^(j/256) (correctly rounded
-// doubles, exp2_table.h) into LDS.
+// p the degree-4 Taylor polynomial of exp(r) - 1, whose remainder
+// r^5 / 120 stays below 3.8e-17 relative (a third of an ulp of 1; on 4e7
+// host-checked points of [-707, 0] the result is within 1.33 ulp of exp).
+// Each block copies the 256 entries 2^(j/256) (correctly rounded doubles,
+// exp2_table.h) into LDS.
 // Every step is a full-rate fp64 or integer operation: adding 1.5 * 2^52 to
 // x * 256 / ln 2 (in one fma) rounds it to the nearest integer, ties to even,
 // and leaves that integer in the low word of the sum; the power 2^(k >> 8)
@@ -88,22 +96,54 @@ __device__ __forceinline__ void exp_table_init(double* tab) {
   for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) tab[j] = kExp2Tab[j];
 }
 
-__device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
-  constexpr double kMin = -800.0;
+struct ExpReduced {
+  double pr;   // p(r)
+  uint32_t k;  // k, two's complement
+};
+
+__device__ __forceinline__ ExpReduced exp_reduce(double xc) {
   constexpr double kShift = 0x1.8p52;
   constexpr double kInvStep = 256.0 / 0.693147180559945309417232121458176568;
   constexpr double kStepHi = 0x1.62e42fefa39efp-1 / 256.0;   // ln 2 rounded to double, / 256
   constexpr double kStepLo = 2.319046813846299558e-17 / 256.0;  // ln 2 minus that double, / 256
-  const double xc = fmax(x, kMin);
   const double ks = fma(xc, kInvStep, kShift);
-  const int ki = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(ks)));
+  const uint32_t ki = static_cast<uint32_t>(__double_as_longlong(ks));
   const double k = ks - kShift;
   double r = fma(-k, kStepHi, xc);
   r = fma(-k, kStepLo, r);
-  const double pr =
-      r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0 + r * (1.0 / 120.0)))));
-  const double t = tab[ki & (kExpTab - 1)];
-  return ldexp(fma(t, pr, t), ki >> 8);
+  const double pr = r * fma(r, fma(r, fma(r, 1.0 / 24.0, 1.0 / 6.0), 0.5), 1.0);
+  return {pr, ki};
+}
+
+__device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
+  const ExpReduced e = exp_reduce(fmax(x, -800.0));
+  const double t = tab[e.k & (kExpTab - 1)];
+  return ldexp(fma(t, e.pr, t), static_cast<int>(e.k) >> 8);
+}
+
+// The variant for the row sums.  x is clamped to -707 instead, so every
+// result is a normal number and 2^(k >> 8) can go into the table entry's
+// exponent field by one integer add: the table (exp_table_init_biased) holds
+// 2^(j/256) with j << 12 taken off its high word, and adding k << 12 to that
+// word puts j's bits back and adds k >> 8 to the exponent (both exact in
+// arithmetic mod 2^32, since k << 12 = ((k >> 8) << 20) + ((k & 255) << 12)).
+// On [-707, 0] the result equals exp_nonpos bit for bit.  Below -707 (also
+// -inf) it is e^-707, about 9e-308 instead of a smaller value: a chunk sum
+// also holds the entry at the chunk's maximum, e^0 = 1, so these terms are
+// lost in its rounding.
+__device__ __forceinline__ void exp_table_init_biased(uint2* tab) {
+  for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) {
+    const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(kExp2Tab[j]));
+    tab[j] = make_uint2(static_cast<uint32_t>(b),
+                        static_cast<uint32_t>(b >> 32) - (static_cast<uint32_t>(j) << 12));
+  }
+}
+
+__device__ __forceinline__ double exp_nonpos_sum(double x, const uint2* tab_biased) {
+  const ExpReduced e = exp_reduce(fmax(x, -707.0));
+  const uint2 w = tab_biased[e.k & (kExpTab - 1)];
+  const double t = __hiloint2double(static_cast<int>(w.y + (e.k << 12)), static_cast<int>(w.x));
+  return fma(t, e.pr, t);
 }
 
 // Workspace layout (byte offsets are 256-aligned).
@@ -223,25 +263,47 @@ __device__ __forceinline__ int chunk_entry(int chunk, int tid, int e) {
   return chunk * kChunk + ((e / NV) * kThreads + tid) * NV + e % NV;
 }
 
-// A thread's kPerThread entries of one chunk of row `row`, every load issued
+// A thread's kPerThread entries of one chunk of row `row` as loaded (raw
+// bits, so that holding them in flight needs no wait), every load issued
 // before any is used; an entry past V reads a valid entry of the row and is
 // masked by the caller.
 template <typename T, bool VEC>
-__device__ __forceinline__ void load_chunk(const void* src, int row, int V, int chunk, int tid,
-                                           float* out) {
+struct ChunkRaw {
+  using S = typename io<T>::storage;
+  static constexpr int NV = VEC ? kVecN<T> : 1;
+  static constexpr int N = VEC ? kPerThread / NV : kPerThread;
+  using R = std::conditional_t<VEC, uint4, S>;
+  R raw[N];
+};
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_chunk_raw(const void* src, int row, int V, int chunk, int tid,
+                                               ChunkRaw<T, VEC>& c) {
   using S = typename io<T>::storage;
   if constexpr (VEC) {
     constexpr int NV = kVecN<T>;
     const uint4* p =
         reinterpret_cast<const uint4*>(static_cast<const S*>(src) + static_cast<size_t>(row) * V);
     const int last = V / NV - 1;
-    uint4 raw[kPerThread / NV];
 #pragma unroll
     for (int l = 0; l < kPerThread / NV; ++l)
-      raw[l] = p[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
+      c.raw[l] = p[min(chunk * (kChunk / NV) + l * kThreads + tid, last)];
+  } else {
+    const S* p = static_cast<const S*>(src) + static_cast<size_t>(row) * V;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      c.raw[e] = p[min(chunk_entry<T, false>(chunk, tid, e), V - 1)];
+  }
+}
+
+// The entries as fp32 values (bf16 widens exactly).
+template <typename T, bool VEC>
+__device__ __forceinline__ void unpack_chunk(const ChunkRaw<T, VEC>& c, float* out) {
+  if constexpr (VEC) {
+    constexpr int NV = kVecN<T>;
 #pragma unroll
     for (int l = 0; l < kPerThread / NV; ++l) {
-      const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+      const uint32_t w[4] = {c.raw[l].x, c.raw[l].y, c.raw[l].z, c.raw[l].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if constexpr (NV == 8) {  // two bf16 entries per word, the lower first
@@ -253,37 +315,65 @@ __device__ __forceinline__ void load_chunk(const void* src, int row, int V, int 
       }
     }
   } else {
-    const size_t base = static_cast<size_t>(row) * V;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      out[e] = ld<T>(src, base + min(chunk_entry<T, false>(chunk, tid, e), V - 1));
+    for (int e = 0; e < kPerThread; ++e) {
+      if constexpr (std::is_same<T, float>::value) out[e] = c.raw[e];
+      else out[e] = bf16_to_f32(c.raw[e]);
+    }
   }
 }
 
-// ------------------------------------------------------------------ greedy
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void row_argmax_partial(AcceptArgs a) {
-  const int chunk = blockIdx.x, row = blockIdx.y;
+__device__ __forceinline__ void load_chunk(const void* src, int row, int V, int chunk, int tid,
+                                           float* out) {
+  ChunkRaw<T, VEC> c;
+  load_chunk_raw<T, VEC>(src, row, V, chunk, tid, c);
+  unpack_chunk<T, VEC>(c, out);
+}
+
+// ------------------------------------------------------------------ greedy
+// The row kernels below are persistent: block i takes the (row, chunk) items
+// i, i + grid, ... (chunk fastest) and issues the next item's loads before it
+// reduces the current one, so a block always has a chunk in flight.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void row_argmax_partial(AcceptArgs a, int n_items) {
   const int tid = threadIdx.x;
-  const int nc = gridDim.x;
-  unsigned long long best = 0;
-  float vals[kPerThread];
-  load_chunk<T, VEC>(a.target, row, a.V, chunk, tid, vals);
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {  // the key orders ties by index
-    const int idx = chunk_entry<T, VEC>(chunk, tid, e);
-    const unsigned long long key = idx < a.V ? argmax_key(vals[e], idx) : 0ull;
-    best = key > best ? key : best;
-  }
-  best = wave_max_u64(best);
+  const int nc = n_chunks(a.V);
   __shared__ unsigned long long red[kThreads / 64];
-  if ((tid & 63) == 0) red[tid >> 6] = best;
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kThreads / 64; ++w) best = red[w] > best ? red[w] : best;
-    const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
-    reinterpret_cast<unsigned long long*>(static_cast<char*>(a.ws) + L.keys)
-        [static_cast<size_t>(row) * nc + chunk] = best;
+  const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(a.ws) + L.keys);
+  ChunkRaw<T, VEC> nxt;
+  int item = blockIdx.x;
+  if (item < n_items) load_chunk_raw<T, VEC>(a.target, item / nc, a.V, item % nc, tid, nxt);
+  for (; item < n_items; item += gridDim.x) {
+    const int row = item / nc, chunk = item - row * nc;
+    float vals[kPerThread];
+    unpack_chunk<T, VEC>(nxt, vals);
+    const int next = item + gridDim.x;
+    if (next < n_items) load_chunk_raw<T, VEC>(a.target, next / nc, a.V, next % nc, tid, nxt);
+    unsigned long long best = 0;
+    if (chunk_has_tail(chunk, a.V)) {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {  // the key orders ties by index
+        const int idx = chunk_entry<T, VEC>(chunk, tid, e);
+        const unsigned long long key = idx < a.V ? argmax_key(vals[e], idx) : 0ull;
+        best = key > best ? key : best;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        const unsigned long long key = argmax_key(vals[e], chunk_entry<T, VEC>(chunk, tid, e));
+        best = key > best ? key : best;
+      }
+    }
+    best = wave_max_u64(best);
+    if ((tid & 63) == 0) red[tid >> 6] = best;
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < kThreads / 64; ++w) best = red[w] > best ? red[w] : best;
+      keys[static_cast<size_t>(row) * nc + chunk] = best;
+    }
+    __syncthreads();  // red is written again by the next item
   }
 }
 
@@ -343,44 +433,52 @@ __global__ __launch_bounds__(64) void decide_greedy(AcceptArgs a) {
 // Row r < total_T: target row r; otherwise draft row r - total_T.
 // VEC: 16-byte row loads (see chunk_entry).
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a) {
-  const int chunk = blockIdx.x, r = blockIdx.y;
+__global__ __launch_bounds__(kThreads) void row_stats_partial(AcceptArgs a, int n_items) {
   const int tid = threadIdx.x;
-  const int nc = gridDim.x;
-  const void* src = r < a.total_T ? a.target : a.draft;
-  auto entry = [&](int e) { return chunk_entry<T, VEC>(chunk, tid, e); };
-  float vals[kPerThread];
-  load_chunk<T, VEC>(src, r < a.total_T ? r : r - a.total_T, a.V, chunk, tid, vals);
+  const int nc = n_chunks(a.V);
   __shared__ float redm[kThreads / 64];
   __shared__ double reds[kThreads / 64];
-  __shared__ double tab[kExpTab];
-  exp_table_init(tab);  // read after the barrier below
-  float m = -INFINITY;
+  __shared__ uint2 tab[kExpTab];
+  exp_table_init_biased(tab);  // read after the first barrier below
+  const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
+  double2* stats = reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats);
+  auto load = [&](int it, ChunkRaw<T, VEC>& c) __attribute__((always_inline)) {
+    const int r = it / nc;
+    load_chunk_raw<T, VEC>(r < a.total_T ? a.target : a.draft,
+                           r < a.total_T ? r : r - a.total_T, a.V, it - r * nc, tid, c);
+  };
+  ChunkRaw<T, VEC> nxt;
+  int item = blockIdx.x;
+  if (item < n_items) load(item, nxt);
+  for (; item < n_items; item += gridDim.x) {
+    const int r = item / nc, chunk = item - r * nc;
+    float vals[kPerThread];
+    unpack_chunk<T, VEC>(nxt, vals);
+    if (item + static_cast<int>(gridDim.x) < n_items) load(item + gridDim.x, nxt);
+    if (chunk_has_tail(chunk, a.V)) {
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    if (entry(e) >= a.V) vals[e] = -INFINITY;
-    m = fmaxf(m, vals[e]);
-  }
-  m = wave_max_f32(m);
-  if ((tid & 63) == 0) redm[tid >> 6] = m;
-  __syncthreads();
-  m = redm[0];
-  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, redm[w]);
-  double s = 0.0;
-  if (m > -INFINITY) {
+      for (int e = 0; e < kPerThread; ++e)
+        if (chunk_entry<T, VEC>(chunk, tid, e) >= a.V) vals[e] = -INFINITY;
+    }
+    float m = vals[0];
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      s += exp_nonpos(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
-  }
-  s = wave_sum_f64(s);
-  if ((tid & 63) == 0) reds[tid >> 6] = s;
-  __syncthreads();
-  if (tid == 0) {
-    s = reds[0];
-    for (int w = 1; w < kThreads / 64; ++w) s += reds[w];
-    const AcceptWs L = accept_ws_layout(a.B, a.total_T, a.V, a.mode);
-    reinterpret_cast<double2*>(static_cast<char*>(a.ws) + L.stats)
-        [static_cast<size_t>(r) * nc + chunk] = make_double2(static_cast<double>(m), s);
+    for (int e = 1; e < kPerThread; ++e) m = fmaxf(m, vals[e]);
+    m = wave_max_f32(m);
+    if ((tid & 63) == 0) redm[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+    double sum = 0.0;
+    if (m > -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        sum += exp_nonpos_sum(static_cast<double>(vals[e]) - static_cast<double>(m), tab);
+    }
+    sum = wave_sum_f64(sum);
+    if ((tid & 63) == 0) reds[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0)
+      stats[static_cast<size_t>(r) * nc + chunk] =
+          make_double2(static_cast<double>(m), reds[0] + reds[1] + reds[2] + reds[3]);
   }
 }
 
@@ -517,17 +615,52 @@ __device__ __forceinline__ void load_draw_logits(const AcceptArgs& a, int kind, 
   }
 }
 
-// Weight of vocabulary entry y from its logits; rz holds the reciprocals of
-// the two normalisers (f.y, f.w).  Entries past the vocabulary weigh 0.
+// Weight of vocabulary entry y < V from its logits; rz holds the reciprocals
+// of the two normalisers (f.y, f.w).  KIND 0: p; 1: max(p - q, 0); 2: p
+// with the point-mass draft at rd taken out.
+template <int KIND>
+__device__ __forceinline__ double draw_weight_k(int rd, const double4& f, const double2& rz, int y,
+                                                float2 lg, const double* tab) {
+  const double p = exp_nonpos(static_cast<double>(lg.x) - f.x, tab) * rz.x;
+  if constexpr (KIND == 0) {
+    return p;
+  } else if constexpr (KIND == 2) {
+    return y == rd ? 0.0 : p;
+  } else {
+    const double q = exp_nonpos(static_cast<double>(lg.y) - f.z, tab) * rz.y;
+    return fmax(p - q, 0.0);
+  }
+}
+
+// The same for any kind and any y; entries past the vocabulary weigh 0.
 __device__ __forceinline__ double draw_weight(const AcceptArgs& a, int kind, int rd,
                                               const double4& f, const double2& rz, int y,
                                               float2 lg, const double* tab) {
   if (y >= a.V) return 0.0;
-  const double p = exp_nonpos(static_cast<double>(lg.x) - f.x, tab) * rz.x;
-  if (kind == 0) return p;
-  if (kind == 2) return y == rd ? 0.0 : p;  // point-mass draft at rd
-  const double q = exp_nonpos(static_cast<double>(lg.y) - f.z, tab) * rz.y;
-  return fmax(p - q, 0.0);
+  if (kind == 0) return draw_weight_k<0>(rd, f, rz, y, lg, tab);
+  if (kind == 2) return draw_weight_k<2>(rd, f, rz, y, lg, tab);
+  return draw_weight_k<1>(rd, f, rz, y, lg, tab);
+}
+
+// A thread's sum of the weights of its kPerThread entries of a chunk, in
+// entry order (as draw_weight would give them: a masked entry adds 0).
+template <int KIND, typename T, bool VEC>
+__device__ __forceinline__ double residual_thread_sum(const AcceptArgs& a, int rd, const double4& f,
+                                                      const double2& rz, int chunk, int tid,
+                                                      const float2* lg, const double* tab) {
+  double s = 0.0;
+  if (chunk_has_tail(chunk, a.V)) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int y = chunk_entry<T, VEC>(chunk, tid, e);
+      if (y < a.V) s += draw_weight_k<KIND>(rd, f, rz, y, lg[e], tab);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      s += draw_weight_k<KIND>(rd, f, rz, chunk_entry<T, VEC>(chunk, tid, e), lg[e], tab);
+  }
+  return s;
 }
 
 // VEC: as for row_stats_partial.
@@ -539,7 +672,6 @@ __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
   const double4 f = reinterpret_cast<const double4*>(static_cast<const char*>(a.ws) + L.fin)[b];
   if (d.x < 0) return;
   const double2 rz = make_double2(1.0 / f.y, 1.0 / f.w);
-  auto entry = [&](int e) { return chunk_entry<T, VEC>(chunk, tid, e); };
   float2 lg[kPerThread];
   {
     float pt[kPerThread], pq[kPerThread];
@@ -557,10 +689,10 @@ __global__ __launch_bounds__(kThreads) void residual_partial(AcceptArgs a) {
   __shared__ double red[kThreads / 64];
   exp_table_init(tab);
   __syncthreads();
-  double s = 0.0;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e)
-    s += draw_weight(a, d.y, d.w, f, rz, entry(e), lg[e], tab);
+  double s;
+  if (d.y == 1) s = residual_thread_sum<1, T, VEC>(a, d.w, f, rz, chunk, tid, lg, tab);
+  else if (d.y == 2) s = residual_thread_sum<2, T, VEC>(a, d.w, f, rz, chunk, tid, lg, tab);
+  else s = residual_thread_sum<0, T, VEC>(a, d.w, f, rz, chunk, tid, lg, tab);
   s = wave_sum_f64(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
@@ -767,6 +899,16 @@ __global__ __launch_bounds__(kThreads) void final_draw(AcceptArgs a) {
   if (tid == 0) write_outputs(a, b, d.z - d.x, d.x, y);  // d.z - d.x = first row x0
 }
 
+// Blocks of the persistent row kernels: eight per compute unit.
+int row_blocks() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return 8 * cus;
+}
+
 template <typename T>
 hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
   const int nc = n_chunks(a.V);
@@ -776,17 +918,21 @@ hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
                    reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
                    (!a.draft || reinterpret_cast<uintptr_t>(a.draft) % 16 == 0);
   if (a.mode == SV_ACCEPT_GREEDY) {
+    const int n_items = nc * a.total_T;
+    const dim3 grid(std::min(n_items, row_blocks()));
     if (vec)
-      hipLaunchKernelGGL((row_argmax_partial<T, true>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((row_argmax_partial<T, true>), grid, dim3(kThreads), 0, stream, a, n_items);
     else
-      hipLaunchKernelGGL((row_argmax_partial<T, false>), dim3(nc, a.total_T), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((row_argmax_partial<T, false>), grid, dim3(kThreads), 0, stream, a, n_items);
     hipLaunchKernelGGL(decide_greedy, dim3(a.B), dim3(64), 0, stream, a);
   } else {
     const int rows = a.draft ? 2 * a.total_T - a.B : a.total_T;
+    const int n_items = nc * rows;
+    const dim3 grid(std::min(n_items, row_blocks()));
     if (vec)
-      hipLaunchKernelGGL((row_stats_partial<T, true>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((row_stats_partial<T, true>), grid, dim3(kThreads), 0, stream, a, n_items);
     else
-      hipLaunchKernelGGL((row_stats_partial<T, false>), dim3(nc, rows), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((row_stats_partial<T, false>), grid, dim3(kThreads), 0, stream, a, n_items);
     hipLaunchKernelGGL((decide_reject<T>), dim3(a.B), dim3(kThreads), 0, stream, a);
     if (vec)
       hipLaunchKernelGGL((residual_partial<T, true>), dim3(nc, a.B), dim3(kThreads), 0, stream, a);
