@@ -19,11 +19,14 @@ figures).
 
 Prints one JSON line.  value = verified draft tokens per second (sum_b k_b
 per step) over the timed steps; the per-step median, p10 and p90 come from
-HIP events between the steps.  Also reported: algorithmic HBM bytes per
-step and GB/s (% of the 8 TB/s peak and of the copy / read rates measured
-in the same run), the roofline of the dominant kernel (timed over
-back-to-back launches with HIP events on the stream it runs on), and the CPU
-oracle timed on a bounded sample of the same workload.
+HIP events between the steps (for the single-call workloads 1 and 2, whose
+calls last tens of microseconds, from a second pass: an event between calls
+costs a few microseconds, so the timed pass records events only at its two
+ends).  Also reported: algorithmic HBM bytes per step and GB/s (% of the
+8 TB/s peak and of the copy / read rates measured in the same run), the
+roofline of the dominant kernel (back-to-back launches between two HIP
+events on the stream it runs on), and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 
 import argparse
@@ -361,6 +364,20 @@ def percentiles(ms):
             'p90': round(float(np.percentile(a, 90)), 4), 'n': int(a.size)}
 
 
+def timed_block(stream, calls):
+    """Run the callables back to back on `stream` between two HIP events
+    (nothing recorded between them); returns the total time (ms)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for c in calls:
+        c()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def timed_calls(stream, calls):
     """Run the callables back to back on `stream` with a HIP event before
     each one and after the last; returns the per-call times (ms) and the
@@ -483,15 +500,22 @@ def base_line(w, args, steps, warmup, value, ms_step, config):
     }
 
 
-def graph_replay_ms(make_graphs, replay_plan, finish, stream, steps):
+def graph_replay_ms(make_graphs, replay_plan, finish, stream, steps, two_pass=False):
     """Capture HIP graphs (make_graphs returns them after an eager lead-in),
     replay them `steps` times per replay_plan(i), finish() (the flush), all
-    between HIP events; returns the per-replay times and the total / steps."""
+    between HIP events; returns the per-replay times and the total / steps.
+    two_pass (replays that can be repeated, each well under a millisecond):
+    the total from a pass with no event between replays, the per-replay
+    times from a second pass."""
     import torch
     graphs = make_graphs()
     calls = [(lambda i=i: graphs[replay_plan(i)].replay()) for i in range(steps)]
     calls.append(finish)
-    per, total = timed_calls(stream, calls)
+    if two_pass:
+        total = timed_block(stream, calls)
+        per, _ = timed_calls(stream, calls)
+    else:
+        per, total = timed_calls(stream, calls)
     return per[:steps], total / steps
 
 
@@ -625,17 +649,17 @@ def run_step_workload(w, args, dev, ceil):
             calls.append(lambda l=l: bd.spec_verify_attention(
                 sb, l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
                 batch.block_table, ctx_fixed, l['out'], workspace=ws, err=err))
-    _, att_total = timed_calls(stream, calls)
+    att_total = timed_block(stream, calls)
     n_launch = len(calls)
     att_ms_mean = att_total / n_launch
     b_att = attn_bytes(w, batch, ctx_fixed.tolist())
-    _, g_total = timed_calls(stream, [
+    g_total = timed_block(stream, [
         (lambda l=l: bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_COMMIT, l['state'], l['q'],
                                           l['k'], l['v'], l['alpha'], l['beta'], commits[0],
                                           l['out'])) for l in gdn_l])
     gdn_ms = g_total / max(1, len(gdn_l))
     acc_reps = 20
-    _, a_total = timed_calls(stream, [
+    a_total = timed_block(stream, [
         (lambda: bd.spec_accept(sb, amode, acc['target_logits'], acc['draft_tokens'], result,
                                 draft_logits=acc.get('draft_logits'),
                                 u_accept=acc.get('u_accept'), u_final=acc.get('u_final'),
@@ -826,8 +850,11 @@ def run_attention_workload(w, args, dev, ceil):
     for i in range(warmup):
         call(i)
     stream = torch.cuda.current_stream()
-    per, total = timed_calls(stream, [(lambda i=i: call(i)) for i in range(steps)])
+    total = timed_block(stream, [(lambda i=i: call(i)) for i in range(steps)])
     ms = total / steps
+    # per-call spread from a second pass with an event between calls (each
+    # event adds a few microseconds, so the mean above is taken without them)
+    per, _ = timed_calls(stream, [(lambda i=i: call(i)) for i in range(steps)])
     assert int(err.item()) == 0
     graph = None
     if not args.no_graph:
@@ -840,7 +867,7 @@ def run_attention_workload(w, args, dev, ceil):
                 gs.append(g)
             return gs
         gper, gms = graph_replay_ms(make_graphs, lambda i: i % n_sets, lambda: None, stream,
-                                    steps)
+                                    steps, two_pass=True)
         graph = {'ms_per_step': round(gms, 4), 'step_ms': percentiles(gper),
                  'how': 'each buffer set\'s call captured into a HIP graph, replayed in turn'}
     draft = batch.total_T - batch.B
@@ -902,8 +929,11 @@ def run_gdn_workload(w, args, dev, ceil):
     for i in range(warmup):
         call(i)
     stream = torch.cuda.current_stream()
-    per, total = timed_calls(stream, [(lambda i=i: call(i)) for i in range(steps)])
+    total = timed_block(stream, [(lambda i=i: call(i)) for i in range(steps)])
     ms = total / steps
+    # per-call spread from a second pass with an event between calls (each
+    # event adds a few microseconds, so the mean above is taken without them)
+    per, _ = timed_calls(stream, [(lambda i=i: call(i)) for i in range(steps)])
     assert int(err.item()) == 0
     graph = None
     if not args.no_graph:
@@ -916,7 +946,7 @@ def run_gdn_workload(w, args, dev, ceil):
                 gs.append(g)
             return gs
         gper, gms = graph_replay_ms(make_graphs, lambda i: i % n_sets, lambda: None, stream,
-                                    steps)
+                                    steps, two_pass=True)
         graph = {'ms_per_step': round(gms, 4), 'step_ms': percentiles(gper),
                  'how': 'each buffer set\'s call captured into a HIP graph, replayed in turn'}
     draft = batch.total_T - batch.B
