@@ -722,6 +722,8 @@ def run_step_workload(w, args, dev, ceil):
         'step_with_short_conv': with_conv,
         'next_rows': next_rows,
         'mean_accept_len': round(accepted, 3),
+        # sum_b (a_b + 1) per timed step, from the ctx_lens the steps advanced
+        'committed_tokens_per_step': round(c_last.sum().item(), 2),
         'dtype_detail': ('bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance'
                          if dt_a == bd.SV_BF16 else
                          'fp32 I/O and accumulation, fp32 GDN state, fp64 acceptance'),
