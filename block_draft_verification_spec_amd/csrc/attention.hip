@@ -142,54 +142,78 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 // Work split: the (sequence, KV head) segments are laid end to end as one
 // sequence of N 64-key tiles (segment s = b * Hkv + g holds the tiles of
 // sequence b, head g, in position order).  Each segment is priced at its
-// tiles plus kPieceCost units for the set-up of a piece (bounds, Q, page
+// tiles plus piece_cost() units for the set-up of a piece (bounds, Q, page
 // ids, a first tile with none in flight, and the write of its result);
-// the U units are split over the W workgroups by weight (kRoundW below),
+// the U units are split over the W workgroups by weight (round_w below),
 // workgroup w taking units [U S(w) / S(W), U S(w + 1) / S(W)) with S(w) the
 // weight of workgroups 0 .. w - 1, and a unit range maps to the tiles it
-// covers (unit r of a segment is its tile max(r - kPieceCost, 0)).  So each
+// covers (unit r of a segment is its tile max(r - piece_cost, 0)).  So each
 // workgroup's share of the cost is fixed whatever the context lengths: one
-// that starts more segments streams fewer tiles.  A segment cut by range boundaries is
-// computed in pieces; piece (s, w) of a segment writes its partial
-// (max, sum, O) to slot s + w (distinct for every piece, since segments
-// advance with w) and the workgroup that owns the segment's first tile
-// records which workgroups cover the segment; a combine kernel merges the
-// pieces.  A segment covered by one workgroup is written directly.
+// that starts more segments streams fewer tiles.  A segment cut by range
+// boundaries is computed in pieces; piece (s, w) of a segment writes its
+// partial (max, sum, O) to slot s + w (distinct for every piece, since
+// segments advance with w) and the workgroup that owns the segment's first
+// tile records which workgroups cover the segment; a combine kernel merges
+// the pieces.  A segment covered by one workgroup is written directly.
 constexpr int kMaxB = 2048;        // sequences per call on the bf16 path
 constexpr int kChunkTiles = 256;   // tiles whose page ids are staged at once
 constexpr int kRound = 12;         // tiles per unrolled round (a multiple of PF)
 constexpr int kMaxRows = 64;       // query rows per (sequence, KV head)
-constexpr int kPieceCost = 3;  // a piece's set-up, in tiles
 // Wave priority while a wave issues the next tile's loads (0 while it
 // computes), so a CU's waves issue their loads ahead of each other's compute:
 // INT8 pages 2.5 % faster per layer, bf16 unchanged.
 constexpr int kLoadPrio = 3;
-// Share of the units by dispatch round.  Workgroups are placed in order, one
-// per compute unit per round, and a CU's older waves win its arbitration: at
-// three workgroups per CU and equal tile counts the one placed first finished
-// after 189 us, the second after 198 and the last after 229 (MI355X, 16
-// attention layers of 64 sequences with contexts of 2048 to 8192 keys).  The
-// CU's memory path, not the workgroup, sets the rate (the three together
-// stream as fast as a load-only kernel), so the youngest workgroup slows down
-// when given fewer tiles; shorter ranges for later rounds still measured
-// about 1 % faster per layer than equal ones.
-constexpr int kRoundW[4] = {64, 61, 53, 53};
-constexpr int round_w_min() {
-  int m = kRoundW[0];
-  for (int i = 1; i < 4; ++i) m = kRoundW[i] < m ? kRoundW[i] : m;
+
+// Split parameters, measured on MI355X (64 sequences of 2048 to 8192 keys,
+// 32q/8kv heads, D = 128, 4 verify tokens; 32 sequences of 512 to 4096
+// keys; 256 sequences of 16384 to 32768 keys with 2 to 8 verify tokens).
+//
+// Profile 0, bf16 pages with one 16-row tile (G T_b <= 16): two workgroups
+// per CU (the register budget is that of three; see wg_per_cu_cap), equal
+// weights and a piece set-up priced at 7 tiles: 0.227-0.231 ms per layer
+// against 0.239-0.241 ms at three workgroups per CU, and 61.6-63.3 against
+// 67-68 us for the 32-sequence call.  One tile in flight per workgroup at
+// two workgroups streams faster than at three: a CU's memory path is shared,
+// and the third workgroup mostly lengthened the queue (a 2-deep register
+// ring at two per CU measured 0.237 ms, one per CU 0.270 ms).
+//
+// Profile 1, everything else: INT8 pages at three workgroups per CU (their
+// tiles carry more VALU work per byte; at two per CU they ran 0.136-0.155
+// against 0.132-0.140 ms) and the 32-row tiles of longer verify blocks at
+// the two per CU their registers allow (equal weights and a 7-tile set-up
+// made the 256-sequence layer 2.5 % slower), with a 3-tile piece set-up and
+// weights by dispatch round: workgroups are placed in order, one per CU per
+// round, and a CU's older waves win its arbitration (at equal tile counts
+// and three per CU the one placed first finished after 189 us, the second
+// after 198 and the last after 229), so later rounds get shorter ranges
+// (about 1 % faster per layer than equal ones).
+// 16-row MFMA tiles of query rows per (sequence, KV head): G max_T rows.
+__host__ __device__ constexpr int nqt_for(int G, int max_T) {
+  return G * max_T <= 16 ? 1 : (G * max_T <= 32 ? 2 : 4);
+}
+__host__ __device__ constexpr int split_profile(bool kv8, int nqt) {
+  return (!kv8 && nqt == 1) ? 0 : 1;
+}
+template <int PROF>
+constexpr int piece_cost() { return PROF == 0 ? 7 : 3; }
+constexpr int kRoundW[2][4] = {{64, 64, 64, 64}, {64, 61, 53, 53}};  // [profile][round]
+__host__ __device__ inline int round_w(int r, int prof) { return kRoundW[prof][r < 3 ? r : 3]; }
+__host__ __device__ inline int round_w_min(int prof) {
+  int m = kRoundW[prof][0];
+  for (int i = 1; i < 4; ++i) m = kRoundW[prof][i] < m ? kRoundW[prof][i] : m;
   return m;
 }
-__host__ __device__ inline int round_w(int r) { return kRoundW[r < 3 ? r : 3]; }
 // Weight of workgroups [0, w): n_cu workgroups per round.
-__host__ __device__ inline long long wg_weight(int w, int n_cu) {
+__host__ __device__ inline long long wg_weight(int w, int n_cu, int prof) {
   long long s = 0;
   int r = 0;
-  for (; (r + 1) * n_cu <= w; ++r) s += static_cast<long long>(n_cu) * round_w(r);
-  return s + static_cast<long long>(w - r * n_cu) * round_w(r);
+  for (; (r + 1) * n_cu <= w; ++r) s += static_cast<long long>(n_cu) * round_w(r, prof);
+  return s + static_cast<long long>(w - r * n_cu) * round_w(r, prof);
 }
 // First unit of workgroup w: U S(w) / S(W).
-__host__ __device__ inline int wg_unit(int w, int W, int n_cu, int U) {
-  return static_cast<int>(static_cast<long long>(U) * wg_weight(w, n_cu) / wg_weight(W, n_cu));
+__host__ __device__ inline int wg_unit(int w, int W, int n_cu, int U, int prof) {
+  return static_cast<int>(static_cast<long long>(U) * wg_weight(w, n_cu, prof) /
+                          wg_weight(W, n_cu, prof));
 }
 
 // One tile's slice of K and V held by a thread.
@@ -199,17 +223,17 @@ struct TileRegs {
   u32x4_t v[KPT];
 };
 
-__host__ __device__ inline int piece_wg(int u, int W, int n_cu, int U) {
+__host__ __device__ inline int piece_wg(int u, int W, int n_cu, int U, int prof) {
   // the workgroup whose range [wg_unit(w), wg_unit(w + 1)) holds unit u: the
   // last w with U S(w) < (u + 1) S(W), i.e. S(w) <= smax
-  const long long smax = ((static_cast<long long>(u) + 1) * wg_weight(W, n_cu) - 1) / U;
+  const long long smax = ((static_cast<long long>(u) + 1) * wg_weight(W, n_cu, prof) - 1) / U;
   int r = 0;
   long long base = 0;
-  while ((r + 1) * n_cu < W && base + static_cast<long long>(n_cu) * round_w(r) <= smax) {
-    base += static_cast<long long>(n_cu) * round_w(r);
+  while ((r + 1) * n_cu < W && base + static_cast<long long>(n_cu) * round_w(r, prof) <= smax) {
+    base += static_cast<long long>(n_cu) * round_w(r, prof);
     ++r;
   }
-  return min(r * n_cu + static_cast<int>((smax - base) / round_w(r)), W - 1);
+  return min(r * n_cu + static_cast<int>((smax - base) / round_w(r, prof)), W - 1);
 }
 
 // PF: tiles in flight per workgroup (a ring of register buffers; registers
@@ -218,6 +242,8 @@ __host__ __device__ inline int piece_wg(int u, int W, int n_cu, int U) {
 template <int D, int NQT, int PF, bool KV8>
 __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   constexpr int DPC = KV8 ? 16 : 8;  // dims per 16-byte chunk
+  constexpr int kProf = split_profile(KV8, NQT);
+  constexpr int kPC = piece_cost<kProf>();  // a piece's set-up, in tiles
   constexpr int CPK = D / DPC;      // 16-byte chunks per key row
   constexpr int KPT = CPK / 4;      // keys per thread per tile (4, 2 or 1)
   constexpr int KS = D + 8;         // K row stride in LDS (16-bit elements)
@@ -269,7 +295,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     if (b < B && attn_seq_valid(a, cuv[i], cuv[i + 1] - cuv[i], lv[i], blockIdx.x == 0))
       nts[i] = seq_tiles(lv[i], cuv[i + 1] - cuv[i]);
     run += nts[i] * Hkv;
-    urun += nts[i] > 0 ? (nts[i] + kPieceCost) * Hkv : 0;
+    urun += nts[i] > 0 ? (nts[i] + kPC) * Hkv : 0;
   }
   // inclusive scans of the per-thread tile and unit totals: within each wave
   // by shuffles, then the totals of the waves before it
@@ -296,8 +322,8 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   const int U = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
   const int W = gridDim.x, wg = blockIdx.x;
   if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = U;  // for the combine launch
-  const int u_lo = wg_unit(wg, W, a.n_cu, U);
-  const int u_hi = wg_unit(wg + 1, W, a.n_cu, U);
+  const int u_lo = wg_unit(wg, W, a.n_cu, U, kProf);
+  const int u_hi = wg_unit(wg + 1, W, a.n_cu, U, kProf);
   // the sequences whose units hold u_lo and u_hi: their owners map them to
   // tiles (sequences without tiles own no units and never match; unit U maps
   // to tile N)
@@ -305,10 +331,10 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     int pre = excl, upre = uexcl;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int nt = nts[i], uend = upre + (nt > 0 ? (nt + kPieceCost) * Hkv : 0);
+      const int nt = nts[i], uend = upre + (nt > 0 ? (nt + kPC) * Hkv : 0);
       auto tile_of = [&](int u) {
-        const int r = u - upre, h = r / (nt + kPieceCost);
-        return pre + h * nt + max(r - h * (nt + kPieceCost) - kPieceCost, 0);
+        const int r = u - upre, h = r / (nt + kPC);
+        return pre + h * nt + max(r - h * (nt + kPC) - kPC, 0);
       };
       if (u_lo >= upre && u_lo < uend) {
         s_first[0] = tid * kPer + i;
@@ -576,13 +602,13 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     const int s = b * Hkv + g;
     const bool whole = lt_begin == 0 && lt_end == nt_b;
     M = G * T;
-    // the segment's last tile is its unit kPieceCost + nt_b - 1
+    // the segment's last tile is its unit kPC + nt_b - 1
     const int seg_last_wg =
-        piece_wg(ucbase + g * (nt_b + kPieceCost) + kPieceCost + nt_b - 1, W, a.n_cu, U);
+        piece_wg(ucbase + g * (nt_b + kPC) + kPC + nt_b - 1, W, a.n_cu, U, kProf);
     t = seg_start + lt_end;
     if (t == cbase + Hkv * nt_b) {
       cbase = t;
-      ucbase += Hkv * (nt_b + kPieceCost);
+      ucbase += Hkv * (nt_b + kPC);
       ++cb;
       next_seq = true;
     }
@@ -903,11 +929,12 @@ __global__ __launch_bounds__(kThreads) void attn_combine_bf16(AttnArgs a) {
   // last tiles every unit is a tile, so a non-empty unit range there is a
   // non-empty piece.
   const int W = a.n_wg, ncu = a.n_cu;
-  const bool sparse = static_cast<long long>(Units) * round_w_min() < wg_weight(W, ncu);
+  const int prof = split_profile(a.kv8 != 0, nqt_for(G, a.max_T));
+  const bool sparse = static_cast<long long>(Units) * round_w_min(prof) < wg_weight(W, ncu, prof);
   constexpr int kFew = 4;  // pieces fetched at once (one round trip)
   int pws[kFew], np = 0;
   for (int w = wf; w <= wl_; ++w) {
-    if (sparse && wg_unit(w, W, ncu, Units) == wg_unit(w + 1, W, ncu, Units)) continue;
+    if (sparse && wg_unit(w, W, ncu, Units, prof) == wg_unit(w + 1, W, ncu, Units, prof)) continue;
     if (np < kFew) pws[np] = w;
     ++np;
   }
@@ -939,7 +966,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_bf16(AttnArgs a) {
         if (q < np) add(ml[q].x, ml[q].y, po[q]);
     } else {
       for (int w = wf; w <= wl_; ++w) {
-        if (sparse && wg_unit(w, W, ncu, Units) == wg_unit(w + 1, W, ncu, Units)) continue;
+        if (sparse && wg_unit(w, W, ncu, Units, prof) == wg_unit(w + 1, W, ncu, Units, prof)) continue;
         const size_t pi = static_cast<size_t>(s + w) * kMaxRows + m;
         const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * pi);
         add(ml.x, ml.y, *reinterpret_cast<const float4*>(a.part_o + pi * D + d4));
@@ -1042,10 +1069,11 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
   if (lane + 64 < D) out[lane + 64] = o[1] * inv;
 }
 
-// One tile in flight per workgroup and three resident workgroups per CU
-// measured fastest: more workgroups hide latency better than a deeper ring in
-// fewer of them, but a fourth (128 registers, the LDS of four fitting a CU)
-// was 10 % slower at the 64-sequence hybrid shape.
+// One tile in flight per workgroup.  The register budget is that of three
+// resident workgroups per CU (a fourth, at 128 registers, was 10 % slower at
+// the 64-sequence hybrid shape); INT8 pages launch three per CU, bf16 pages
+// two (wg_per_cu_cap), and a deeper ring in fewer workgroups measured slower
+// for both.
 template <int D, int NQT>
 constexpr int ring_depth() {
   return 1;
@@ -1054,6 +1082,9 @@ template <int D, int NQT>
 constexpr int waves_per_simd() {
   return NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
 }
+// Workgroups launched per CU, at most: split profile 0 (bf16 pages, one
+// 16-row tile) runs two per CU although three fit.
+constexpr int wg_per_cu_cap(bool kv8, int nqt) { return split_profile(kv8, nqt) == 0 ? 2 : 8; }
 
 template <int D, int NQT, bool KV8>
 const void* stream_kernel() {
@@ -1065,10 +1096,6 @@ const void* stream_kernel() {
         &attn_stream_bf16<D, NQT, ring_depth<D, NQT>(), waves_per_simd<D, NQT>()>);
 }
 
-int nqt_for(int G, int max_T) {
-  const int rows = G * max_T;
-  return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-}
 
 template <bool KV8>
 const void* stream_kernel_for(int D, int nqt) {
@@ -1103,6 +1130,7 @@ int stream_grid(int D, int nqt, bool kv8, int* n_cu = nullptr) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
+  per_cu = std::min(per_cu, wg_per_cu_cap(kv8, nqt));
   const int n = cus * per_cu;
   cache[key] = {n, cus};
   if (n_cu) *n_cu = cus;
