@@ -168,32 +168,30 @@ constexpr int kLoadPrio = 3;
 // 32q/8kv heads, D = 128, 4 verify tokens; 32 sequences of 512 to 4096
 // keys; 256 sequences of 16384 to 32768 keys with 2 to 8 verify tokens).
 //
-// Profile 0, bf16 pages with one 16-row tile (G T_b <= 16): two workgroups
-// per CU (the register budget is that of three; see wg_per_cu_cap), equal
-// weights and a piece set-up priced at 7 tiles: 0.227-0.231 ms per layer
-// against 0.239-0.241 ms at three workgroups per CU, and 61.6-63.3 against
-// 67-68 us for the 32-sequence call.  One tile in flight per workgroup at
-// two workgroups streams faster than at three: a CU's memory path is shared,
-// and the third workgroup mostly lengthened the queue (a 2-deep register
-// ring at two per CU measured 0.237 ms, one per CU 0.270 ms).
+// Profile 0, bf16 pages: at most two workgroups per CU (with one 16-row
+// query tile the register budget is that of three; see wg_per_cu_cap),
+// equal weights and a piece set-up priced at 7 tiles: 0.227-0.231 ms per
+// 64-sequence layer against 0.239-0.241 ms at three workgroups per CU, and
+// 61.6-63.3 against 67-68 us for the 32-sequence call.  One tile in flight
+// per workgroup at two workgroups streams faster than at three: a CU's
+// memory path is shared, and the third workgroup mostly lengthened the
+// queue (a 2-deep register ring at two per CU measured 0.237 ms, one per CU
+// 0.270 ms).  The 256-sequence layer (32-row tiles, two per CU by
+// registers) measured the same under either profile.
 //
-// Profile 1, everything else: INT8 pages at three workgroups per CU (their
-// tiles carry more VALU work per byte; at two per CU they ran 0.136-0.155
-// against 0.132-0.140 ms) and the 32-row tiles of longer verify blocks at
-// the two per CU their registers allow (equal weights and a 7-tile set-up
-// made the 256-sequence layer 2.5 % slower), with a 3-tile piece set-up and
-// weights by dispatch round: workgroups are placed in order, one per CU per
-// round, and a CU's older waves win its arbitration (at equal tile counts
-// and three per CU the one placed first finished after 189 us, the second
-// after 198 and the last after 229), so later rounds get shorter ranges
-// (about 1 % faster per layer than equal ones).
+// Profile 1, INT8 pages: three workgroups per CU (their tiles carry more
+// VALU work per byte; at two per CU they ran 0.136-0.155 against
+// 0.132-0.140 ms), a 3-tile piece set-up and weights by dispatch round:
+// workgroups are placed in order, one per CU per round, and a CU's older
+// waves win its arbitration (at equal tile counts the one placed first
+// finished after 189 us, the second after 198 and the last after 229), so
+// later rounds get shorter ranges (about 1 % faster per layer than equal
+// ones).
 // 16-row MFMA tiles of query rows per (sequence, KV head): G max_T rows.
 __host__ __device__ constexpr int nqt_for(int G, int max_T) {
   return G * max_T <= 16 ? 1 : (G * max_T <= 32 ? 2 : 4);
 }
-__host__ __device__ constexpr int split_profile(bool kv8, int nqt) {
-  return (!kv8 && nqt == 1) ? 0 : 1;
-}
+__host__ __device__ constexpr int split_profile(bool kv8) { return kv8 ? 1 : 0; }
 template <int PROF>
 constexpr int piece_cost() { return PROF == 0 ? 7 : 3; }
 constexpr int kRoundW[2][4] = {{64, 64, 64, 64}, {64, 61, 53, 53}};  // [profile][round]
@@ -242,7 +240,7 @@ __host__ __device__ inline int piece_wg(int u, int W, int n_cu, int U, int prof)
 template <int D, int NQT, int PF, bool KV8>
 __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   constexpr int DPC = KV8 ? 16 : 8;  // dims per 16-byte chunk
-  constexpr int kProf = split_profile(KV8, NQT);
+  constexpr int kProf = split_profile(KV8);
   constexpr int kPC = piece_cost<kProf>();  // a piece's set-up, in tiles
   constexpr int CPK = D / DPC;      // 16-byte chunks per key row
   constexpr int KPT = CPK / 4;      // keys per thread per tile (4, 2 or 1)
@@ -929,7 +927,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_bf16(AttnArgs a) {
   // last tiles every unit is a tile, so a non-empty unit range there is a
   // non-empty piece.
   const int W = a.n_wg, ncu = a.n_cu;
-  const int prof = split_profile(a.kv8 != 0, nqt_for(G, a.max_T));
+  const int prof = split_profile(a.kv8 != 0);
   const bool sparse = static_cast<long long>(Units) * round_w_min(prof) < wg_weight(W, ncu, prof);
   constexpr int kFew = 4;  // pieces fetched at once (one round trip)
   int pws[kFew], np = 0;
@@ -1082,9 +1080,9 @@ template <int D, int NQT>
 constexpr int waves_per_simd() {
   return NQT == 1 ? 3 : (NQT == 2 ? 2 : 1);
 }
-// Workgroups launched per CU, at most: split profile 0 (bf16 pages, one
-// 16-row tile) runs two per CU although three fit.
-constexpr int wg_per_cu_cap(bool kv8, int nqt) { return split_profile(kv8, nqt) == 0 ? 2 : 8; }
+// Workgroups launched per CU, at most: split profile 0 (bf16 pages) runs
+// two per CU, also where three fit.
+constexpr int wg_per_cu_cap(bool kv8) { return split_profile(kv8) == 0 ? 2 : 8; }
 
 template <int D, int NQT, bool KV8>
 const void* stream_kernel() {
@@ -1130,7 +1128,7 @@ int stream_grid(int D, int nqt, bool kv8, int* n_cu = nullptr) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
-  per_cu = std::min(per_cu, wg_per_cu_cap(kv8, nqt));
+  per_cu = std::min(per_cu, wg_per_cu_cap(kv8));
   const int n = cus * per_cu;
   cache[key] = {n, cus};
   if (n_cu) *n_cu = cus;
