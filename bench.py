@@ -688,6 +688,14 @@ def run_step_workload(w, args, dev, ceil):
     draft_per_step = T - batch.B
     b_step = (n_att * attn_bytes(w, batch, ctx_mean) + n_gdn * gdn_bytes(w, batch)
               + accept_bytes(w, batch, mode))
+    # bytes the schedule actually moves beyond the method's minimum: the
+    # replayed tokens' k, v and gates (deferred: read again by the next
+    # verify; two-phase: by the batched commit), and under two-phase one more
+    # read of every GDN state
+    es = elem_size(w.gdn_dtype)
+    sum_c = float(c_last.sum().item())
+    replay = sum_c * w.H * ((w.dk + w.dv) * es + 8)
+    extra = n_gdn * (replay + (0 if deferred else batch.B * w.H * w.dv * w.dk * 4))
     pc = percentiles(per[:steps])
     gbs = b_step / (ms_step * 1e-3) / 1e9
     gbs_med = b_step / (pc['median'] * 1e-3) / 1e9
@@ -705,7 +713,12 @@ def run_step_workload(w, args, dev, ceil):
                      'frac_of_peak': round(gbs / HBM_PEAK_GBS, 4),
                      'GBps_at_median': round(gbs_med, 1),
                      'frac_of_measured_read': round(gbs / ceil['read_GBps'], 4),
-                     'contexts': 'mean over the timed steps'},
+                     'contexts': 'mean over the timed steps',
+                     'actual_bytes': int(b_step + extra),
+                     'actual_GBps': round((b_step + extra) / (ms_step * 1e-3) / 1e9, 1),
+                     'actual_how': f'{args.schedule} schedule: the replayed tokens\' k, v and '
+                                   'gates' + ('' if deferred else
+                                              ' and one more read of every GDN state')},
         'ceilings': ceil,
         'roofline': {'kernel': ('spec_verify_attention, one layer (attn_stream_bf16 + '
                                 'attn_combine_bf16 launches)' if dt_a == bd.SV_BF16 else
