@@ -910,10 +910,8 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
                    stream, who);
   if (st != SV_OK) return st;
   // 3. two-phase: commit the first a+1 tokens of every GDN layer
+  // (every layer's state, k, v and gates were checked in step 0)
   if (schedule == SV_SCHEDULE_TWO_PHASE && n_gdn > 0) {
-    sv_status cs = check_gdn_common(batch, gdn[0].state, gcfg->state_dtype, gcfg->num_slots,
-                                    gcfg->io_dtype, gcfg->H, gcfg->dk, gcfg->dv, who);
-    if (cs != SV_OK) return cs;
     sv::GdnScalars s{};
     s.B = batch->B;
     s.total_T = batch->total_T;
@@ -932,8 +930,6 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
       sv::GdnCommitTable t{};
       for (int i = 0; i < nl; ++i) {
         const sv_gdn_layer& G = gdn[l0 + i];
-        if (!G.state || !G.k || !G.v || !G.alpha || !G.beta)
-          return fail(SV_EINVAL, "%s: GDN layer %d lacks state/k/v/alpha/beta", who, l0 + i);
         t.l[i] = sv::GdnCommitPtrs{G.state, G.k, G.v, G.alpha, G.beta};
         t.c[i] = sv::ConvCommitPtrs{G.conv_state, G.conv_x};
       }
