@@ -10,8 +10,9 @@ from block_draft_verification_spec_amd import binding as bd
 DEV = 'cuda'
 
 # Tolerances (stated in the test of each op): attention max-abs 2e-3 (fp32
-# I/O) / 1e-2 (bf16 I/O); committed GDN state max|dS| / max|S_ref| <= 1e-4 per
-# (b, h) tile; GDN outputs 2e-3 (fp32) / 1e-2 + half a bf16 ulp of |o_ref|.
+# I/O) / 1e-2 + half a bf16 ulp of |o_ref| (bf16 I/O); committed GDN state
+# max|dS| / max|S_ref| <= 1e-4 per (b, h) tile; GDN outputs 2e-3 (fp32) /
+# 1e-2 + half a bf16 ulp of |o_ref|.
 ATT_TOL = {torch.float32: 2e-3, torch.bfloat16: 1e-2}
 GDN_STATE_TOL = 1e-4
 # an fp16 state adds one rounding to nearest per stored element (unit
@@ -89,7 +90,16 @@ def check_gdn_out(o_gpu, o_ref, dtype):
 
 
 def check_attn_out(o_gpu, o_ref, dtype):
+    """Max-abs error against the bound of the I/O dtype; a bf16 output also
+    carries its own final rounding, half a bf16 ulp of |o_ref| (at |o| >= 4 the
+    bf16 neighbours are 2^-5 apart, so no bf16 result is within 1e-2 of
+    every real value there)."""
     d = np.abs(np.asarray(o_gpu, dtype=np.float64) - o_ref)
     m = float(d.max()) if d.size else 0.0
-    assert m <= ATT_TOL[dtype], f'attention max abs error {m:.3e} > {ATT_TOL[dtype]}'
+    bound = ATT_TOL[dtype]
+    if dtype == torch.bfloat16 and d.size:
+        bound = ATT_TOL[dtype] + bf16_half_ulp(o_ref)
+    bad = d > bound
+    assert not np.any(bad), (f'attention: {int(np.sum(bad))} elements out of bound, '
+                             f'max abs error {m:.3e}')
     return m

@@ -1,8 +1,9 @@
 """GPU parity of spec_verify_attention against the oracle (through the C ABI).
 
-Tolerance: output max-abs <= 2e-3 at fp32 I/O, <= 1e-2 at bf16 I/O.  The KV
-pools after the call must equal the oracle's append bit for bit (every slot,
-written or not).  Page-permutation invariance is checked bit-exactly.
+Tolerance: output max-abs <= 2e-3 at fp32 I/O, <= 1e-2 + half a bf16 ulp of
+|o_ref| at bf16 I/O (the output's own rounding).  The KV pools after the
+call must equal the oracle's append bit for bit (every slot, written or
+not).  Page-permutation invariance is checked bit-exactly.
 """
 
 import numpy as np

@@ -11,8 +11,8 @@ stress_ragged_long: one two-phase step (B = 256, k_b ~ U{1..7}, contexts
 U[16384, 32768], fragmented pool, one GDN,GDN,GDN,ATT group).
 
 Checked against the oracle, for all sequences: acceptance, commit lengths
-and ctx_lens (bit-exact); every attention output (max-abs <= 1e-2, bf16
-I/O); every KV page after each step (bit-exact: each sequence's pages
+and ctx_lens (bit-exact); every attention output (max-abs <= 1e-2 + half a
+bf16 ulp, bf16 I/O); every KV page after each step (bit-exact: each sequence's pages
 against the oracle's append, pages no sequence owns unchanged); every GDN
 output (1e-2 + half a bf16 ulp) and every committed state tile (normwise
 1e-4).  The oracle runs one sequence at a time (a sequence's result depends

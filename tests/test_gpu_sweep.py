@@ -1,0 +1,312 @@
+"""Seeded sweeps of random valid configurations, every entry point against
+the oracle (through the C ABI).
+
+Each case draws its shapes from its own seed (printed before the GPU call):
+head sizes, page sizes, GQA group sizes, per-sequence draft counts 0..7,
+context lengths from empty to a few thousand keys, attention scales, state
+and I/O dtypes, slot maps, modes, pending (deferred) tokens, convolution
+widths and channel counts, vocabulary sizes off and on the load width,
+point-mass drafts and supplied bonus ids.  The bars are those of the
+dedicated tests: attention max-abs 2e-3 (fp32 I/O) / 1e-2 + half a bf16 ulp
+of |o_ref| (bf16 I/O) and the page pools bit for bit; GDN states 1e-4 normwise per (slot, head) tile
+(fp16 storage: plus one fp16 rounding) and outputs 2e-3 / 1e-2 + half a bf16
+ulp; convolution states bit for bit; acceptance bit-exact.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from block_draft_verification_spec_amd import binding as bd
+from gpu_helpers import (DEV, GDN_STATE_TOL, GDN_STATE_TOL_F16, bits, check_attn_out,
+                         check_gdn_out, check_gdn_state, err_word, np64, npi, say, sv_batch)
+
+pytestmark = pytest.mark.gpu
+
+N_ATTN, N_KV8, N_F32, N_GDN, N_CONV, N_ACC = 12, 6, 4, 10, 8, 10
+
+
+def _ks(r, B, kmax):
+    return [r.randint(0, kmax) for _ in range(B)]
+
+
+def _attn_case(r, kv8=False, f32=False):
+    if f32:
+        D, P = r.choice([8, 32, 40, 64, 96, 128]), r.choice([1, 3, 16, 64])
+    else:
+        D, P = r.choice([64, 128]), r.choice([16, 32, 64, 128, 256])
+    Hkv = r.choice([1, 2, 4, 8])
+    kmax = r.randint(0, 7)
+    groups = [g for g in (1, 2, 4, 8, 16) if g * (kmax + 1) <= 64]
+    G = r.choice(groups)
+    B = r.randint(1, 24)
+    lo = r.choice([0, 0, 1, 63, 500])
+    hi = lo + r.choice([0, 1, 70, 700, 2500])
+    w = wl.Workload('sweep', B=B, k=kmax, ragged_k=False, ctx=(lo, hi), P=P, Hq=G * Hkv,
+                    Hkv=Hkv, D=D, attn_dtype=torch.float32 if f32 else torch.bfloat16,
+                    pool_factor=r.choice([1.0, 1.3]))
+    ks = _ks(r, B, kmax)
+    scale = r.choice([0.0, 0.0, 0.05, 0.3])
+    return w, ks, scale
+
+
+def _sub_table(table, b):
+    pages = table[b][table[b] >= 0]
+    sub = np.full_like(table[b:b + 1], -1)
+    sub[0, :len(pages)] = np.arange(len(pages))
+    return pages, sub
+
+
+@pytest.mark.parametrize('i', range(N_ATTN + N_F32))
+def test_attention_sweep(i):
+    r = random.Random(9100 + i)
+    f32 = i >= N_ATTN
+    w, ks, scale = _attn_case(r, f32=f32)
+    batch = wl.make_batch(w, 9200 + i, DEV, k_override=ks)
+    lay = wl.make_attn_layer(w, batch, 9300 + i, DEV)
+    say(f'attention sweep {i}: B={w.B} D={w.D} P={w.P} Hq={w.Hq} Hkv={w.Hkv} '
+        f'T={batch.T} ctx={batch.ctx} scale={scale} {w.attn_dtype}')
+    dt = bd.SV_F32 if f32 else bd.SV_BF16
+    kc, vc = lay['k_cache'].clone(), lay['v_cache'].clone()
+    out = torch.full_like(lay['q'], float('nan'))
+    n = bd.spec_verify_attention_workspace_bytes(batch.B, batch.total_T, w.Hq, w.Hkv, w.D,
+                                                 batch.block_table.shape[1], batch.P, dt)
+    ws = torch.full((max(n, 1),), 0x7f, dtype=torch.uint8, device=DEV)
+    err = err_word()
+    bd.spec_verify_attention(sv_batch(batch), lay['q'], lay['k_new'], lay['v_new'], kc, vc,
+                             batch.block_table, batch.ctx_lens, out, scale=scale,
+                             workspace=ws, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    cu, table, ctx = npi(batch.cu_seqlens), npi(batch.block_table), npi(batch.ctx_lens)
+    e = 0.0
+    for b in range(batch.B):
+        pages, sub = _sub_table(table, b)
+        rows = slice(cu[b], cu[b + 1])
+        pg = torch.from_numpy(pages).to(DEV)
+        ref = oracle.verify_attention(
+            np64(lay['q'][rows]), np64(lay['k_new'][rows]), np64(lay['v_new'][rows]),
+            np64(lay['k_cache'][pg]), np64(lay['v_cache'][pg]), sub, ctx[b:b + 1],
+            np.array([0, cu[b + 1] - cu[b]]), batch.P, scale=scale or None)
+        e = max(e, check_attn_out(np64(out[rows]), ref, w.attn_dtype))
+    k_exp, v_exp = oracle.append_kv(bits(lay['k_cache']), bits(lay['v_cache']),
+                                    bits(lay['k_new']), bits(lay['v_new']), table, ctx, cu,
+                                    batch.P)
+    assert np.array_equal(bits(kc), k_exp)
+    assert np.array_equal(bits(vc), v_exp)
+    say(f'  max abs err {e:.2e}')
+
+
+@pytest.mark.parametrize('i', range(N_KV8))
+def test_attention_kv8_sweep(i):
+    r = random.Random(9400 + i)
+    w, ks, scale = _attn_case(r, kv8=True)
+    batch = wl.make_batch(w, 9500 + i, DEV, k_override=ks)
+    lay = wl.make_attn_layer_kv8(w, batch, 9600 + i, DEV)
+    say(f'INT8 attention sweep {i}: B={w.B} D={w.D} P={w.P} Hq={w.Hq} Hkv={w.Hkv} '
+        f'T={batch.T} ctx={batch.ctx} scale={scale}')
+    kc, vc = lay['k_cache'].clone(), lay['v_cache'].clone()
+    out = torch.full_like(lay['q'], float('nan'))
+    n = bd.spec_verify_attention_workspace_bytes(batch.B, batch.total_T, w.Hq, w.Hkv, w.D,
+                                                 batch.block_table.shape[1], batch.P,
+                                                 bd.SV_BF16)
+    ws = torch.full((max(n, 1),), 0x7f, dtype=torch.uint8, device=DEV)
+    err = err_word()
+    bd.spec_verify_attention_kv8(sv_batch(batch), lay['q'], lay['k_new'], lay['v_new'], kc, vc,
+                                 lay['k_scale'], lay['v_scale'], batch.block_table,
+                                 batch.ctx_lens, out, scale=scale, workspace=ws, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    cu, table, ctx = npi(batch.cu_seqlens), npi(batch.block_table), npi(batch.ctx_lens)
+    f32 = lambda t: t.detach().float().cpu().numpy()
+    i8 = lambda t: t.detach().cpu().numpy()
+    ksc, vsc = f32(lay['k_scale']), f32(lay['v_scale'])
+    e = 0.0
+    for b in range(batch.B):
+        pages, sub = _sub_table(table, b)
+        rows = slice(cu[b], cu[b + 1])
+        pg = torch.from_numpy(pages).to(DEV)
+        ref = oracle.verify_attention_int8(
+            np64(lay['q'][rows]), f32(lay['k_new'][rows]), f32(lay['v_new'][rows]),
+            i8(lay['k_cache'][pg]), i8(lay['v_cache'][pg]), ksc, vsc, sub, ctx[b:b + 1],
+            np.array([0, cu[b + 1] - cu[b]]), batch.P, scale=scale or None)
+        e = max(e, check_attn_out(np64(out[rows]), ref, torch.bfloat16))
+    k_exp, v_exp = oracle.append_kv_int8(i8(lay['k_cache']), i8(lay['v_cache']),
+                                         f32(lay['k_new']), f32(lay['v_new']), ksc, vsc, table,
+                                         ctx, cu, batch.P)
+    assert np.array_equal(i8(kc), k_exp)
+    assert np.array_equal(i8(vc), v_exp)
+    say(f'  max abs err {e:.2e}')
+
+
+GDN_MODES = [bd.SV_GDN_VERIFY_COMMIT, bd.SV_GDN_VERIFY_ONLY, bd.SV_GDN_COMMIT_ONLY]
+ORACLE_MODE = {bd.SV_GDN_VERIFY_COMMIT: oracle.GDN_VERIFY_COMMIT,
+               bd.SV_GDN_VERIFY_ONLY: oracle.GDN_VERIFY_ONLY,
+               bd.SV_GDN_COMMIT_ONLY: oracle.GDN_COMMIT_ONLY}
+
+
+def _commit(r, T):
+    return torch.tensor([r.randint(0, t) for t in T], dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize('i', range(N_GDN))
+def test_gdn_sweep(i):
+    r = random.Random(9700 + i)
+    B, H = r.randint(1, 20), r.randint(1, 5)
+    dk, dv = r.choice([64, 128]), r.choice([64, 128, 192, 256])
+    io = r.choice([torch.float32, torch.bfloat16])
+    sdt = r.choice([torch.float32, torch.float16])
+    mode = r.choice(GDN_MODES)
+    use_slots, pend = r.random() < 0.5, r.random() < 0.5
+    kmax = r.randint(0, 7)
+    w = wl.Workload('sweep', B=B, k=kmax, ragged_k=False, ctx=(0, 0), H=H, dk=dk, dv=dv,
+                    gdn_dtype=io, gdn_init=r.choice(['sigmoid', 'uniform']))
+    cur = wl.make_batch(w, 9800 + i, DEV, k_override=_ks(r, B, kmax))
+    ns = B + (r.randint(0, 9) if use_slots else 0)
+    g = wl.make_gdn_layer(w, cur, 9900 + i, DEV, num_slots=ns, state_dtype=sdt)
+    slots = wl.make_state_slots(cur, ns, 9950 + i, DEV) if use_slots else None
+    commit = None if mode == bd.SV_GDN_VERIFY_ONLY else _commit(r, cur.T)
+    say(f'GDN sweep {i}: B={B} H={H} dk={dk} dv={dv} io={io} state={sdt} mode={mode} '
+        f'slots={use_slots} pending={pend} T={cur.T}')
+    S0 = np64(g['state'])
+    pending = None
+    if pend:
+        prev = wl.make_batch(w, 9850 + i, DEV, k_override=_ks(r, B, kmax))
+        gp = wl.make_gdn_layer(w, prev, 9870 + i, DEV, num_slots=ns)
+        pcommit = _commit(r, prev.T)
+        pending = bd.make_gdn_pending(sv_batch(prev), gp['k'], gp['v'], gp['alpha'],
+                                      gp['beta'], pcommit)
+        _, S0 = oracle.gdn_step(S0, None if slots is None else npi(slots), None,
+                                np64(gp['k']), np64(gp['v']), np64(gp['alpha']),
+                                np64(gp['beta']), npi(prev.cu_seqlens), npi(pcommit),
+                                oracle.GDN_COMMIT_ONLY)
+        if sdt == torch.float16:  # the replayed state is stored, then continued from
+            S0 = S0.astype(np.float16).astype(np.float64)
+    st = g['state'].clone()
+    out = torch.full_like(g['v'], float('nan'))
+    err = err_word()
+    bd.gdn_verify_commit(sv_batch(cur), mode, st, g['q'], g['k'], g['v'], g['alpha'],
+                         g['beta'], commit, out, state_slot=slots, pending=pending, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    o_ref, S_ref = oracle.gdn_step(S0, None if slots is None else npi(slots),
+                                   np64(g['q']), np64(g['k']), np64(g['v']),
+                                   np64(g['alpha']), np64(g['beta']), npi(cur.cu_seqlens),
+                                   None if commit is None else npi(commit), ORACLE_MODE[mode])
+    tol = GDN_STATE_TOL_F16 if sdt == torch.float16 else GDN_STATE_TOL
+    if sdt == torch.float16 and pend:
+        # the replayed state is rounded to fp16 from fp32 on the GPU and from
+        # fp64 here: where the two straddle a rounding midpoint they differ by
+        # one fp16 ulp (at most 2^-10 of the element); the current tokens
+        # carry that on (k unit-norm, 0 <= alpha, beta <= 1: no growth)
+        tol = 2.0 ** -10 * (1 + GDN_STATE_TOL) + GDN_STATE_TOL_F16
+    e_s = check_gdn_state(np64(st), S_ref, tol=tol)
+    e_o = 0.0
+    if mode != bd.SV_GDN_COMMIT_ONLY:
+        e_o = check_gdn_out(np64(out), o_ref, io)
+    say(f'  state err {e_s:.2e}  out err {e_o:.2e}')
+
+
+@pytest.mark.parametrize('i', range(N_CONV))
+def test_conv_sweep(i):
+    r = random.Random(10100 + i)
+    B, K = r.randint(1, 20), r.randint(2, 8)
+    C = r.choice([1, 3, 64, 255, 256, 257, 1000])
+    io = r.choice([torch.float32, torch.bfloat16])
+    mode = r.choice(GDN_MODES)
+    use_slots, pend, silu = r.random() < 0.5, r.random() < 0.5, r.random() < 0.5
+    bias = r.random() < 0.7
+    kmax = r.randint(0, 7)
+    w = wl.Workload('sweep', B=B, k=kmax, ragged_k=False, ctx=(0, 0), gdn_dtype=io, conv_K=K)
+    cur = wl.make_batch(w, 10200 + i, DEV, k_override=_ks(r, B, kmax))
+    ns = B + (r.randint(0, 9) if use_slots else 0)
+    c = wl.make_conv_layer(w, cur, 10300 + i, DEV, num_slots=ns, bias=bias, C=C)
+    slots = wl.make_state_slots(cur, ns, 10350 + i, DEV) if use_slots else None
+    commit = None if mode == bd.SV_GDN_VERIFY_ONLY else _commit(r, cur.T)
+    say(f'conv sweep {i}: B={B} C={C} K={K} io={io} mode={mode} slots={use_slots} '
+        f'pending={pend} silu={silu} bias={bias} T={cur.T}')
+    S0 = np64(c['state'])
+    pending = None
+    if pend:
+        prev = wl.make_batch(w, 10250 + i, DEV, k_override=_ks(r, B, kmax))
+        cp = wl.make_conv_layer(w, prev, 10270 + i, DEV, num_slots=ns, bias=bias, C=C)
+        pcommit = _commit(r, prev.T)
+        pending = bd.make_conv_pending(sv_batch(prev), cp['x'], pcommit)
+        _, S0 = oracle.conv_step(S0, None if slots is None else npi(slots), np64(cp['x']),
+                                 np64(c['weight']), None if c['bias'] is None else np64(c['bias']),
+                                 npi(prev.cu_seqlens), npi(pcommit), oracle.GDN_COMMIT_ONLY,
+                                 silu=silu)
+    st = c['state'].clone()
+    out = torch.full_like(c['x'], float('nan'))
+    err = err_word()
+    bd.short_conv_verify_commit(sv_batch(cur), mode, st, c['x'], c['weight'], c['bias'], commit,
+                                out, state_slot=slots,
+                                activation=bd.SV_ACT_SILU if silu else bd.SV_ACT_NONE,
+                                pending=pending, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    y, S = oracle.conv_step(S0, None if slots is None else npi(slots), np64(c['x']),
+                            np64(c['weight']), None if c['bias'] is None else np64(c['bias']),
+                            npi(cur.cu_seqlens), None if commit is None else npi(commit),
+                            ORACLE_MODE[mode], silu=silu)
+    assert np.array_equal(bits(st), bits(torch.from_numpy(S).to(st.dtype)))
+    e = 0.0
+    if mode != bd.SV_GDN_COMMIT_ONLY:
+        e = check_gdn_out(np64(out), y, io)
+    say(f'  max abs err {e:.2e}')
+
+
+@pytest.mark.parametrize('i', range(N_ACC))
+def test_accept_sweep(i):
+    r = random.Random(10500 + i)
+    B = r.randint(1, 20)
+    V = r.choice([2, 3, 7, 100, 1000, 4095, 4096, 4097, 10007, 65537, 151936])
+    ldt = r.choice([torch.float32, torch.bfloat16])
+    mode = (bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION)[i % 2]
+    point_mass = mode == bd.SV_ACCEPT_REJECTION and r.random() < 0.4
+    with_bonus = r.random() < 0.3
+    kmax = r.randint(0, 7)
+    w = wl.Workload('sweep', B=B, k=kmax, ragged_k=False, ctx=(0, 3000), V=V, logit_dtype=ldt)
+    batch = wl.make_batch(w, 10600 + i, DEV, k_override=_ks(r, B, kmax))
+    a = wl.make_accept(w, batch, 10700 + i, 'greedy' if mode == bd.SV_ACCEPT_GREEDY
+                       else 'rejection', DEV)
+    if point_mass:
+        a['draft_logits'] = None
+    bonus = (torch.tensor([r.randrange(V) for _ in range(B)], dtype=torch.int32, device=DEV)
+             if with_bonus else None)
+    say(f'accept sweep {i}: B={B} V={V} {ldt} mode={mode} point_mass={point_mass} '
+        f'bonus={with_bonus} T={batch.T}')
+    mT = batch.max_T
+    result = torch.full((B * (1 + mT),), -7, dtype=torch.int32, device=DEV)
+    commit = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    ctx = batch.ctx_lens.clone()
+    ws = torch.empty(bd.spec_accept_workspace_bytes(B, batch.total_T, V, mode),
+                     dtype=torch.uint8, device=DEV)
+    err = err_word()
+    bd.spec_accept(sv_batch(batch), mode, a['target_logits'], a['draft_tokens'], result,
+                   draft_logits=a.get('draft_logits'), u_accept=a.get('u_accept'),
+                   u_final=a.get('u_final'), commit_len_out=commit, ctx_lens_inout=ctx,
+                   workspace=ws, err=err, bonus_tokens=bonus)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    res = npi(result)
+    acc, out = res[:B], res[B:].reshape(B, mT)
+    cu = npi(batch.cu_seqlens)
+    bn = None if bonus is None else npi(bonus)
+    if mode == bd.SV_ACCEPT_GREEDY:
+        acc_r, out_r = oracle.greedy_accept(np64(a['target_logits']), npi(a['draft_tokens']), cu,
+                                            mT, bonus_tokens=bn)
+    else:
+        dl = a['draft_logits']
+        acc_r, out_r = oracle.rejection_accept(
+            np64(a['target_logits']), None if dl is None else np64(dl), npi(a['draft_tokens']),
+            np64(a['u_accept']), np64(a['u_final']), cu, mT, bonus_tokens=bn)
+    np.testing.assert_array_equal(acc, acc_r)
+    np.testing.assert_array_equal(out, out_r)
+    np.testing.assert_array_equal(npi(commit), acc_r + 1)
+    np.testing.assert_array_equal(npi(ctx), np.array(batch.ctx) + acc_r + 1)
+    say(f'  accepted {acc_r.tolist()}')

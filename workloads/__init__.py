@@ -252,11 +252,12 @@ def make_gdn_layer(w: Workload, batch: Batch, seed: int, device='cpu',
 
 
 def make_conv_layer(w: Workload, batch: Batch, seed: int, device='cpu',
-                    num_slots=None, bias=True):
+                    num_slots=None, bias=True, C=None):
     """Short-convolution inputs: rolling state and inputs ~N(0, 1) in the GDN
-    I/O dtype, taps ~N(0, 1/K) and bias ~N(0, 0.1) in fp32."""
+    I/O dtype, taps ~N(0, 1/K) and bias ~N(0, 0.1) in fp32.  ``C`` overrides
+    the channel count (default: the layer's q, k and v features)."""
     g = generator(seed, device)
-    Tt, C, K = batch.total_T, w.conv_C, w.conv_K
+    Tt, C, K = batch.total_T, (w.conv_C if C is None else C), w.conv_K
     ns = batch.B if num_slots is None else num_slots
     state = torch.randn((ns, K - 1, C), generator=g, device=device)
     x = torch.randn((Tt, C), generator=g, device=device)
