@@ -310,3 +310,213 @@ def test_accept_sweep(i):
     np.testing.assert_array_equal(npi(commit), acc_r + 1)
     np.testing.assert_array_equal(npi(ctx), np.array(batch.ctx) + acc_r + 1)
     say(f'  accepted {acc_r.tolist()}')
+
+
+N_STEP = 8
+
+
+def _step_batch(first, T, ctx):
+    """The batch of a later step: same sequences, table and pool, new T_b and
+    the contexts the previous step left."""
+    cu = torch.zeros(first.B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(T, dtype=torch.int32), 0)
+    return wl.Batch(B=first.B, max_T=first.max_T, T=list(T), ctx=list(ctx),
+                    cu_seqlens=cu.to(DEV),
+                    ctx_lens=torch.tensor(ctx, dtype=torch.int32, device=DEV),
+                    block_table=first.block_table, num_pages=first.num_pages, P=first.P)
+
+
+@pytest.mark.parametrize('i', range(N_STEP))
+def test_step_sweep(i):
+    """Three spec_verify_step calls in a row on the same pages, states and
+    convolution windows: random layer order, fp32 or bf16 I/O (bf16 with an
+    fp32 or fp16 state bank), either schedule (deferred: each step replays
+    the previous one's accepted tokens; flushed after the last), short
+    convolutions on or off, slot maps, greedy or rejection acceptance.  Every
+    step is compared with the oracle's step run on the oracle's own previous
+    results: acceptance, commit lengths, ctx_lens and pages bit for bit,
+    attention, GDN and convolution outputs within their bounds; states after
+    each two-phase step and after the deferred flush."""
+    r = random.Random(11000 + i)
+    B = r.randint(1, 10)
+    fam = ('f32', 'bf16', 'bf16')[i % 3]
+    f32 = fam == 'f32'
+    sdt = torch.float16 if not f32 and r.random() < 0.4 else torch.float32
+    pattern = [r.choice(['gdn', 'attn']) for _ in range(r.randint(1, 5))]
+    schedule = (bd.SV_SCHEDULE_TWO_PHASE, bd.SV_SCHEDULE_DEFERRED)[(i // 3) % 2]
+    conv = 'gdn' in pattern and r.random() < 0.5
+    K, silu = r.randint(2, 6), r.random() < 0.5
+    mode = (bd.SV_ACCEPT_GREEDY, bd.SV_ACCEPT_REJECTION)[i % 2]
+    use_slots = r.random() < 0.5
+    kmax = r.randint(1, 7)
+    Hkv = r.choice([1, 2, 4])
+    G = r.choice([g for g in (1, 2, 4, 8) if g * (kmax + 1) <= 64])
+    D = r.choice([32, 64, 128]) if f32 else r.choice([64, 128])
+    P = r.choice([16, 32, 64])
+    lo = r.choice([0, 30, 400])
+    w = wl.Workload('sweep_step', B=B, k=kmax, ragged_k=False, ctx=(lo, lo + r.choice([0, 90, 900])),
+                    P=P, Hq=G * Hkv, Hkv=Hkv, D=D,
+                    attn_dtype=torch.float32 if f32 else torch.bfloat16,
+                    H=r.randint(1, 3), dk=r.choice([64, 128]), dv=r.choice([64, 128]),
+                    gdn_dtype=torch.float32 if f32 else torch.bfloat16,
+                    V=r.choice([50, 1000, 4097]),
+                    logit_dtype=torch.float32 if f32 else torch.bfloat16,
+                    layers=pattern, conv_K=K, pool_factor=1.2)
+    n_steps = 3
+    first = wl.make_batch(w, 11100 + i, DEV, k_override=_ks(r, B, kmax), reserve=8 * n_steps)
+    first.max_T = kmax + 1  # the bound of every step
+    ns = B + (r.randint(0, 5) if use_slots else 0)
+    slots = wl.make_state_slots(first, ns, 11200 + i, DEV) if use_slots else None
+    say(f'step sweep {i}: B={B} {fam} state={sdt} layers={pattern} schedule={schedule} '
+        f'conv={conv} K={K} silu={silu} mode={mode} slots={use_slots} kmax={kmax} D={D} '
+        f'P={P} Hq={w.Hq} Hkv={Hkv} H={w.H} dk={w.dk} dv={w.dv} V={w.V}')
+    # persistent buffers: pools, state banks, conv windows and taps
+    pers = []
+    for li, kind in enumerate(pattern):
+        if kind == 'attn':
+            a0 = wl.make_attn_layer(w, first, 11300 + 10 * li + 1000 * i, DEV)
+            pers.append({'kind': 'attn', 'k_cache': a0['k_cache'], 'v_cache': a0['v_cache']})
+        else:
+            g0 = wl.make_gdn_layer(w, first, 11300 + 10 * li + 1000 * i, DEV, num_slots=ns,
+                                   state_dtype=sdt)
+            d = {'kind': 'gdn', 'state': g0['state']}
+            if conv:
+                c0 = wl.make_conv_layer(w, first, 11350 + 10 * li + 1000 * i, DEV, num_slots=ns)
+                d.update(conv_state=c0['state'], weight=c0['weight'], bias=c0['bias'])
+            pers.append(d)
+    # the oracle's own copies, advanced by the oracle
+    ora = [{k: (np64(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+           for p in pers]
+    dt_a = bd.SV_F32 if f32 else bd.SV_BF16
+    dt_g = bd.SV_F32 if f32 else bd.SV_BF16
+    sl_np = None if slots is None else npi(slots)
+    batch, prev = first, None
+    n_f16 = 0
+    for step in range(n_steps):
+        if step:
+            batch = _step_batch(first, [k + 1 for k in _ks(r, B, kmax)], ctx_next)
+        lays = []
+        for li, p in enumerate(pers):
+            seed = 12000 + 100 * step + 10 * li + 1000 * i
+            if p['kind'] == 'attn':
+                a = wl.make_attn_layer(w, batch, seed, DEV)
+                lay = {'kind': 'attn', 'q': a['q'], 'k_new': a['k_new'], 'v_new': a['v_new'],
+                       'out': torch.full_like(a['q'], float('nan'))}
+            else:
+                g = wl.make_gdn_layer(w, batch, seed, DEV, num_slots=ns)
+                lay = {'kind': 'gdn', **{k: g[k] for k in ('q', 'k', 'v', 'alpha', 'beta')},
+                       'out': torch.full_like(g['v'], float('nan'))}
+                if conv:
+                    c = wl.make_conv_layer(w, batch, seed + 5, DEV, num_slots=ns)
+                    lay['conv'] = {'state': p['conv_state'], 'x': c['x'], 'weight': p['weight'],
+                                   'bias': p['bias'], 'out': torch.full_like(c['x'], float('nan'))}
+            lays.append(lay)
+        acc = wl.make_accept(w, batch, 12900 + 100 * step + 1000 * i,
+                             'greedy' if mode == bd.SV_ACCEPT_GREEDY else 'rejection', DEV)
+        a_layers = [bd.attn_layer(l['q'], l['k_new'], l['v_new'], p['k_cache'], p['v_cache'],
+                                  l['out']) for l, p in zip(lays, pers) if l['kind'] == 'attn']
+        g_layers = [bd.gdn_layer(p['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'],
+                                 l['out'], conv=l.get('conv'))
+                    for l, p in zip(lays, pers) if l['kind'] == 'gdn']
+        args = bd.StepArgs(
+            [1 if l['kind'] == 'attn' else 0 for l in lays],
+            bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table, dt_a),
+            a_layers,
+            bd.gdn_config(w.H, w.dk, w.dv, ns, dt_g, state_slot=slots,
+                          state_dtype=bd.SV_F16 if sdt == torch.float16 else bd.SV_F32,
+                          conv_C=w.conv_C if conv else 0, conv_K=K if conv else 0,
+                          conv_activation=bd.SV_ACT_SILU if silu else bd.SV_ACT_NONE),
+            g_layers,
+            bd.accept_args(mode, acc['target_logits'], acc['draft_tokens'],
+                           acc.get('draft_logits'), acc.get('u_accept'), acc.get('u_final')))
+        sb = sv_batch(batch)
+        ws = torch.full((max(1, bd.spec_verify_step_workspace_bytes(sb, args)),), 0x7f,
+                        dtype=torch.uint8, device=DEV)
+        result = torch.full((B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
+        commit = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        ctx = batch.ctx_lens.clone()
+        err = err_word()
+        pend = None
+        if schedule == bd.SV_SCHEDULE_DEFERRED and prev is not None:
+            parr = (bd.SvGdnLayer * len(prev['args'].gdn))(*prev['args'].gdn)
+            pend = bd.SvStepPending(sv_batch(prev['batch']), parr, prev['commit'].data_ptr())
+        say(f'  step {step}: T={batch.T} ctx={batch.ctx}')
+        bd.spec_verify_step(sb, args, ctx, result, commit, schedule=schedule, pending=pend,
+                            workspace=ws, err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        # the oracle's step on its own previous results
+        olays = []
+        for l, o in zip(lays, ora):
+            if l['kind'] == 'attn':
+                olays.append({'kind': 'attn', 'q': np64(l['q']), 'k_new': np64(l['k_new']),
+                              'v_new': np64(l['v_new']), 'k_cache': o['k_cache'],
+                              'v_cache': o['v_cache']})
+            else:
+                d = {'kind': 'gdn', 'state': o['state'],
+                     **{k: np64(l[k]) for k in ('q', 'k', 'v', 'alpha', 'beta')}}
+                if conv:
+                    d['conv'] = {'state': o['conv_state'], 'x': np64(l['conv']['x']),
+                                 'weight': o['weight'],
+                                 'bias': None if o['bias'] is None else o['bias'],
+                                 'silu': silu}
+                olays.append(d)
+        ai = {'target_logits': np64(acc['target_logits']),
+              'draft_tokens': npi(acc['draft_tokens'])}
+        if mode == bd.SV_ACCEPT_REJECTION:
+            ai.update(draft_logits=np64(acc['draft_logits']), u_accept=np64(acc['u_accept']),
+                      u_final=np64(acc['u_final']))
+        ref = oracle.verify_step(olays, npi(batch.cu_seqlens), np.array(batch.ctx),
+                                 npi(batch.block_table), batch.P, batch.max_T,
+                                 'greedy' if mode == bd.SV_ACCEPT_GREEDY else 'rejection', ai,
+                                 state_slot=sl_np)
+        res = npi(result)
+        np.testing.assert_array_equal(res[:B], ref['accept_len'])
+        np.testing.assert_array_equal(res[B:].reshape(B, batch.max_T), ref['out_tokens'])
+        np.testing.assert_array_equal(npi(commit), ref['commit_len'])
+        np.testing.assert_array_equal(npi(ctx), ref['ctx_lens'])
+        n_f16 += 1
+        for li, (l, p, o) in enumerate(zip(lays, pers, ora)):
+            if l['kind'] == 'attn':
+                check_attn_out(np64(l['out']), ref['outputs'][li], w.attn_dtype)
+                o['k_cache'], o['v_cache'] = ref['k_cache'][li], ref['v_cache'][li]
+                for key in ('k_cache', 'v_cache'):
+                    exp = torch.from_numpy(o[key]).to(p[key].dtype)
+                    assert np.array_equal(bits(p[key]), bits(exp)), key
+            else:
+                check_gdn_out(np64(l['out']), ref['outputs'][li], w.gdn_dtype)
+                S = ref['state'][li]
+                if sdt == torch.float16:   # stored once per step, continued from
+                    S = S.astype(np.float16).astype(np.float64)
+                o['state'] = S
+                if conv:
+                    check_gdn_out(np64(l['conv']['out']), ref['conv_outputs'][li], w.gdn_dtype)
+                    o['conv_state'] = ref['conv_state'][li]
+        if schedule == bd.SV_SCHEDULE_TWO_PHASE or step == n_steps - 1:
+            if schedule == bd.SV_SCHEDULE_DEFERRED:   # flush the last step's tokens
+                for l, p in zip(lays, pers):
+                    if l['kind'] != 'gdn':
+                        continue
+                    bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, p['state'], l['q'], l['k'],
+                                         l['v'], l['alpha'], l['beta'], commit, l['out'],
+                                         state_slot=slots)
+                    if conv:
+                        bd.short_conv_verify_commit(
+                            sb, bd.SV_GDN_COMMIT_ONLY, p['conv_state'], l['conv']['x'],
+                            p['weight'], p['bias'], commit, l['conv']['out'], state_slot=slots,
+                            activation=bd.SV_ACT_SILU if silu else bd.SV_ACT_NONE)
+                torch.cuda.synchronize()
+            # fp16 storage: each step's store may round across a midpoint the
+            # oracle's fp64 value did not (one fp16 ulp, 2^-10 of the element)
+            tol = (GDN_STATE_TOL_F16 + n_f16 * 2.0 ** -10 * (1 + GDN_STATE_TOL)
+                   if sdt == torch.float16 else GDN_STATE_TOL)
+            for p, o in zip(pers, ora):
+                if p['kind'] != 'gdn':
+                    continue
+                check_gdn_state(np64(p['state']), o['state'], tol=tol)
+                if conv:
+                    exp = torch.from_numpy(o['conv_state']).to(p['conv_state'].dtype)
+                    assert np.array_equal(bits(p['conv_state']), bits(exp))
+        # the pending replay of the next step reads these tensors: keep them
+        prev = {'args': args, 'batch': batch, 'commit': commit, 'lays': lays}
+        ctx_next = list(ref['ctx_lens'])
