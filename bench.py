@@ -584,11 +584,7 @@ def run_step_workload(w, args, dev, ceil):
 
     def flush():
         if deferred and state['n'] > 0:
-            last = commits[(state['n'] - 1) % 2]
-            for l in layers:
-                if l['kind'] == 'gdn':
-                    bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, l['state'], l['q'], l['k'],
-                                         l['v'], l['alpha'], l['beta'], last, l['out'])
+            bd.spec_verify_flush(step_args, pends[(state['n'] - 1) % 2], err=err)
             state['n'] = 0
 
     for _ in range(warmup):
@@ -798,15 +794,7 @@ def step_with_conv_timing(w, batch, layers, acc, amode, sb, ws, ctx, err, steps,
 
     def flush():
         if deferred and st['n'] > 0:
-            last = commits[(st['n'] - 1) % 2]
-            for i, l in enumerate(layers):
-                if l['kind'] == 'gdn':
-                    bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, l['state'], l['q'], l['k'],
-                                         l['v'], l['alpha'], l['beta'], last, l['out'])
-                    c = convs[i]
-                    bd.short_conv_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, c['state'], c['x'],
-                                                c['weight'], c['bias'], last, c['out'],
-                                                activation=bd.SV_ACT_SILU)
+            bd.spec_verify_flush(args, pends[(st['n'] - 1) % 2], err=err)
             st['n'] = 0
 
     for _ in range(warmup):

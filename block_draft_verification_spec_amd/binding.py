@@ -137,6 +137,9 @@ _SIGS = {
          ctypes.POINTER(SvGdnConfig), ctypes.POINTER(SvGdnLayer),
          ctypes.POINTER(SvAcceptArgs), _vp, _vp, _vp, ctypes.c_int,
          ctypes.POINTER(SvStepPending), _vp, _sz, _vp, _vp], ctypes.c_int),
+    'spec_verify_flush': (
+        [_c_i32, ctypes.POINTER(SvGdnConfig), ctypes.POINTER(SvStepPending), _vp, _vp],
+        ctypes.c_int),
 }
 
 _lib = None
@@ -508,3 +511,22 @@ def spec_verify_step(batch, step_args, ctx_lens, result, commit_len,
         _i32(commit_len, 'commit_len'), int(schedule),
         ctypes.byref(pending) if pending is not None else None,
         _ptr(workspace), ws_n, _i32(err, 'err'), _stream(stream)))
+
+
+def step_pending(batch, step_args, commit_len):
+    """The deferred schedule's pending tokens (``sv_step_pending``): the GDN
+    layers of a step that ran with ``step_args`` on ``batch``, and the commit
+    lengths it returned.  The structure keeps ``step_args`` alive."""
+    p = SvStepPending(batch, step_args.gdn, _i32(commit_len, 'commit_len'))
+    p.keep = step_args
+    return p
+
+
+def spec_verify_flush(step_args, pending, err=None, stream=None):
+    """Commit the pending tokens of every GDN layer (``spec_verify_flush``):
+    ``step_args`` gives the GDN configuration and layer count."""
+    a = step_args
+    n_gdn = sum(1 for k in a.layer_kind if k == 0)
+    _check(lib().spec_verify_flush(
+        n_gdn, ctypes.byref(a.gdn_cfg) if a.gdn_cfg is not None else None,
+        ctypes.byref(pending), _i32(err, 'err'), _stream(stream)))

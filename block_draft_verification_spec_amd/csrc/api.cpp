@@ -553,6 +553,42 @@ sv::ConvArgs step_conv_args(const sv_batch* batch, const sv_gdn_config* g, int m
   return a;
 }
 
+// COMMIT_ONLY of the first commit_len[b] tokens of every layer (and its short
+// convolution when gcfg->conv_C > 0) in batched launches; arguments checked.
+sv_status commit_layers(const sv_batch* batch, const sv_gdn_config* gcfg,
+                        const sv_gdn_layer* layers, int n_gdn, const int32_t* commit_len,
+                        int32_t* err, hipStream_t stream, const char* who) {
+  sv::GdnScalars s{};
+  s.B = batch->B;
+  s.total_T = batch->total_T;
+  s.max_T = batch->max_T;
+  s.cu = batch->cu_seqlens;
+  s.mode = SV_GDN_COMMIT_ONLY;
+  s.state_slot = gcfg->state_slot;
+  s.num_slots = gcfg->num_slots;
+  s.commit_len = commit_len;
+  s.H = gcfg->H;
+  s.dk = gcfg->dk;
+  s.dv = gcfg->dv;
+  s.err = err;
+  for (int l0 = 0; l0 < n_gdn; l0 += sv::kGdnLayersPerLaunch) {
+    const int nl = std::min(sv::kGdnLayersPerLaunch, n_gdn - l0);
+    sv::GdnCommitTable t{};
+    for (int i = 0; i < nl; ++i) {
+      const sv_gdn_layer& G = layers[l0 + i];
+      t.l[i] = sv::GdnCommitPtrs{G.state, G.k, G.v, G.alpha, G.beta};
+      t.c[i] = sv::ConvCommitPtrs{G.conv_state, G.conv_x};
+    }
+    const sv::ConvArgs c = step_conv_args(batch, gcfg, SV_GDN_COMMIT_ONLY, commit_len, err);
+    const sv_status st =
+        hip_status(sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, gcfg->state_dtype, stream,
+                                               gcfg->conv_C > 0 ? &c : nullptr),
+                   who);
+    if (st != SV_OK) return st;
+  }
+  return SV_OK;
+}
+
 }  // namespace
 
 sv_status gdn_verify_checkpoint(const sv_batch* batch, const void* state, sv_dtype state_dtype,
@@ -912,35 +948,40 @@ sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers, const uint8_
   // 3. two-phase: commit the first a+1 tokens of every GDN layer
   // (every layer's state, k, v and gates were checked in step 0)
   if (schedule == SV_SCHEDULE_TWO_PHASE && n_gdn > 0) {
-    sv::GdnScalars s{};
-    s.B = batch->B;
-    s.total_T = batch->total_T;
-    s.max_T = batch->max_T;
-    s.cu = batch->cu_seqlens;
-    s.mode = SV_GDN_COMMIT_ONLY;
-    s.state_slot = gcfg->state_slot;
-    s.num_slots = gcfg->num_slots;
-    s.commit_len = commit_len;
-    s.H = gcfg->H;
-    s.dk = gcfg->dk;
-    s.dv = gcfg->dv;
-    s.err = err;
-    for (int l0 = 0; l0 < n_gdn; l0 += sv::kGdnLayersPerLaunch) {
-      const int nl = std::min(sv::kGdnLayersPerLaunch, n_gdn - l0);
-      sv::GdnCommitTable t{};
-      for (int i = 0; i < nl; ++i) {
-        const sv_gdn_layer& G = gdn[l0 + i];
-        t.l[i] = sv::GdnCommitPtrs{G.state, G.k, G.v, G.alpha, G.beta};
-        t.c[i] = sv::ConvCommitPtrs{G.conv_state, G.conv_x};
-      }
-      const sv::ConvArgs c = step_conv_args(batch, gcfg, SV_GDN_COMMIT_ONLY, commit_len, err);
-      st = hip_status(sv::launch_gdn_commit_multi(s, t, nl, gcfg->io_dtype, gcfg->state_dtype,
-                                                  stream, gcfg->conv_C > 0 ? &c : nullptr),
-                      who);
-      if (st != SV_OK) return st;
-    }
+    st = commit_layers(batch, gcfg, gdn, n_gdn, commit_len, err, stream, who);
+    if (st != SV_OK) return st;
   }
   return ok();
+}
+
+sv_status spec_verify_flush(int32_t n_gdn, const sv_gdn_config* gcfg,
+                            const sv_step_pending* pending, int32_t* err, hipStream_t stream) {
+  const char* who = "spec_verify_flush";
+  if (n_gdn < 0) return fail(SV_EINVAL, "%s: n_gdn must be >= 0 (got %d)", who, n_gdn);
+  if (!pending) return fail(SV_EINVAL, "%s: pending is required", who);
+  if (n_gdn == 0) return ok();
+  if (!gcfg || !pending->layers || !pending->commit_len)
+    return fail(SV_EINVAL, "%s: gdn config, pending layers and commit_len are required", who);
+  const sv_batch* batch = &pending->batch;
+  // every layer is checked before the first launch
+  char what[64];
+  for (int l = 0; l < n_gdn; ++l) {
+    std::snprintf(what, sizeof(what), "%s: layer %d", who, l);
+    const sv_gdn_layer& G = pending->layers[l];
+    sv_status st = check_gdn_call(batch, SV_GDN_COMMIT_ONLY, G.state, gcfg->state_dtype,
+                                  gcfg->state_slot, gcfg->num_slots, nullptr, G.k, G.v,
+                                  gcfg->io_dtype, G.alpha, G.beta, pending->commit_len,
+                                  nullptr, gcfg->H, gcfg->dk, gcfg->dv, nullptr, what);
+    if (st != SV_OK) return st;
+    if (gcfg->conv_C > 0) {
+      if (gcfg->conv_K < 2 || gcfg->conv_K > 8)
+        return fail(SV_EINVAL, "%s: conv_K must be in 2..8 (got %d)", what, gcfg->conv_K);
+      if (!G.conv_state || !G.conv_x)
+        return fail(SV_EINVAL, "%s: conv_state and conv_x are required", what);
+    }
+  }
+  return commit_layers(batch, gcfg, pending->layers, n_gdn, pending->commit_len, err, stream,
+                       who);
 }
 
 }  // extern "C"

@@ -378,9 +378,8 @@ SV_API sv_status short_conv_commit_prefix(const sv_batch* batch,
  *   2. spec_accept -> result, commit_len = accept_len + 1;
  *   3. two-phase schedule: one launch applies the first commit_len tokens of
  *      every GDN layer (and its convolution) and stores the states (deferred
- *      schedule: nothing, the next step's verify pass does it; call
- *      gdn_verify_commit and short_conv_verify_commit in COMMIT_ONLY mode on
- *      the pending tokens to flush);
+ *      schedule: nothing, the next step's verify pass does it, or
+ *      spec_verify_flush);
  *   4. ctx_lens += commit_len.
  * Attention layers share block_table / ctx_lens; GDN layers share
  * state_slot.  `layer_kind` (host) holds 0 = GDN, 1 = attention, in model
@@ -449,6 +448,26 @@ SV_API sv_status spec_verify_step(const sv_batch* batch, int32_t n_layers,
     const sv_accept_args* acc, int32_t* ctx_lens, int32_t* result,
     int32_t* commit_len, sv_schedule schedule, const sv_step_pending* pending,
     void* workspace, size_t workspace_bytes, int32_t* err, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Flush of the deferred schedule: the commit the next step's verify pass
+ * would have done, without a next step (the state of a sequence that
+ * leaves, or every state before it is read).  For each of the n_gdn layers
+ * of `pending` (their state, k, v, alpha, beta and, with gcfg->conv_C > 0,
+ * conv_state and conv_x are read; gcfg as given to the step), the first
+ * pending->commit_len[b] tokens of sequence b are applied to its state (and
+ * convolution window) and the result is stored: the stored state is the one
+ * the two-phase schedule would have left (onnxruntime-genai #2457:
+ * CommitPrefix of the accepted prefix; lmdeploy #5019 "Two fixes" item 2:
+ * the commit runs after acceptance).  The layers are committed in batched
+ * launches, as the two-phase step commits; no workspace.  Every argument of
+ * every layer is checked before the first launch.  Device errors as for
+ * gdn_verify_commit (a bad commit length, T_b or slot skips the sequence).
+ * Calling it twice applies the tokens twice: a flushed `pending` must not
+ * be passed to a later step.
+ * ------------------------------------------------------------------------ */
+SV_API sv_status spec_verify_flush(int32_t n_gdn, const sv_gdn_config* gcfg,
+    const sv_step_pending* pending, int32_t* err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Sizing and errors.

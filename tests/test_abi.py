@@ -271,6 +271,48 @@ def test_step_checks_every_layer_before_any_launch(bad, layer):
     assert layer in L.sv_last_error().decode()
 
 
+def _flush(L, n=3, bad_layer=None, bad=None, conv_C=0, pending=True, commit=16):
+    """spec_verify_flush over n GDN layers with fake aligned pointers; layer
+    bad_layer gets the fields in `bad`."""
+    gcfg = bd.SvGdnConfig(4, 128, 128, 2, None, bd.SV_BF16, bd.SV_F32, conv_C, 4, 0)
+    layers = []
+    for i in range(n):
+        f = dict(state=16, q=None, k=16, v=16, alpha=16, beta=16, out=None,
+                 conv_state=16, conv_x=16)
+        if i == bad_layer:
+            f.update(bad)
+        layers.append(bd.SvGdnLayer(f['state'], f['q'], f['k'], f['v'], f['alpha'],
+                                    f['beta'], f['out'], f['conv_state'], f['conv_x']))
+    arr = (bd.SvGdnLayer * max(1, n))(*layers)
+    p = bd.SvStepPending(_batch(), arr, commit)
+    return L.spec_verify_flush(n, ctypes.byref(gcfg), ctypes.byref(p) if pending else None,
+                               None, None)
+
+
+@pytest.mark.parametrize('kw,msg', [
+    (dict(n=-1), 'n_gdn'),
+    (dict(pending=False), 'pending is required'),
+    (dict(commit=None), 'commit_len'),
+    (dict(bad_layer=2, bad=dict(k=24)), 'layer 2'),          # misaligned k, last layer
+    (dict(bad_layer=2, bad=dict(alpha=None)), 'layer 2'),
+    (dict(bad_layer=1, bad=dict(state=None)), 'layer 1'),
+    (dict(bad_layer=2, bad=dict(conv_x=None), conv_C=64), 'layer 2'),
+])
+def test_flush_validation(kw, msg):
+    """Refusals come before the first launch: on a host without a GPU a
+    launch would return SV_EHIP, so a refusal of the last layer shows that
+    no earlier layer was committed."""
+    L = bd.lib()
+    st = _flush(L, **kw)
+    assert st == bd.SV_EINVAL, L.sv_last_error().decode()
+    assert msg in L.sv_last_error().decode()
+
+
+def test_flush_of_no_layers_is_a_no_op():
+    L = bd.lib()
+    assert _flush(L, n=0) == bd.SV_OK
+
+
 def test_device_error_calls_validate():
     L = bd.lib()
     assert L.sv_read_device_error(None, None) == -1

@@ -487,3 +487,112 @@ def test_step_with_short_conv(schedule, K, act):
                                           npi(batch.block_table), npi(batch.ctx_lens) + c1, cu,
                                           batch.P)
             check_attn_out(np64(l['out']), ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.float16])
+def test_flush_equals_per_layer_commits_and_two_phase(state_dtype):
+    """spec_verify_flush after a deferred step stores, bit for bit, what
+    per-layer COMMIT_ONLY calls on the same pending tokens store, and what the
+    two-phase step stores, for the GDN states and the short-convolution
+    windows (slot map, fp32 or fp16 state bank)."""
+    w = wl.WORKLOADS[3]
+    w = wl.Workload(**{**w.__dict__, 'B': 8, 'layers': wl._hybrid(1), 'H': 4})
+    batch = wl.make_batch(w, 41, DEV)
+    ns = batch.B + 3
+    slots = wl.make_state_slots(batch, ns, 42, DEV)
+    layers = []
+    for i, kind in enumerate(w.layers):
+        if kind == 'attn':
+            lay = wl.make_attn_layer(w, batch, 4300 + 10 * i, DEV)
+            lay['out'] = torch.full_like(lay['q'], float('nan'))
+        else:
+            lay = wl.make_gdn_layer(w, batch, 4300 + 10 * i, DEV, num_slots=ns,
+                                    state_dtype=state_dtype)
+            lay['out'] = torch.full_like(lay['v'], float('nan'))
+            c = wl.make_conv_layer(w, batch, 4350 + 10 * i, DEV, num_slots=ns)
+            c['out'] = torch.full_like(c['x'], float('nan'))
+            lay['conv'] = c
+        lay['kind'] = kind
+        layers.append(lay)
+    acc = wl.make_accept(w, batch, 4399, 'rejection', DEV)
+    gdn = [l for l in layers if l['kind'] == 'gdn']
+    init = [(l['state'].clone(), l['conv']['state'].clone()) for l in gdn]
+    pools = [(l['k_cache'].clone(), l['v_cache'].clone()) for l in layers if l['kind'] == 'attn']
+    args = bd.StepArgs(
+        [1 if l['kind'] == 'attn' else 0 for l in layers],
+        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table,
+                       bd.SV_BF16),
+        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'])
+         for l in layers if l['kind'] == 'attn'],
+        bd.gdn_config(w.H, w.dk, w.dv, ns, bd.SV_BF16, state_slot=slots,
+                      state_dtype=bd.state_dtype(gdn[0]['state']), conv_C=w.conv_C,
+                      conv_K=w.conv_K, conv_activation=bd.SV_ACT_SILU),
+        [bd.gdn_layer(l['state'], l['q'], l['k'], l['v'], l['alpha'], l['beta'], l['out'],
+                      conv=l['conv']) for l in gdn],
+        bd.accept_args(bd.SV_ACCEPT_REJECTION, acc['target_logits'], acc['draft_tokens'],
+                       acc['draft_logits'], acc['u_accept'], acc['u_final']))
+    sb = sv_batch(batch)
+    ws = torch.zeros(bd.spec_verify_step_workspace_bytes(sb, args), dtype=torch.uint8,
+                     device=DEV)
+    err = err_word()
+
+    def step(schedule):
+        for l, (s0, c0) in zip(gdn, init):
+            l['state'].copy_(s0)
+            l['conv']['state'].copy_(c0)
+        ai = 0
+        for l in layers:
+            if l['kind'] == 'attn':
+                l['k_cache'].copy_(pools[ai][0])
+                l['v_cache'].copy_(pools[ai][1])
+                ai += 1
+        result = torch.full((batch.B * (1 + batch.max_T),), -7, dtype=torch.int32, device=DEV)
+        commit = torch.full((batch.B,), -7, dtype=torch.int32, device=DEV)
+        ctx = batch.ctx_lens.clone()
+        bd.spec_verify_step(sb, args, ctx, result, commit, schedule=schedule, workspace=ws,
+                            err=err)
+        return commit
+
+    say('flush: deferred step, then spec_verify_flush')
+    commit = step(bd.SV_SCHEDULE_DEFERRED)
+    torch.cuda.synchronize()
+    for l, (s0, c0) in zip(gdn, init):   # the deferred step stores nothing
+        assert torch.equal(l['state'], s0) and torch.equal(l['conv']['state'], c0)
+    bd.spec_verify_flush(args, bd.step_pending(sb, args, commit), err=err)
+    torch.cuda.synchronize()
+    flushed = [(l['state'].clone(), l['conv']['state'].clone()) for l in gdn]
+
+    say('flush: the same step, then per-layer COMMIT_ONLY calls')
+    commit2 = step(bd.SV_SCHEDULE_DEFERRED)
+    for l in gdn:
+        bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, l['state'], l['q'], l['k'], l['v'],
+                             l['alpha'], l['beta'], commit2, l['out'], state_slot=slots)
+        c = l['conv']
+        bd.short_conv_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, c['state'], c['x'], c['weight'],
+                                    c['bias'], commit2, c['out'], state_slot=slots,
+                                    activation=bd.SV_ACT_SILU)
+    torch.cuda.synchronize()
+    assert torch.equal(commit, commit2)
+    for l, (s1, c1) in zip(gdn, flushed):
+        assert torch.equal(l['state'], s1)
+        assert torch.equal(l['conv']['state'], c1)
+
+    say('flush: the two-phase step')
+    step(bd.SV_SCHEDULE_TWO_PHASE)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for l, (s1, c1) in zip(gdn, flushed):
+        assert torch.equal(l['state'], s1)
+        assert torch.equal(l['conv']['state'], c1)
+    # and against the oracle (one commit of the accepted prefix)
+    cu = npi(batch.cu_seqlens)
+    for l, (s0, c0), (s1, c1) in zip(gdn, init, flushed):
+        _, S = oracle.gdn_step(np64(s0), npi(slots), None, np64(l['k']), np64(l['v']),
+                               np64(l['alpha']), np64(l['beta']), cu, npi(commit),
+                               oracle.GDN_COMMIT_ONLY)
+        check_gdn_state(np64(s1), S, tol=GDN_STATE_TOL if state_dtype == torch.float32
+                        else GDN_STATE_TOL_F16)
+        _, CS = oracle.conv_step(np64(c0), npi(slots), np64(l['conv']['x']),
+                                 np64(l['conv']['weight']), np64(l['conv']['bias']), cu,
+                                 npi(commit), oracle.CONV_COMMIT_ONLY)
+        assert np.array_equal(bits(c1), bits_of(CS, c1))

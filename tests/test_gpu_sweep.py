@@ -336,7 +336,7 @@ def test_step_sweep(i):
     step is compared with the oracle's step run on the oracle's own previous
     results: acceptance, commit lengths, ctx_lens and pages bit for bit,
     attention, GDN and convolution outputs within their bounds; states after
-    each two-phase step and after the deferred flush."""
+    each two-phase step and after the deferred schedule's spec_verify_flush."""
     r = random.Random(11000 + i)
     B = r.randint(1, 10)
     fam = ('f32', 'bf16', 'bf16')[i % 3]
@@ -494,18 +494,9 @@ def test_step_sweep(i):
                     o['conv_state'] = ref['conv_state'][li]
         if schedule == bd.SV_SCHEDULE_TWO_PHASE or step == n_steps - 1:
             if schedule == bd.SV_SCHEDULE_DEFERRED:   # flush the last step's tokens
-                for l, p in zip(lays, pers):
-                    if l['kind'] != 'gdn':
-                        continue
-                    bd.gdn_verify_commit(sb, bd.SV_GDN_COMMIT_ONLY, p['state'], l['q'], l['k'],
-                                         l['v'], l['alpha'], l['beta'], commit, l['out'],
-                                         state_slot=slots)
-                    if conv:
-                        bd.short_conv_verify_commit(
-                            sb, bd.SV_GDN_COMMIT_ONLY, p['conv_state'], l['conv']['x'],
-                            p['weight'], p['bias'], commit, l['conv']['out'], state_slot=slots,
-                            activation=bd.SV_ACT_SILU if silu else bd.SV_ACT_NONE)
+                bd.spec_verify_flush(args, bd.step_pending(sb, args, commit), err=err)
                 torch.cuda.synchronize()
+                assert int(err.item()) == 0
             # fp16 storage: each step's store may round across a midpoint the
             # oracle's fp64 value did not (one fp16 ulp, 2^-10 of the element)
             tol = (GDN_STATE_TOL_F16 + n_f16 * 2.0 ** -10 * (1 + GDN_STATE_TOL)
