@@ -32,6 +32,11 @@
 // stored state is g S' and storing never changes the registers, so outputs
 // do not depend on where (or whether) the state is stored.
 
+#include <map>
+#include <mutex>
+#include <type_traits>
+#include <utility>
+
 #include "conv_block.h"
 #include "device_common.h"
 #include "internal.h"
@@ -530,6 +535,61 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GdnScalars s, GdnFul
                                      rb == 0 && h == 0);
 }
 
+// Resident blocks per CU of the dk = 128 launches over an fp32 state bank.
+// Registers and LDS admit eight; measured on MI355X (32 heads, dk = dv =
+// 128; 64 sequences with 4 verify tokens, 256 with 2 to 8), holding a CU to
+// five by padding each block's LDS makes a layer 1.5-2 % faster in verify +
+// commit and 2-4 % faster in the deferred replay + verify (four: the same;
+// three: 7-20 % slower).  With eight, the resident blocks load, compute and
+// store in step, and the state traffic pauses while they compute.  An fp16
+// bank is bound by its VALU work instead and runs 9 % slower at five, so it
+// keeps eight.
+constexpr int kGdnBlocksPerCU = 5;
+
+// Dynamic LDS that leaves at most kGdnBlocksPerCU blocks of `kernel` (static
+// LDS `fixed` bytes, 256 threads) on a CU of the current device, checked
+// with the occupancy query; 0 if the device does not report its LDS size.
+size_t gdn_lds_pad(const void* kernel, size_t fixed) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int lds = 0, per_block = 0;
+  size_t pad = 0;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+          hipSuccess &&
+      hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+          hipSuccess &&
+      lds > 0 && per_block > 0) {
+    const size_t share = static_cast<size_t>(lds) / kGdnBlocksPerCU;
+    const size_t cap = static_cast<size_t>(per_block);
+    pad = share > fixed ? ((std::min(share, cap) - fixed) & ~size_t(255)) : 0;
+    // the allocation granule may fit one block more or fewer: step the pad
+    // until the occupancy query agrees (bounded)
+    for (int k = 0; k < 64; ++k) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, pad) != hipSuccess)
+        break;
+      if (n > kGdnBlocksPerCU && fixed + pad + 256 <= cap) pad += 256;
+      else if (n < kGdnBlocksPerCU && pad >= 256) pad -= 256;
+      else break;
+    }
+  }
+  cache[key] = pad;
+  return pad;
+}
+
+template <typename ST, typename K>
+size_t pad_for(K* kernel, int dk) {
+  return dk == 128 && std::is_same<ST, float>::value
+             ? gdn_lds_pad(reinterpret_cast<const void*>(kernel), sizeof(GdnSmem<128>))
+             : 0;
+}
+
 template <typename IO, typename ST>
 void launch_gdn_t(const GdnScalars& s, const GdnFullPtrs& p, hipStream_t stream) {
   const dim3 grid(s.dv / kRowsPerBlock, s.H, s.B);
@@ -540,7 +600,8 @@ void launch_gdn_t(const GdnScalars& s, const GdnFullPtrs& p, hipStream_t stream)
       hipLaunchKernelGGL((gdn_kernel<IO, ST, 64, true>), grid, dim3(kThreads), 0, stream, s, p);
   } else {
     if (s.dk == 128)
-      hipLaunchKernelGGL((gdn_kernel<IO, ST, 128, false>), grid, dim3(kThreads), 0, stream, s, p);
+      hipLaunchKernelGGL((gdn_kernel<IO, ST, 128, false>), grid, dim3(kThreads),
+                         pad_for<ST>(&gdn_kernel<IO, ST, 128, false>, 128), stream, s, p);
     else
       hipLaunchKernelGGL((gdn_kernel<IO, ST, 64, false>), grid, dim3(kThreads), 0, stream, s, p);
   }
@@ -564,15 +625,17 @@ void launch_commit_t(const GdnScalars& s, const GdnCommitTable& t, int n_layers,
   const dim3 grid(n_gdn + n_conv);
   if (conv) {
     if (s.dk == 128)
-      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128, true>), grid, dim3(kThreads), 0,
-                         stream, s, t, c, n_gdn);
+      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128, true>), grid, dim3(kThreads),
+                         pad_for<ST>(&gdn_commit_multi_kernel<IO, ST, 128, true>, 128), stream, s, t,
+                         c, n_gdn);
     else
       hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 64, true>), grid, dim3(kThreads), 0,
                          stream, s, t, c, n_gdn);
   } else {
     if (s.dk == 128)
-      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128, false>), grid, dim3(kThreads), 0,
-                         stream, s, t, c, n_gdn);
+      hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 128, false>), grid, dim3(kThreads),
+                         pad_for<ST>(&gdn_commit_multi_kernel<IO, ST, 128, false>, 128), stream, s,
+                         t, c, n_gdn);
     else
       hipLaunchKernelGGL((gdn_commit_multi_kernel<IO, ST, 64, false>), grid, dim3(kThreads), 0,
                          stream, s, t, c, n_gdn);
@@ -586,8 +649,8 @@ void launch_gdn_conv_t(const GdnScalars& s, const GdnFullPtrs& p, const ConvArgs
   const int n_conv = (c.C + kConvThreads - 1) / kConvThreads * c.B;
   const dim3 grid(n_gdn + n_conv);
   if (s.dk == 128)
-    hipLaunchKernelGGL((gdn_conv_kernel<IO, ST, 128>), grid, dim3(kThreads), 0, stream, s, p, c,
-                       n_gdn);
+    hipLaunchKernelGGL((gdn_conv_kernel<IO, ST, 128>), grid, dim3(kThreads),
+                       pad_for<ST>(&gdn_conv_kernel<IO, ST, 128>, 128), stream, s, p, c, n_gdn);
   else
     hipLaunchKernelGGL((gdn_conv_kernel<IO, ST, 64>), grid, dim3(kThreads), 0, stream, s, p, c,
                        n_gdn);
