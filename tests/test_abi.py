@@ -32,6 +32,31 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def test_header_compiles_as_c_and_links():
+    """include/spec_verify.h is plain C: a C99 program compiles against it,
+    links against the library and gets host-side answers (no GPU work)."""
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which('gcc')
+    hip_inc = '/opt/rocm/include'
+    if gcc is None or not os.path.isdir(hip_inc):
+        pytest.skip('gcc or the HIP headers are not installed')
+    lib_dir = os.path.dirname(bd.LIB_PATH)
+    with tempfile.TemporaryDirectory() as tmp:
+        exe = os.path.join(tmp, 'c_abi_check')
+        r = subprocess.run([gcc, '-std=c99', '-Wall', '-Werror=implicit-function-declaration',
+                            '-D__HIP_PLATFORM_AMD__', '-I', hip_inc, '-I',
+                            os.path.join(ROOT, 'include'),
+                            os.path.join(ROOT, 'tests', 'c_abi_check.c'), '-L', lib_dir,
+                            '-lspecverify', '-Wl,-rpath,' + lib_dir, '-o', exe],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+        assert run.returncode == 0, run.stdout + run.stderr
+        assert 'gfx950' in run.stdout
+
+
 def test_version_and_empty_error():
     assert 'gfx950' in bd.version()
 
