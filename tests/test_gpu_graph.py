@@ -7,7 +7,8 @@ The step enqueues kernels only (no memset or copy nodes, nothing
 allocated), which is what makes it capturable.  Deferred schedule: one graph
 per commit buffer (step i reads the pending commit lengths step i - 1
 wrote), replayed alternately, so the recurrent states advance exactly once
-per replayed step.
+per replayed step; the flush of the last step's tokens (spec_verify_flush)
+replayed from a graph equals the eager flush.
 """
 
 import numpy as np
@@ -134,6 +135,20 @@ def test_graph_replays_equal_eager_steps(schedule):
         assert torch.isfinite(junk)
         _equal(ref[i], g.snapshot())
     assert int(g.err.item()) == 0
+    if deferred:  # the flush of the last step's tokens, eager and replayed from a graph
+        last = plan[-1][0]
+        bd.spec_verify_flush(eager.args, bd.step_pending(eager.sb, eager.args,
+                                                         eager.commits[last]), err=eager.err)
+        torch.cuda.synchronize()
+        ref_flush = eager.snapshot()
+        pend = bd.step_pending(g.sb, g.args, g.commits[last])
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg, capture_error_mode='thread_local'):
+            bd.spec_verify_flush(g.args, pend, err=g.err)
+        cg.replay()
+        torch.cuda.synchronize()
+        _equal(ref_flush, g.snapshot())
+        assert int(g.err.item()) == 0
 
 
 def test_graph_replay_matches_the_oracle():
