@@ -72,10 +72,6 @@ union U16x8 {
 
 // 16-bit element e (0..7, a compile-time constant after unrolling) of a
 // 16-byte vector, as the low half of a 32-bit value.
-__device__ __forceinline__ uint32_t half16(const uint4& u, int e) {
-  const uint32_t w = e < 2 ? u.x : (e < 4 ? u.y : (e < 6 ? u.z : u.w));
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
 __device__ __forceinline__ uint32_t half16(u32x4_t u, int e) {
   const uint32_t w = u[e >> 1];
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
