@@ -51,6 +51,10 @@ def parse():
     p.add_argument('--workload', type=int, default=3, help='index into workloads.WORKLOADS')
     p.add_argument('--accept', choices=['rejection', 'greedy'], default='rejection')
     p.add_argument('--schedule', choices=['deferred', 'two_phase'], default='deferred')
+    p.add_argument('--kv-format', choices=['bf16', 'int8'], default='bf16',
+                   help='page format of the step\'s attention layers (int8: per-channel codes)')
+    p.add_argument('--state-dtype', choices=['f32', 'f16'], default='f32',
+                   help='storage of the step\'s GDN state bank')
     p.add_argument('--no-cpu-baseline', action='store_true')
     p.add_argument('--no-graph', action='store_true', help='skip the graph-replay timing')
     p.add_argument('--no-next-rows', action='store_true',
@@ -225,11 +229,11 @@ def checkpoint_timing(w, batch, sb, commit, stream, dev, reps=10):
     return res
 
 
-def attn_kv8_bytes(w, batch):
+def attn_kv8_bytes(w, batch, ctx=None):
     """Algorithmic HBM bytes of one attention layer over INT8 pages: the
     cached codes, the in-flight bf16 rows and their codes, Q, O, the scales
-    and the block table."""
-    ctx = sum(batch.ctx)
+    and the block table (at the given contexts, default the batch's)."""
+    ctx = sum(batch.ctx if ctx is None else ctx)
     T = batch.total_T
     per_tok = w.Hq * w.D * 2 + 2 * w.Hkv * w.D * 2 + 2 * w.Hkv * w.D + w.Hq * w.D * 2
     return (ctx * w.Hkv * w.D * 2 + T * per_tok + 2 * w.Hkv * w.D * 4
@@ -264,7 +268,7 @@ def attn_kv8_timing(w, batch, sb, ctx, ws, stream, dev, n_layers=16, reps=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (reps * n_layers)
-    nbytes = attn_kv8_bytes(w, wl.Batch(**{**batch.__dict__, 'ctx': ctx.tolist()}))
+    nbytes = attn_kv8_bytes(w, batch, ctx.tolist())
     del layers
     return {'layer_ms': round(ms, 4), 'bytes': nbytes,
             'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -306,12 +310,12 @@ def attn_bytes(w, batch, ctx=None):
     return int(kv_ctx + T * per_tok + batch.B * batch.block_table.shape[1] * 4)
 
 
-def gdn_bytes(w, batch):
+def gdn_bytes(w, batch, state_bytes=4):
     """One GDN layer: the state read and written once (the method's minimum),
     q, k, v, the gates and the outputs."""
     s = elem_size(w.gdn_dtype)
     T = batch.total_T
-    return (2 * batch.B * w.H * w.dv * w.dk * 4 + T * w.H * (2 * w.dk + w.dv) * s
+    return (2 * batch.B * w.H * w.dv * w.dk * state_bytes + T * w.H * (2 * w.dk + w.dv) * s
             + T * w.H * 8 + T * w.H * w.dv * s)
 
 
@@ -462,11 +466,17 @@ def cpu_baseline(w, batch, layers, acc, mode, draft_tokens_per_step, budget, com
             sub_t = np.arange(len(pages))[None, :]
             rows = slice(cu[b], cu[b + 1])
             q, kn, vn = f64(a['q'][rows]), f64(a['k_new'][rows]), f64(a['v_new'][rows])
+            one = np.array([0, cu[b + 1] - cu[b]])
             t0 = time.perf_counter()
-            oracle.verify_attention(q, kn, vn, kc, vc, sub_t, ctx[b:b + 1],
-                                    np.array([0, cu[b + 1] - cu[b]]), batch.P)
-            oracle.append_kv(kc, vc, kn, vn, sub_t, ctx[b:b + 1],
-                             np.array([0, cu[b + 1] - cu[b]]), batch.P)
+            if 'k_scale' in a:   # INT8 pages: the codes and the per-channel scales
+                ks, vs = f64(a['k_scale']), f64(a['v_scale'])
+                oracle.verify_attention_int8(q, kn, vn, kc, vc, ks, vs, sub_t, ctx[b:b + 1],
+                                             one, batch.P)
+                oracle.append_kv_int8(kc, vc, kn, vn, ks, vs, sub_t, ctx[b:b + 1], one,
+                                      batch.P)
+            else:
+                oracle.verify_attention(q, kn, vn, kc, vc, sub_t, ctx[b:b + 1], one, batch.P)
+                oracle.append_kv(kc, vc, kn, vn, sub_t, ctx[b:b + 1], one, batch.P)
             t_att_sample += time.perf_counter() - t0
             seqs.append(b)
             if t_att_sample > 0.5 * budget:
@@ -527,15 +537,21 @@ def run_step_workload(w, args, dev, ceil):
     from block_draft_verification_spec_amd import binding as bd
     mode = args.accept if args.accept in w.accept_modes else w.accept_modes[-1]
     steps, warmup = args.steps, args.warmup
+    kv8 = args.kv_format == 'int8'
+    f16 = args.state_dtype == 'f16'
+    if kv8 and w.attn_dtype != torch.bfloat16:
+        sys.exit(f'--kv-format int8 takes bf16 activations; {w.name} is fp32')
+    default_formats = not kv8 and not f16
     # room in every block table for the tokens all eager and graph steps commit
     batch = wl.make_batch(w, args.seed, dev, reserve=w.max_T * (3 * (steps + warmup) + 8))
     layers = []
     for i, kind in enumerate(w.layers):
         if kind == 'attn':
-            lay = wl.make_attn_layer(w, batch, 1000 + i, dev)
+            lay = (wl.make_attn_layer_kv8 if kv8 else wl.make_attn_layer)(w, batch, 1000 + i, dev)
             lay['out'] = torch.empty_like(lay['q'])
         else:
-            lay = wl.make_gdn_layer(w, batch, 1000 + i, dev)
+            lay = wl.make_gdn_layer(w, batch, 1000 + i, dev,
+                                    state_dtype=torch.float16 if f16 else torch.float32)
             lay['out'] = torch.empty_like(lay['v'])
         lay['kind'] = kind
         layers.append(lay)
@@ -551,10 +567,13 @@ def run_step_workload(w, args, dev, ceil):
                                l['out']) for l in layers if l['kind'] == 'gdn']
     step_args = bd.StepArgs(
         [1 if l['kind'] == 'attn' else 0 for l in layers],
-        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table, dt_a),
-        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'])
+        bd.attn_config(w.Hq, w.Hkv, w.D, batch.P, batch.num_pages, batch.block_table, dt_a,
+                       kv_format=bd.SV_KV_INT8 if kv8 else bd.SV_KV_PLAIN),
+        [bd.attn_layer(l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'], l['out'],
+                       l.get('k_scale'), l.get('v_scale'))
          for l in layers if l['kind'] == 'attn'],
-        bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt_g), gdn_layers,
+        bd.gdn_config(w.H, w.dk, w.dv, batch.B, dt_g,
+                      state_dtype=bd.SV_F16 if f16 else bd.SV_F32), gdn_layers,
         bd.accept_args(amode, acc['target_logits'], acc['draft_tokens'],
                        acc.get('draft_logits'), acc.get('u_accept'), acc.get('u_final')))
     sb = bd.make_batch(batch.cu_seqlens, batch.B, batch.max_T, batch.total_T)
@@ -642,13 +661,20 @@ def run_step_workload(w, args, dev, ceil):
     calls = []
     for _ in range(args.attn_reps):
         for l in att_layers:
-            calls.append(lambda l=l: bd.spec_verify_attention(
-                sb, l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
-                batch.block_table, ctx_fixed, l['out'], workspace=ws, err=err))
+            if kv8:
+                calls.append(lambda l=l: bd.spec_verify_attention_kv8(
+                    sb, l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
+                    l['k_scale'], l['v_scale'], batch.block_table, ctx_fixed, l['out'],
+                    workspace=ws, err=err))
+            else:
+                calls.append(lambda l=l: bd.spec_verify_attention(
+                    sb, l['q'], l['k_new'], l['v_new'], l['k_cache'], l['v_cache'],
+                    batch.block_table, ctx_fixed, l['out'], workspace=ws, err=err))
     att_total = timed_block(stream, calls)
     n_launch = len(calls)
     att_ms_mean = att_total / n_launch
-    b_att = attn_bytes(w, batch, ctx_fixed.tolist())
+    b_att = (attn_kv8_bytes(w, batch, ctx_fixed.tolist()) if kv8 else
+             attn_bytes(w, batch, ctx_fixed.tolist()))
     g_total = timed_block(stream, [
         (lambda l=l: bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_COMMIT, l['state'], l['q'],
                                           l['k'], l['v'], l['alpha'], l['beta'], commits[0],
@@ -663,14 +689,14 @@ def run_step_workload(w, args, dev, ceil):
     acc_ms = a_total / acc_reps
 
     with_conv = None
-    if w.name == 'hybrid_step_64l' and not args.no_next_rows:
+    if w.name == 'hybrid_step_64l' and not args.no_next_rows and default_formats:
         with_conv = step_with_conv_timing(w, batch, layers, acc, amode, sb, ws, ctx, err, steps,
                                           warmup, stream, dev, sched, deferred)
         print(f'[bench] step with short conv: {with_conv["ms_per_step"]:.3f} ms/step',
               file=sys.stderr, flush=True)
 
     next_rows = None
-    if w.name == 'hybrid_step_64l' and not args.no_next_rows:
+    if w.name == 'hybrid_step_64l' and not args.no_next_rows and default_formats:
         next_rows = {'short_conv': short_conv_timing(w, batch, sb, commits[0], stream, dev),
                      'gdn_state_dtype': gdn_state_dtype_timing(w, batch, sb, commits[0], stream,
                                                                dev),
@@ -682,8 +708,10 @@ def run_step_workload(w, args, dev, ceil):
     T = batch.total_T
     n_att, n_gdn = len(att_layers), len(gdn_l)
     draft_per_step = T - batch.B
-    b_step = (n_att * attn_bytes(w, batch, ctx_mean) + n_gdn * gdn_bytes(w, batch)
-              + accept_bytes(w, batch, mode))
+    sbytes = 2 if f16 else 4
+    b_step = (n_att * (attn_kv8_bytes(w, batch, ctx_mean) if kv8 else
+                       attn_bytes(w, batch, ctx_mean))
+              + n_gdn * gdn_bytes(w, batch, sbytes) + accept_bytes(w, batch, mode))
     # bytes the schedule actually moves beyond the method's minimum: the
     # replayed tokens' k, v and gates (deferred: read again by the next
     # verify; two-phase: by the batched commit), and under two-phase one more
@@ -691,7 +719,7 @@ def run_step_workload(w, args, dev, ceil):
     es = elem_size(w.gdn_dtype)
     sum_c = float(c_last.sum().item())
     replay = sum_c * w.H * ((w.dk + w.dv) * es + 8)
-    extra = n_gdn * (replay + (0 if deferred else batch.B * w.H * w.dv * w.dk * 4))
+    extra = n_gdn * (replay + (0 if deferred else batch.B * w.H * w.dv * w.dk * sbytes))
     pc = percentiles(per[:steps])
     gbs = b_step / (ms_step * 1e-3) / 1e9
     gbs_med = b_step / (pc['median'] * 1e-3) / 1e9
@@ -701,7 +729,10 @@ def run_step_workload(w, args, dev, ceil):
         'batch': batch.B, 'drafts_per_seq': f'U{{1..{w.k}}}' if w.ragged_k else w.k,
         'ctx': list(w.ctx), 'Hq_Hkv_D': [w.Hq, w.Hkv, w.D], 'page': batch.P,
         'gdn_H_dk_dv': [w.H, w.dk, w.dv], 'vocab': w.V, 'accept': mode,
-        'schedule': args.schedule})
+        'schedule': args.schedule, 'kv_format': args.kv_format,
+        'state_dtype': args.state_dtype})
+    if kv8:  # the attention arithmetic: INT8 codes widened to fp16 for the MFMAs
+        line['dtype'] = 'f16'
     line.update({
         'step_ms': pc,
         'graph': graph,
@@ -716,13 +747,16 @@ def run_step_workload(w, args, dev, ceil):
                                    'gates' + ('' if deferred else
                                               ' and one more read of every GDN state')},
         'ceilings': ceil,
-        'roofline': {'kernel': ('spec_verify_attention, one layer (attn_stream_bf16 + '
+        'roofline': {'kernel': ('spec_verify_attention_kv8, one layer (attn_append_kv8 + '
+                                'attn_stream_kv8 + attn_combine_bf16 launches)' if kv8 else
+                                'spec_verify_attention, one layer (attn_stream_bf16 + '
                                 'attn_combine_bf16 launches)' if dt_a == bd.SV_BF16 else
                                 'spec_verify_attention, one layer (attn_f32)'),
                      'bound': 'hbm', 'achieved': round(achieved, 1), 'peak': HBM_PEAK_GBS,
                      'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
                      'frac_of_measured_read': round(achieved / ceil['read_GBps'], 4),
-                     'traffic': measured_traffic() if w.name == 'hybrid_step_64l' else None,
+                     'traffic': (measured_traffic() if w.name == 'hybrid_step_64l'
+                                 and not kv8 else None),
                      'traffic_unit': 'HBM bytes per launch', 'bytes_per_launch': b_att,
                      'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
@@ -733,9 +767,11 @@ def run_step_workload(w, args, dev, ceil):
         'mean_accept_len': round(accepted, 3),
         # sum_b (a_b + 1) per timed step, from the ctx_lens the steps advanced
         'committed_tokens_per_step': round(c_last.sum().item(), 2),
-        'dtype_detail': ('bf16 I/O and MFMA, fp32 accumulation and GDN state, fp64 acceptance'
-                         if dt_a == bd.SV_BF16 else
-                         'fp32 I/O and accumulation, fp32 GDN state, fp64 acceptance'),
+        'dtype_detail': (('INT8 per-channel KV pages, fp16 MFMA, ' if kv8 else
+                          'bf16 I/O and MFMA, ' if dt_a == bd.SV_BF16 else 'fp32 I/O, ')
+                         + 'fp32 accumulation, '
+                         + ('fp16 GDN state bank (fp32 arithmetic)' if f16 else
+                            'fp32 GDN state') + ', fp64 acceptance'),
     })
     if not args.no_cpu_baseline:
         print('[bench] timing the CPU oracle on a bounded sample', file=sys.stderr, flush=True)

@@ -193,6 +193,22 @@ def _dtype(t):
     raise ValueError(f'unsupported dtype {t.dtype}')
 
 
+def _require(dtype, **tensors):
+    """Every named tensor (None skipped) has `dtype`: the library sees only
+    pointers, so a page pool or state of another element size would be read
+    out of bounds."""
+    for name, t in tensors.items():
+        if t is not None and t.dtype != dtype:
+            raise ValueError(f'{name} must be {dtype}, not {t.dtype}')
+
+
+def _pool_shape(k_cache, v_cache, Hkv, D):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or \
+            k_cache.shape[1] != Hkv or k_cache.shape[3] != D:
+        raise ValueError(f'page pools must both be [num_pages, {Hkv}, page_size, {D}], '
+                         f'not {tuple(k_cache.shape)} and {tuple(v_cache.shape)}')
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -249,6 +265,8 @@ def spec_verify_attention(batch, q, k_new, v_new, k_cache, v_cache,
     """
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k_new.shape[1]
+    _require(q.dtype, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, out=out)
+    _pool_shape(k_cache, v_cache, Hkv, D)
     num_pages, P = k_cache.shape[0], k_cache.shape[2]
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().spec_verify_attention(
@@ -271,8 +289,10 @@ def spec_verify_attention_kv8(batch, q, k_new, v_new, k_cache, v_cache, k_scale,
         raise ValueError('INT8 pages must be torch.int8')
     if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
         raise ValueError('scales must be float32')
+    _require(torch.bfloat16, q=q, k_new=k_new, v_new=v_new, out=out)
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k_new.shape[1]
+    _pool_shape(k_cache, v_cache, Hkv, D)
     num_pages, P = k_cache.shape[0], k_cache.shape[2]
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().spec_verify_attention_kv8(
@@ -292,6 +312,8 @@ def gdn_verify_commit(batch, mode, state, q, k, v, alpha, beta, commit_len,
     ``pending``: an ``SvGdnPending`` or None.
     """
     num_slots, H, dv, dk = state.shape
+    _require(k.dtype, q=q, v=v, out=out)
+    _require(torch.float32, alpha=alpha, beta=beta)
     _check(lib().gdn_verify_commit(
         ctypes.byref(batch), int(mode), _ptr(state), state_dtype(state),
         _i32(state_slot, 'state_slot'),
@@ -422,6 +444,50 @@ def spec_accept_noalloc(batch, mode, target_logits, draft_tokens, result, draft_
         _i32(err, 'err'), _stream(stream)))
 
 
+_TORCH_DTYPE = {SV_F32: torch.float32, SV_BF16: torch.bfloat16, SV_F16: torch.float16}
+
+
+def _check_step_layers(attn_cfg, attn_layers, gdn_cfg, gdn_layers):
+    """The step's layers against its configurations (layers made by attn_layer
+    and gdn_layer carry their tensors): page pools of the configured format
+    and shape, activations and states of the configured dtypes."""
+    for i, lay in enumerate(attn_layers):
+        t = getattr(lay, 'tensors', None)
+        if t is None or attn_cfg is None:
+            continue
+        int8 = attn_cfg.kv_format == SV_KV_INT8
+        act = torch.bfloat16 if int8 else _TORCH_DTYPE.get(attn_cfg.dtype)
+        try:
+            _require(act, q=t['q'], k_new=t['k_new'], v_new=t['v_new'], out=t['out'])
+            _require(torch.int8 if int8 else act, k_cache=t['k_cache'], v_cache=t['v_cache'])
+            _pool_shape(t['k_cache'], t['v_cache'], attn_cfg.Hkv, attn_cfg.D)
+            if t['k_cache'].shape[0] != attn_cfg.num_pages or \
+                    t['k_cache'].shape[2] != attn_cfg.page_size:
+                raise ValueError('page pools do not match num_pages / page_size')
+            if int8:
+                if t['k_scale'] is None or t['v_scale'] is None:
+                    raise ValueError('INT8 pages need k_scale and v_scale')
+                _require(torch.float32, k_scale=t['k_scale'], v_scale=t['v_scale'])
+        except ValueError as e:
+            raise ValueError(f'attention layer {i}: {e}') from None
+    for i, lay in enumerate(gdn_layers):
+        t = getattr(lay, 'tensors', None)
+        if t is None or gdn_cfg is None:
+            continue
+        io = _TORCH_DTYPE.get(gdn_cfg.io_dtype)
+        try:
+            _require(_TORCH_DTYPE.get(gdn_cfg.state_dtype), state=t['state'])
+            _require(io, q=t['q'], k=t['k'], v=t['v'], out=t['out'], conv_state=t['conv_state'],
+                     conv_x=t['conv_x'], conv_out=t['conv_out'])
+            _require(torch.float32, alpha=t['alpha'], beta=t['beta'])
+            if tuple(t['state'].shape[1:]) != (gdn_cfg.H, gdn_cfg.dv, gdn_cfg.dk) or \
+                    t['state'].shape[0] < gdn_cfg.num_slots:
+                raise ValueError(f'state must be [{gdn_cfg.num_slots}, {gdn_cfg.H}, '
+                                 f'{gdn_cfg.dv}, {gdn_cfg.dk}], not {tuple(t["state"].shape)}')
+        except ValueError as e:
+            raise ValueError(f'GDN layer {i}: {e}') from None
+
+
 class StepArgs:
     """Host-side structures of one ``spec_verify_step`` call.
 
@@ -431,6 +497,7 @@ class StepArgs:
 
     def __init__(self, layer_kind, attn_cfg, attn_layers, gdn_cfg, gdn_layers,
                  accept_args):
+        _check_step_layers(attn_cfg, attn_layers, gdn_cfg, gdn_layers)
         self.layer_kind = (ctypes.c_uint8 * len(layer_kind))(*layer_kind)
         self.n_layers = len(layer_kind)
         self.attn_cfg = attn_cfg
@@ -464,8 +531,13 @@ def gdn_config(H, dk, dv, num_slots, io_dtype, state_slot=None, state_dtype=SV_F
 
 
 def attn_layer(q, k_new, v_new, k_cache, v_cache, out, k_scale=None, v_scale=None):
-    return SvAttnLayer(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-                       _ptr(v_cache), _ptr(out), _ptr(k_scale), _ptr(v_scale))
+    """One attention layer of the step (its tensors' dtypes and pool shapes are
+    checked against the step's attention configuration in StepArgs)."""
+    lay = SvAttnLayer(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                      _ptr(v_cache), _ptr(out), _ptr(k_scale), _ptr(v_scale))
+    lay.tensors = dict(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+                       out=out, k_scale=k_scale, v_scale=v_scale)
+    return lay
 
 
 def gdn_layer(state, q, k, v, alpha, beta, out, conv=None):
@@ -476,9 +548,12 @@ def gdn_layer(state, q, k, v, alpha, beta, out, conv=None):
     if c and (c['weight'].dtype != torch.float32 or
               (c.get('bias') is not None and c['bias'].dtype != torch.float32)):
         raise ValueError('conv weight and bias must be float32')
-    return SvGdnLayer(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                      _ptr(beta), _ptr(out), _ptr(c.get('state')), _ptr(c.get('x')),
-                      _ptr(c.get('out')), _ptr(c.get('weight')), _ptr(c.get('bias')))
+    lay = SvGdnLayer(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                     _ptr(beta), _ptr(out), _ptr(c.get('state')), _ptr(c.get('x')),
+                     _ptr(c.get('out')), _ptr(c.get('weight')), _ptr(c.get('bias')))
+    lay.tensors = dict(state=state, q=q, k=k, v=v, alpha=alpha, beta=beta, out=out,
+                       conv_state=c.get('state'), conv_x=c.get('x'), conv_out=c.get('out'))
+    return lay
 
 
 def accept_args(mode, target_logits, draft_tokens, draft_logits=None,

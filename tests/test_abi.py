@@ -367,6 +367,54 @@ def test_workspace_sizes_are_consistent():
     assert 0 < g < r
 
 
+def test_step_layers_are_checked_against_their_configuration():
+    """The binding refuses step layers whose pools or states do not have the
+    configured element type or shape (the library sees only pointers, so an
+    INT8 pool under a bf16 configuration would be read out of bounds)."""
+    import types
+
+    import torch
+    B, H, dk, dv, Hq, Hkv, D, P, pages = 2, 2, 64, 64, 4, 2, 64, 16, 6
+
+    def attn(cache_dtype, act=torch.bfloat16, shape=(pages, Hkv, P, D), scales=False):
+        t = dict(q=torch.zeros(8, Hq, D, dtype=act), k_new=torch.zeros(8, Hkv, D, dtype=act),
+                 v_new=torch.zeros(8, Hkv, D, dtype=act), out=torch.zeros(8, Hq, D, dtype=act),
+                 k_cache=torch.zeros(shape, dtype=cache_dtype),
+                 v_cache=torch.zeros(shape, dtype=cache_dtype),
+                 k_scale=torch.ones(Hkv, D) if scales else None,
+                 v_scale=torch.ones(Hkv, D) if scales else None)
+        return types.SimpleNamespace(tensors=t)
+
+    def gdn(state_dtype=torch.float32, io=torch.bfloat16, slots=B):
+        t = dict(state=torch.zeros(slots, H, dv, dk, dtype=state_dtype),
+                 q=torch.zeros(8, H, dk, dtype=io), k=torch.zeros(8, H, dk, dtype=io),
+                 v=torch.zeros(8, H, dv, dtype=io), out=torch.zeros(8, H, dv, dtype=io),
+                 alpha=torch.ones(8, H), beta=torch.ones(8, H),
+                 conv_state=None, conv_x=None, conv_out=None)
+        return types.SimpleNamespace(tensors=t)
+
+    cfg = bd.SvAttnConfig(Hq, Hkv, D, P, pages, 4, None, bd.SV_BF16, 0.0, bd.SV_KV_PLAIN)
+    cfg8 = bd.SvAttnConfig(Hq, Hkv, D, P, pages, 4, None, bd.SV_BF16, 0.0, bd.SV_KV_INT8)
+    gcfg = bd.SvGdnConfig(H, dk, dv, B, None, bd.SV_BF16, bd.SV_F32)
+    gcfg16 = bd.SvGdnConfig(H, dk, dv, B, None, bd.SV_BF16, bd.SV_F16)
+    bd._check_step_layers(cfg, [attn(torch.bfloat16)], gcfg, [gdn()])        # consistent
+    bd._check_step_layers(cfg8, [attn(torch.int8, scales=True)], gcfg16,
+                          [gdn(torch.float16)])
+    for args, msg in [
+        ((cfg, [attn(torch.int8)], gcfg, []), 'k_cache must be torch.bfloat16'),
+        ((cfg8, [attn(torch.bfloat16, scales=True)], gcfg, []), 'k_cache must be torch.int8'),
+        ((cfg8, [attn(torch.int8)], gcfg, []), 'k_scale'),
+        ((cfg, [attn(torch.bfloat16, shape=(pages, Hkv, 2 * P, D))], gcfg, []), 'page_size'),
+        ((cfg, [attn(torch.bfloat16, act=torch.float32)], gcfg, []), 'q must be'),
+        ((cfg, [], gcfg, [gdn(torch.float16)]), 'state must be torch.float32'),
+        ((cfg, [], gcfg16, [gdn()]), 'state must be torch.float16'),
+        ((cfg, [], gcfg, [gdn(io=torch.float32)]), 'q must be torch.bfloat16'),
+        ((cfg, [], gcfg, [gdn(slots=1)]), 'state must be'),
+    ]:
+        with pytest.raises(ValueError, match=msg):
+            bd._check_step_layers(*args)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     b = _batch()
