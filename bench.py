@@ -382,6 +382,28 @@ def timed_block(stream, calls):
     return e0.elapsed_time(e1)
 
 
+def graph_block_ms(stream, calls, reps=3):
+    """The callables captured into one HIP graph and replayed `reps` times
+    back to back between two HIP events on `stream` (no host work between
+    the kernels); returns the time per replay (ms)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode='thread_local'):
+        for c in calls:
+            c()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
 def timed_calls(stream, calls):
     """Run the callables back to back on `stream` with a HIP event before
     each one and after the last; returns the per-call times (ms) and the
@@ -672,7 +694,10 @@ def run_step_workload(w, args, dev, ceil):
                     batch.block_table, ctx_fixed, l['out'], workspace=ws, err=err))
     att_total = timed_block(stream, calls)
     n_launch = len(calls)
-    att_ms_mean = att_total / n_launch
+    att_ms_eager = att_total / n_launch
+    # the same launches replayed from a HIP graph: the kernels' own time, with
+    # no host work (marshalling, launch calls) between them
+    att_ms_mean = graph_block_ms(stream, calls) / n_launch
     b_att = (attn_kv8_bytes(w, batch, ctx_fixed.tolist()) if kv8 else
              attn_bytes(w, batch, ctx_fixed.tolist()))
     g_total = timed_block(stream, [
@@ -758,7 +783,11 @@ def run_step_workload(w, args, dev, ceil):
                      'traffic': (measured_traffic() if w.name == 'hybrid_step_64l'
                                  and not kv8 else None),
                      'traffic_unit': 'HBM bytes per launch', 'bytes_per_launch': b_att,
-                     'launch_ms': round(att_ms_mean, 4), 'launches': n_launch},
+                     'launch_ms': round(att_ms_mean, 4), 'launches': n_launch,
+                     'launch_ms_eager': round(att_ms_eager, 4),
+                     'how': 'the layer\'s launches captured into one HIP graph and replayed '
+                            'between two HIP events on the launch stream (launch_ms_eager: the '
+                            'same launches issued eagerly)'},
         'parts_ms': {'attention_layer': round(att_ms_mean, 4),
                      'gdn_layer_verify_commit': round(gdn_ms, 4),
                      'acceptance': round(acc_ms, 4)},
