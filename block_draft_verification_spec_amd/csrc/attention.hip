@@ -98,6 +98,32 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// Two fp32 values rounded to nearest even into bf16 or fp16 (element 0 in
+// the low half) by one packed conversion, and each half read back as fp32.
+typedef __attribute__((ext_vector_type(2))) float float2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+template <bool F16>
+__device__ __forceinline__ uint32_t round2_t(float2_t x) {
+  if constexpr (F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+template <bool F16>
+__device__ __forceinline__ float lo16_to_f32(uint32_t u) {
+  if constexpr (F16)
+    return f16_bits_to_f32(static_cast<uint16_t>(u & 0xffffu));
+  else
+    return __uint_as_float(u << 16);
+}
+template <bool F16>
+__device__ __forceinline__ float hi16_to_f32(uint32_t u) {
+  if constexpr (F16)
+    return f16_bits_to_f32(static_cast<uint16_t>(u >> 16));
+  else
+    return __uint_as_float(u & 0xffff0000u);
+}
+
 __device__ __forceinline__ int seq_tiles(int L, int T) { return (L + T + kKT - 1) / kKT; }
 
 // Validate a sequence (first row x0, T verify tokens, L cached tokens) for
@@ -484,6 +510,8 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   // wave w owns keys 16 w .. 16 w + 15 of the tile
   auto compute_tile = [&](int tile) __attribute__((always_inline)) {
     const int kbase = tile * kKT + 16 * w;
+    // a tile of context keys below pos_end needs only the padding-row mask
+    const bool inner = (tile + 1) * kKT <= min(L, pos_end);
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
       float4_t sacc = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -500,14 +528,23 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       }
       // lane holds S^T[key 4 lg + r][row lr]
       const int m = 16 * nt + lr;
-      const int lim = (m < M) ? L + m / G : -1;  // last visible position
       float sv[4];
       float tmax = -INFINITY;
+      if (inner) {  // every key visible to every query row of the sequence
+        const bool row_ok = m < M;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = kbase + 4 * lg + r;
-        sv[r] = (p <= lim && p < pos_end) ? sacc[r] * sl2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[r]);
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = row_ok ? sacc[r] * sl2 : -INFINITY;
+          tmax = fmaxf(tmax, sv[r]);
+        }
+      } else {
+        const int lim = (m < M) ? L + m / G : -1;  // last visible position
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = kbase + 4 * lg + r;
+          sv[r] = (p <= lim && p < pos_end) ? sacc[r] * sl2 : -INFINITY;
+          tmax = fmaxf(tmax, sv[r]);
+        }
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -516,16 +553,21 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       if (m_new == -INFINITY) {
         pf = short4_t{0, 0, 0, 0};
       } else {
-        const float alpha = exp2f(m_run[nt] - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // the rounded weight enters both the PV product and the normaliser
-          const float e = exp2f(sv[r] - m_new);
-          const uint16_t hb = KV8 ? f32_to_f16_bits(e) : f32_to_bf16(e);
-          pf[r] = static_cast<short>(hb);
-          psum += KV8 ? f16_bits_to_f32(hb) : bf16_to_f32(hb);
-        }
+        // 2^x by the hardware instruction (arguments <= 0; -inf gives 0)
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        float2_t e01, e23;
+        e01[0] = __builtin_amdgcn_exp2f(sv[0] - m_new);
+        e01[1] = __builtin_amdgcn_exp2f(sv[1] - m_new);
+        e23[0] = __builtin_amdgcn_exp2f(sv[2] - m_new);
+        e23[1] = __builtin_amdgcn_exp2f(sv[3] - m_new);
+        // the weights rounded to nearest even, two per conversion; the
+        // rounded weight enters both the PV product and the normaliser
+        const uint32_t w01 = round2_t<KV8>(e01), w23 = round2_t<KV8>(e23);
+        pf = __builtin_bit_cast(short4_t, make_uint2(w01, w23));
+        float psum = lo16_to_f32<KV8>(w01);
+        psum += hi16_to_f32<KV8>(w01);
+        psum += lo16_to_f32<KV8>(w23);
+        psum += hi16_to_f32<KV8>(w23);
         l_run[nt] = l_run[nt] * alpha + psum;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // skip when no row's max moved
 #pragma unroll
