@@ -90,10 +90,6 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& 
   hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
 }
 
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-}
-
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
