@@ -140,10 +140,10 @@ def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=4):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
 
-        def run(l):
+        def run(l, s=stream):
             bd.gdn_verify_commit(sb, bd.SV_GDN_VERIFY_ONLY, l['state'], l['q'], l['k'], l['v'],
                                  l['alpha'], l['beta'], None, l['out'], pending=l['pend'],
-                                 stream=stream)
+                                 stream=s)
         for l in layers:
             run(l)
         e0.record(stream)
@@ -153,6 +153,7 @@ def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=4):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / (reps * len(layers))
+        gms = graph_block_ms(stream, [(lambda l=l: run(l, None)) for l in layers]) / len(layers)
         es = torch.finfo(sdt).bits // 8
         T = batch.total_T
         pend_rows = int(commit.sum().item())
@@ -160,9 +161,12 @@ def gdn_state_dtype_timing(w, batch, sb, commit, stream, dev, reps=4):
         nbytes = (2 * batch.B * w.H * w.dv * w.dk * es + T * w.H * (2 * w.dk + 2 * w.dv) * 2
                   + T * w.H * 8 + pend_rows * w.H * ((w.dk + w.dv) * 2 + 8))
         res[name] = {'layer_ms': round(ms, 4), 'bytes': nbytes,
-                     'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1)}
+                     'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     'layer_ms_graph': round(gms, 4),
+                     'GBps_graph': round(nbytes / (gms * 1e-3) / 1e9, 1)}
         del layers
     res['schedule'] = 'deferred (pending replay + verify)'
+    res['graph'] = 'the same sixteen calls replayed from a HIP graph'
     return res
 
 
@@ -252,11 +256,11 @@ def attn_kv8_timing(w, batch, sb, ctx, ws, stream, dev, n_layers=16, reps=3):
     for l in layers:
         l['out'] = torch.empty_like(l['q'])
 
-    def run(l):
+    def run(l, s=stream):
         bd.spec_verify_attention_kv8(sb, l['q'], l['k_new'], l['v_new'], l['k_cache'],
                                      l['v_cache'], l['k_scale'], l['v_scale'],
                                      batch.block_table, ctx, l['out'], workspace=ws,
-                                     stream=stream)
+                                     stream=s)
     for l in layers:
         run(l)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -268,11 +272,17 @@ def attn_kv8_timing(w, batch, sb, ctx, ws, stream, dev, n_layers=16, reps=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (reps * n_layers)
+    # the same launches replayed from a HIP graph (captured on the current
+    # stream, so the calls take the default stream argument)
+    gms = graph_block_ms(stream, [(lambda l=l: run(l, None)) for l in layers]) / n_layers
     nbytes = attn_kv8_bytes(w, batch, ctx.tolist())
     del layers
     return {'layer_ms': round(ms, 4), 'bytes': nbytes,
             'GBps': round(nbytes / (ms * 1e-3) / 1e9, 1),
             'frac_of_peak': round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            'layer_ms_graph': round(gms, 4),
+            'GBps_graph': round(nbytes / (gms * 1e-3) / 1e9, 1),
+            'frac_of_peak_graph': round(nbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             'launches': reps * n_layers}
 
 
