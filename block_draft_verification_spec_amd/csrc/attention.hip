@@ -645,6 +645,15 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       next_seq = true;
     }
 
+    // The first chunk's page ids (the first 4 * kThreads of the sequence, four
+    // per thread) are loaded before the Q fragments, so that the two round
+    // trips overlap; the staging below uses them.
+    const int* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+    const int npg = (L + T - 1) / P + 1;  // pages the sequence uses
+    int pid0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pid0[u] = bt[min(u * kThreads + tid, npg - 1)];
+
     // Q fragments (B operand of S^T = K Q^T): row 16 nt + lr, dims 32 s + 8 lg ..
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
@@ -691,7 +700,6 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       const int n_pages = (pos_end - 1) / P - first_page + 1;
       last_tile = (pos_end - 1) / kKT;
       last_pg = n_pages - 1;
-      const int* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
       __syncthreads();  // the previous chunk is done with s_ids and the tile LDS
       if (c0 == lt_begin) {
         // The piece's first chunk checks every page id the sequence uses
@@ -699,12 +707,8 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
         // an id outside the pool is skipped by all of its pieces (no output,
         // no append) and flagged.  Four loads per thread are issued before
         // any is used.
-        const int npg = (L + T - 1) / P + 1;
         int bad = 0;
-        for (int i0 = 0; i0 < npg; i0 += 4 * kThreads) {
-          int pid[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) pid[u] = bt[min(i0 + u * kThreads + tid, npg - 1)];
+        auto check = [&](int i0, const int (&pid)[4]) __attribute__((always_inline)) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int i = i0 + u * kThreads + tid, li = i - first_page;
@@ -713,6 +717,13 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
               if (li >= 0 && li < n_pages) s_ids[li] = pid[u];
             }
           }
+        };
+        check(0, pid0);
+        for (int i0 = 4 * kThreads; i0 < npg; i0 += 4 * kThreads) {
+          int pid[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pid[u] = bt[min(i0 + u * kThreads + tid, npg - 1)];
+          check(i0, pid);
         }
         // one flag per wave (s_scan is free after the start-up), one barrier
         const bool wave_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
