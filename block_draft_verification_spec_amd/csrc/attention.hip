@@ -807,24 +807,45 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       const float mm = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
       scale_w[nt] = (wm[w][m] == -INFINITY) ? 0.f : exp2f(wm[w][m] - mm);
     }
-    for (int ww = 0; ww < 4; ++ww) {
-      if (w == ww) {
+    // One 16-row tile: each wave writes its rows to a region of its own (the
+    // four fit in the tile space) and the result loop scales and adds them in
+    // wave order, behind one barrier; more tiles: the waves scale and add into
+    // one region in turn.  Either way the sum is
+    // fma(O3, s3, fma(O2, s2, fma(O1, s1, O0 * s0))).
+    constexpr bool kOwnRegions = NQT == 1;
+    static_assert(!kOwnRegions || 4 * 16 * D * 4 <= (kKT * KS + D * VS) * 2,
+                  "four waves' rows fit in the tile space");
+    if constexpr (kOwnRegions) {
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
+      for (int dt = 0; dt < NDT; ++dt) {
+        float4* dst = reinterpret_cast<float4*>(R + (w * 16 + lr) * D + 16 * dt + 4 * lg);
+        const float4_t v = oacc[0][dt];
+        *dst = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      __syncthreads();
+    } else {
+      for (int ww = 0; ww < 4; ++ww) {
+        if (w == ww) {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            float4* dst = reinterpret_cast<float4*>(R + (16 * nt + lr) * D + 16 * dt + 4 * lg);
-            const float4_t v = oacc[nt][dt] * scale_w[nt];
-            if (ww == 0) {
-              *dst = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-              const float4 c = *dst;
-              *dst = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
+          for (int nt = 0; nt < NQT; ++nt) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              float4* dst = reinterpret_cast<float4*>(R + (16 * nt + lr) * D + 16 * dt + 4 * lg);
+              const float4_t v = oacc[nt][dt] * scale_w[nt];
+              if (ww == 0) {
+                *dst = make_float4(v[0], v[1], v[2], v[3]);
+              } else {
+                const float4 c = *dst;
+                const float4_t o = oacc[nt][dt];
+                const float sw = scale_w[nt];
+                *dst = make_float4(fmaf(o[0], sw, c.x), fmaf(o[1], sw, c.y), fmaf(o[2], sw, c.z),
+                                   fmaf(o[3], sw, c.w));
+              }
             }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
 
     // ---- the piece's result: row m -> (token m / G, head g * G + m % G)
@@ -836,6 +857,17 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
       for (int ww = 0; ww < 4; ++ww)
         if (wm[ww][m] != -INFINITY) ls += wl[ww][m] * exp2f(wm[ww][m] - mm);
       float4 o = *reinterpret_cast<const float4*>(R + m * D + d4);
+      if constexpr (kOwnRegions) {
+        const float s0 = (wm[0][m] == -INFINITY) ? 0.f : exp2f(wm[0][m] - mm);
+        o = make_float4(o.x * s0, o.y * s0, o.z * s0, o.w * s0);
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+          const float sw = (wm[ww][m] == -INFINITY) ? 0.f : exp2f(wm[ww][m] - mm);
+          const float4 c = *reinterpret_cast<const float4*>(R + (ww * 16 + m) * D + d4);
+          o = make_float4(fmaf(c.x, sw, o.x), fmaf(c.y, sw, o.y), fmaf(c.z, sw, o.z),
+                          fmaf(c.w, sw, o.w));
+        }
+      }
       if constexpr (KV8) {  // the codes' bias (weight sum ls), then the V channel scales
         const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + static_cast<size_t>(g) * D + d4);
         const float bias = kCodeBias * ls;
