@@ -135,7 +135,7 @@ sv::AttnArgs make_attn_args(const sv_batch* batch, const void* q, const void* k_
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (dtype == SV_BF16) {
-    a.n_wg = sv::attn_stream_grid(D, Hq / Hkv, a.max_T, a.kv8 != 0, &a.n_cu);
+    a.n_wg = sv::attn_stream_grid(D, Hq / Hkv, a.max_T, a.kv8 != 0);
     sv::attn_workspace_carve(ws, a.B, Hkv, D, a.n_wg, &a.seg_meta, &a.part_o, &a.part_ml);
   }
   return a;

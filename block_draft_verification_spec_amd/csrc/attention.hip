@@ -162,9 +162,8 @@ __device__ __forceinline__ long long page_offset(const AttnArgs& a, int b, int g
 // sequence b, head g, in position order).  Each segment is priced at its
 // tiles plus piece_cost() units for the set-up of a piece (bounds, Q, page
 // ids, a first tile with none in flight, and the write of its result);
-// the U units are split over the W workgroups by weight (round_w below),
-// workgroup w taking units [U S(w) / S(W), U S(w + 1) / S(W)) with S(w) the
-// weight of workgroups 0 .. w - 1, and a unit range maps to the tiles it
+// the U units are split evenly over the W workgroups, workgroup w taking
+// units [U w / W, U (w + 1) / W), and a unit range maps to the tiles it
 // covers (unit r of a segment is its tile max(r - piece_cost, 0)).  So each
 // workgroup's share of the cost is fixed whatever the context lengths: one
 // that starts more segments streams fewer tiles.  A segment cut by range
@@ -199,12 +198,12 @@ constexpr int kLoadPrio = 3;
 //
 // Profile 1, INT8 pages: three workgroups per CU (their tiles carry more
 // VALU work per byte; at two per CU they ran 0.136-0.155 against
-// 0.132-0.140 ms), a 3-tile piece set-up and weights by dispatch round:
-// workgroups are placed in order, one per CU per round, and a CU's older
-// waves win its arbitration (at equal tile counts the one placed first
-// finished after 189 us, the second after 198 and the last after 229), so
-// later rounds get shorter ranges (about 1 % faster per layer than equal
-// ones).
+// 0.132-0.140 ms) and a 3-tile piece set-up.  Shorter ranges for the
+// workgroups of later dispatch rounds (a CU's older waves win its
+// arbitration) once measured 1 % faster for INT8 pages; with the kernel as
+// it is now they measured no faster, and the per-workgroup arithmetic of a
+// weighted split slowed every launch's start-up (bf16 pages 0.5-1 %, the
+// 32-sequence call 1.5 %), so every profile splits evenly.
 // 16-row MFMA tiles of query rows per (sequence, KV head): G max_T rows.
 __host__ __device__ constexpr int nqt_for(int G, int max_T) {
   return G * max_T <= 16 ? 1 : (G * max_T <= 32 ? 2 : 4);
@@ -212,24 +211,9 @@ __host__ __device__ constexpr int nqt_for(int G, int max_T) {
 __host__ __device__ constexpr int split_profile(bool kv8) { return kv8 ? 1 : 0; }
 template <int PROF>
 constexpr int piece_cost() { return PROF == 0 ? 7 : 3; }
-constexpr int kRoundW[2][4] = {{64, 64, 64, 64}, {64, 61, 53, 53}};  // [profile][round]
-__host__ __device__ inline int round_w(int r, int prof) { return kRoundW[prof][r < 3 ? r : 3]; }
-__host__ __device__ inline int round_w_min(int prof) {
-  int m = kRoundW[prof][0];
-  for (int i = 1; i < 4; ++i) m = kRoundW[prof][i] < m ? kRoundW[prof][i] : m;
-  return m;
-}
-// Weight of workgroups [0, w): n_cu workgroups per round.
-__host__ __device__ inline long long wg_weight(int w, int n_cu, int prof) {
-  long long s = 0;
-  int r = 0;
-  for (; (r + 1) * n_cu <= w; ++r) s += static_cast<long long>(n_cu) * round_w(r, prof);
-  return s + static_cast<long long>(w - r * n_cu) * round_w(r, prof);
-}
-// First unit of workgroup w: U S(w) / S(W).
-__host__ __device__ inline int wg_unit(int w, int W, int n_cu, int U, int prof) {
-  return static_cast<int>(static_cast<long long>(U) * wg_weight(w, n_cu, prof) /
-                          wg_weight(W, n_cu, prof));
+// First unit of workgroup w: U w / W.
+__host__ __device__ inline int wg_unit(int w, int W, int U) {
+  return static_cast<int>(static_cast<long long>(U) * w / W);
 }
 
 // One tile's slice of K and V held by a thread.
@@ -239,17 +223,10 @@ struct TileRegs {
   u32x4_t v[KPT];
 };
 
-__host__ __device__ inline int piece_wg(int u, int W, int n_cu, int U, int prof) {
+__host__ __device__ inline int piece_wg(int u, int W, int U) {
   // the workgroup whose range [wg_unit(w), wg_unit(w + 1)) holds unit u: the
-  // last w with U S(w) < (u + 1) S(W), i.e. S(w) <= smax
-  const long long smax = ((static_cast<long long>(u) + 1) * wg_weight(W, n_cu, prof) - 1) / U;
-  int r = 0;
-  long long base = 0;
-  while ((r + 1) * n_cu < W && base + static_cast<long long>(n_cu) * round_w(r, prof) <= smax) {
-    base += static_cast<long long>(n_cu) * round_w(r, prof);
-    ++r;
-  }
-  return min(r * n_cu + static_cast<int>((smax - base) / round_w(r, prof)), W - 1);
+  // last w with U w < (u + 1) W
+  return min(static_cast<int>(((static_cast<long long>(u) + 1) * W - 1) / U), W - 1);
 }
 
 // PF: tiles in flight per workgroup (a ring of register buffers; registers
@@ -338,8 +315,8 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
   const int U = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
   const int W = gridDim.x, wg = blockIdx.x;
   if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = U;  // for the combine launch
-  const int u_lo = wg_unit(wg, W, a.n_cu, U, kProf);
-  const int u_hi = wg_unit(wg + 1, W, a.n_cu, U, kProf);
+  const int u_lo = wg_unit(wg, W, U);
+  const int u_hi = wg_unit(wg + 1, W, U);
   // the sequences whose units hold u_lo and u_hi: their owners map them to
   // tiles (sequences without tiles own no units and never match; unit U maps
   // to tile N)
@@ -636,7 +613,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     M = G * T;
     // the segment's last tile is its unit kPC + nt_b - 1
     const int seg_last_wg =
-        piece_wg(ucbase + g * (nt_b + kPC) + kPC + nt_b - 1, W, a.n_cu, U, kProf);
+        piece_wg(ucbase + g * (nt_b + kPC) + kPC + nt_b - 1, W, U);
     t = seg_start + lt_end;
     if (t == cbase + Hkv * nt_b) {
       cbase = t;
@@ -1003,13 +980,12 @@ __global__ __launch_bounds__(kThreads) void attn_combine_bf16(AttnArgs a) {
   // call's data) and is skipped.  Between the units of the segment's first and
   // last tiles every unit is a tile, so a non-empty unit range there is a
   // non-empty piece.
-  const int W = a.n_wg, ncu = a.n_cu;
-  const int prof = split_profile(a.kv8 != 0);
-  const bool sparse = static_cast<long long>(Units) * round_w_min(prof) < wg_weight(W, ncu, prof);
+  const int W = a.n_wg;
+  const bool sparse = Units < W;
   constexpr int kFew = 4;  // pieces fetched at once (one round trip)
   int pws[kFew], np = 0;
   for (int w = wf; w <= wl_; ++w) {
-    if (sparse && wg_unit(w, W, ncu, Units, prof) == wg_unit(w + 1, W, ncu, Units, prof)) continue;
+    if (sparse && wg_unit(w, W, Units) == wg_unit(w + 1, W, Units)) continue;
     if (np < kFew) pws[np] = w;
     ++np;
   }
@@ -1041,7 +1017,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_bf16(AttnArgs a) {
         if (q < np) add(ml[q].x, ml[q].y, po[q]);
     } else {
       for (int w = wf; w <= wl_; ++w) {
-        if (sparse && wg_unit(w, W, ncu, Units, prof) == wg_unit(w + 1, W, ncu, Units, prof)) continue;
+        if (sparse && wg_unit(w, W, Units) == wg_unit(w + 1, W, Units)) continue;
         const size_t pi = static_cast<size_t>(s + w) * kMaxRows + m;
         const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * pi);
         add(ml.x, ml.y, *reinterpret_cast<const float4*>(a.part_o + pi * D + d4));
@@ -1186,18 +1162,15 @@ const void* stream_kernel_for(int D, int nqt) {
 
 // Resident workgroups of one stream-kernel instance on the current device:
 // the grid that keeps every CU busy without a second wave of workgroups.
-int stream_grid(int D, int nqt, bool kv8, int* n_cu = nullptr) {
+int stream_grid(int D, int nqt, bool kv8) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, bool>, std::pair<int, int>> cache;
+  static std::map<std::tuple<int, int, int, bool>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
   const auto key = std::make_tuple(dev, D, nqt, kv8);
   auto it = cache.find(key);
-  if (it != cache.end()) {
-    if (n_cu) *n_cu = it->second.second;
-    return it->second.first;
-  }
+  if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
@@ -1207,8 +1180,7 @@ int stream_grid(int D, int nqt, bool kv8, int* n_cu = nullptr) {
     per_cu = 1;
   per_cu = std::min(per_cu, wg_per_cu_cap(kv8));
   const int n = cus * per_cu;
-  cache[key] = {n, cus};
-  if (n_cu) *n_cu = cus;
+  cache[key] = n;
   return n;
 }
 
@@ -1257,8 +1229,8 @@ void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_m
   *part_ml = reinterpret_cast<float*>(base + meta + o_bytes);
 }
 
-int attn_stream_grid(int D, int G, int max_T, bool kv8, int* n_cu) {
-  return stream_grid(D, nqt_for(G, max_T), kv8, n_cu);
+int attn_stream_grid(int D, int G, int max_T, bool kv8) {
+  return stream_grid(D, nqt_for(G, max_T), kv8);
 }
 
 // Blocks of the combine per segment: one float4 of the segment's rows per

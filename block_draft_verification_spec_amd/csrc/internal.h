@@ -116,7 +116,6 @@ struct AttnArgs {
   int32_t* err;
   // stream-kernel grid and the pieces of segments cut by range boundaries
   int n_wg;                     // workgroups (grid.x)
-  int n_cu;                     // compute units: workgroups placed per dispatch round
   int* seg_meta;                // [B * Hkv][2]: first and last workgroup of a segment,
                                 // then the launch's count of cost units
   float* part_o;                // [(B * Hkv + n_wg) * 64 rows][D]
@@ -129,7 +128,7 @@ size_t attn_workspace_bytes(int B, int total_T, int Hq, int Hkv, int D,
 void attn_workspace_carve(void* ws, int B, int Hkv, int D, int n_wg, int** seg_meta,
                           float** part_o, float** part_ml);
 // Grid of the stream kernel for these shapes on the current device.
-int attn_stream_grid(int D, int G, int max_T, bool kv8, int* n_cu);
+int attn_stream_grid(int D, int G, int max_T, bool kv8);
 hipError_t launch_attention(const AttnArgs& a, sv_dtype dtype,
                             hipStream_t stream);
 
