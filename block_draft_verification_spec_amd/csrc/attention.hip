@@ -186,8 +186,10 @@ constexpr int kLoadPrio = 3;
 // keys; 256 sequences of 16384 to 32768 keys with 2 to 8 verify tokens).
 //
 // Profile 0, bf16 pages: at most two workgroups per CU (with one 16-row
-// query tile the register budget is that of three; see wg_per_cu_cap),
-// equal weights and a piece set-up priced at 7 tiles: 0.227-0.231 ms per
+// query tile the register budget is that of three; see wg_per_cu_cap) and
+// a piece set-up priced at 7 tiles, 6 where the workgroups average 32 tiles
+// or more (the 64-sequence layer 0.8 % faster at 6; the 32-sequence call,
+// at 18 tiles per workgroup, 1.5 % slower at 6): 0.227-0.231 ms per
 // 64-sequence layer against 0.239-0.241 ms at three workgroups per CU, and
 // 61.6-63.3 against 67-68 us for the 32-sequence call.  One tile in flight
 // per workgroup at two workgroups streams faster than at three: a CU's
@@ -280,7 +282,7 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(lv[i]));
   int nts[kPer];  // tiles per segment of each sequence (0: no tiles)
-  int run = 0, urun = 0;
+  int run = 0, srun = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = tid * kPer + i;
@@ -288,32 +290,36 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     if (b < B && attn_seq_valid(a, cuv[i], cuv[i + 1] - cuv[i], lv[i], blockIdx.x == 0))
       nts[i] = seq_tiles(lv[i], cuv[i + 1] - cuv[i]);
     run += nts[i] * Hkv;
-    urun += nts[i] > 0 ? (nts[i] + kPC) * Hkv : 0;
+    srun += nts[i] > 0 ? Hkv : 0;  // segments with tiles
   }
-  // inclusive scans of the per-thread tile and unit totals: within each wave
+  // inclusive scans of the per-thread tile and segment counts: within each wave
   // by shuffles, then the totals of the waves before it
-  int inc = run, uinc = urun;
+  int inc = run, sinc = srun;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off, 64), yu = __shfl_up(uinc, off, 64);
+    const int y = __shfl_up(inc, off, 64), ys = __shfl_up(sinc, off, 64);
     if (lane >= off) {
       inc += y;
-      uinc += yu;
+      sinc += ys;
     }
   }
   if (lane == 63) {
     s_scan[0][w] = inc;
-    s_scan[1][w] = uinc;
+    s_scan[1][w] = sinc;
   }
   __syncthreads();
-  int excl = inc - run, uexcl = uinc - urun;
+  int excl = inc - run, sexcl = sinc - srun;
   for (int ww = 0; ww < w; ++ww) {
     excl += s_scan[0][ww];
-    uexcl += s_scan[1][ww];
+    sexcl += s_scan[1][ww];
   }
   const int N = s_scan[0][0] + s_scan[0][1] + s_scan[0][2] + s_scan[0][3];
-  const int U = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
+  const int NS = s_scan[1][0] + s_scan[1][1] + s_scan[1][2] + s_scan[1][3];
   const int W = gridDim.x, wg = blockIdx.x;
+  // the piece set-up in tiles: one less for bf16 pages with long ranges
+  const int pc = (kProf == 0 && N >= 32 * W) ? kPC - 1 : kPC;
+  const int U = N + pc * NS;
+  const int uexcl = excl + pc * sexcl;
   if (wg == 0 && tid == 0) a.seg_meta[2 * B * Hkv] = U;  // for the combine launch
   const int u_lo = wg_unit(wg, W, U);
   const int u_hi = wg_unit(wg + 1, W, U);
@@ -324,10 +330,10 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     int pre = excl, upre = uexcl;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int nt = nts[i], uend = upre + (nt > 0 ? (nt + kPC) * Hkv : 0);
+      const int nt = nts[i], uend = upre + (nt > 0 ? (nt + pc) * Hkv : 0);
       auto tile_of = [&](int u) {
-        const int r = u - upre, h = r / (nt + kPC);
-        return pre + h * nt + max(r - h * (nt + kPC) - kPC, 0);
+        const int r = u - upre, h = r / (nt + pc);
+        return pre + h * nt + max(r - h * (nt + pc) - pc, 0);
       };
       if (u_lo >= upre && u_lo < uend) {
         s_first[0] = tid * kPer + i;
@@ -613,11 +619,11 @@ __device__ __forceinline__ void attn_stream_body(const AttnArgs& a) {
     M = G * T;
     // the segment's last tile is its unit kPC + nt_b - 1
     const int seg_last_wg =
-        piece_wg(ucbase + g * (nt_b + kPC) + kPC + nt_b - 1, W, U);
+        piece_wg(ucbase + g * (nt_b + pc) + pc + nt_b - 1, W, U);
     t = seg_start + lt_end;
     if (t == cbase + Hkv * nt_b) {
       cbase = t;
-      ucbase += Hkv * (nt_b + kPC);
+      ucbase += Hkv * (nt_b + pc);
       ++cb;
       next_seq = true;
     }
