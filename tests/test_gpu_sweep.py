@@ -27,7 +27,7 @@ from gpu_helpers import (DEV, GDN_STATE_TOL, GDN_STATE_TOL_F16, bits, check_attn
 
 pytestmark = pytest.mark.gpu
 
-N_ATTN, N_KV8, N_F32, N_GDN, N_CONV, N_ACC = 12, 6, 4, 10, 8, 10
+N_ATTN, N_KV8, N_F32, N_GDN, N_CONV, N_ACC = 24, 12, 6, 16, 10, 14
 
 
 def _ks(r, B, kmax):
@@ -312,7 +312,7 @@ def test_accept_sweep(i):
     say(f'  accepted {acc_r.tolist()}')
 
 
-N_STEP = 8
+N_STEP = 12
 
 
 def _step_batch(first, T, ctx):
